@@ -1,0 +1,76 @@
+"""Algorithmic bytes and flops of one decode/verify attention call.
+
+Every byte the method must move is counted once: the visible keys and values of each
+KV head (plus their per-token scales in the FP8 cache), the bias entries at the
+distances that some query reaches, the page-table entries and lengths read, the
+queries, and the outputs (bf16 out and fp32 log-sum-exp). Split partials are an
+implementation detail and are not algorithmic.
+
+Flops: 4*D per (row, query head, visible key): 2*D for q.k and 2*D for p*v.
+"""
+
+from dataclasses import dataclass
+
+
+@dataclass
+class Traffic:
+    kv: int
+    scales: int
+    bias: int
+    q: int
+    out: int
+    lse: int
+    page_table: int
+    seq_lens: int
+    flops: int
+    visible_keys: int     # sum over sequences of keys visible to at least one row
+
+    @property
+    def total(self):
+        return (self.kv + self.scales + self.bias + self.q + self.out + self.lse
+                + self.page_table + self.seq_lens)
+
+
+def visible_span(L, n, window):
+    """Number of keys visible to at least one of the n rows of a sequence of length L."""
+    if window == 0:
+        return L
+    return min(L, window + n - 1)
+
+
+def rows_keys(L, n, window):
+    """Sum over the n rows of the keys each row sees."""
+    total = 0
+    for r in range(n):
+        p = L - n + r
+        total += (p + 1) if window == 0 else min(window, p + 1)
+    return total
+
+
+def traffic(seq_lens, *, n_rows, num_q_heads, num_kv_heads, head_dim, window, dmax,
+            page_size, kv_bytes_per_elem, with_lse=True):
+    seq_lens = [int(x) for x in seq_lens]
+    B = len(seq_lens)
+    spans = [visible_span(L, n_rows, window) for L in seq_lens]
+    keys = sum(spans)
+    kv = keys * num_kv_heads * head_dim * 2 * kv_bytes_per_elem
+    scales = keys * num_kv_heads * 2 * 4 if kv_bytes_per_elem == 1 else 0
+    max_dist = max(((window - 1) if window > 0 else (L - 1)) for L in seq_lens)
+    max_dist = min(max_dist, max(seq_lens) - 1)
+    distinct = min(max_dist, dmax) + 1
+    bias = num_q_heads * 4 * distinct
+    q = B * n_rows * num_q_heads * head_dim * 2
+    out = q
+    lse = B * n_rows * num_q_heads * 4 if with_lse else 0
+    pages = 0
+    for L, s in zip(seq_lens, spans):
+        lo = L - s
+        pages += (L - 1) // page_size - lo // page_size + 1
+    flops = sum(rows_keys(L, n_rows, window) for L in seq_lens) * num_q_heads * 4 * head_dim
+    return Traffic(kv=kv, scales=scales, bias=bias, q=q, out=out, lse=lse,
+                   page_table=pages * 4, seq_lens=B * 4, flops=flops, visible_keys=keys)
+
+
+def kv_bytes_per_token_per_layer(num_kv_heads, head_dim, kv_bytes_per_elem):
+    """Bytes of K and V that one token adds to one attention layer's cache."""
+    return 2 * num_kv_heads * head_dim * kv_bytes_per_elem

@@ -1,0 +1,415 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an oracle package (``oracle`` or a deliberately broken
+copy of it) and raises AssertionError when the oracle disagrees with:
+
+* library routines: torch's scaled_dot_product_attention in float64 (GQA, boolean and
+  additive float masks), torch's float8_e4m3fn and bfloat16 decoding;
+* closed forms: single-key attention, constant logits, geometric bias decay;
+* invariants: a constant bias shift, page permutation, GQA head expansion, NaN in
+  every byte the method must not read, merging split partials;
+* brute force: explicit loops over (row, head, key, dim) on tiny inputs, for windows,
+  verify rows and the Dmax clamp.
+
+``tests/test_oracle_pins.py`` runs them against the oracle; ``tests/test_oracle_mutants.py``
+checks that every planted mistake in a copy of the oracle fails at least one of them.
+"""
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+from decode_attention_verify_amd import synth
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _contiguous_paged(k):
+    """Contiguous float64 K [B][Hkv][L][D] -> paged cache with S = L, identity table."""
+    table = np.arange(k.shape[0], dtype=np.int64)[:, None]      # page b = sequence b
+    return np.ascontiguousarray(k), table
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, "%s: shape %s vs %s" % (what, a.shape, b.shape)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert np.all(np.isfinite(a)) and err <= tol, "%s: max err %r > %r" % (what, err, tol)
+
+
+def _sdpa_reference(q, k, v, seq_len, add_mask, scale):
+    """torch SDPA in float64 for one sequence: q [n][Hq][D], k/v [Hkv][L][D]."""
+    qt = torch.from_numpy(np.ascontiguousarray(np.transpose(q, (1, 0, 2))))[None]
+    kt = torch.from_numpy(np.ascontiguousarray(k))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(v))[None]
+    m = torch.from_numpy(add_mask)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale,
+                                                         enable_gqa=True)
+    return np.transpose(o[0].numpy(), (1, 0, 2))
+
+
+def _case_arrays(case):
+    """numpy views of a synth case: raw codes, as the oracle reads them."""
+    view = torch.uint16 if case.k_cache.dtype == torch.bfloat16 else torch.uint8
+    ks = None if case.k_scale is None else case.k_scale.numpy()
+    vs = None if case.v_scale is None else case.v_scale.numpy()
+    return dict(q=case.q.view(torch.uint16).numpy(), k_cache=case.k_cache.view(view).numpy(),
+                v_cache=case.v_cache.view(view).numpy(), page_table=case.page_table.numpy(),
+                seq_lens=case.seq_lens.numpy(), bias=case.bias.numpy(), k_scale=ks, v_scale=vs)
+
+
+def _run_case(orc, case, **kw):
+    a = _case_arrays(case)
+    sp = case.spec
+    return orc.relative_attention(a["q"], a["k_cache"], a["v_cache"], a["page_table"],
+                                  a["seq_lens"], a["bias"], n_query_rows=sp.n_rows,
+                                  window=sp.window, dmax=sp.dmax,
+                                  softmax_scale=case.softmax_scale, k_scale=a["k_scale"],
+                                  v_scale=a["v_scale"], **kw)
+
+
+def _contiguous_values(orc, case):
+    """Decoded contiguous K/V [B][Hkv][Lmax][D] of a synth case, read slot by slot."""
+    a = _case_arrays(case)
+    sp = case.spec
+    B, Hkv, D, S = sp.batch, sp.num_kv_heads, sp.head_dim, sp.page_size
+    Lmax = int(a["seq_lens"].max())
+    k = np.zeros((B, Hkv, Lmax, D))
+    v = np.zeros((B, Hkv, Lmax, D))
+    for b in range(B):
+        for j in range(int(a["seq_lens"][b])):
+            page = int(a["page_table"][b][j // S])
+            for name, src, dst, sc in (("k", a["k_cache"], k, a["k_scale"]),
+                                       ("v", a["v_cache"], v, a["v_scale"])):
+                raw = src[page, :, j % S, :]
+                if raw.dtype == np.uint16:
+                    dst[b, :, j, :] = torch.from_numpy(raw.copy()).view(torch.bfloat16).double().numpy()
+                else:
+                    vals = torch.from_numpy(raw.copy()).view(torch.float8_e4m3fn).double().numpy()
+                    dst[b, :, j, :] = vals * sc[page, :, j % S].astype(np.float64)[:, None]
+    return k, v
+
+
+# --------------------------------------------------------------------------- library pins
+
+def pin_zero_bias_is_sdpa(orc):
+    """B = 0: plain softmax attention, GQA, causal rows, windows (torch SDPA, float64)."""
+    rng = _rng(1)
+    for n, W, L in ((1, 0, 37), (3, 0, 50), (8, 5, 40), (2, 17, 64), (8, 0, 9)):
+        Hq, Hkv, D, dmax = 12, 2, 32, 80
+        q = rng.standard_normal((1, n, Hq, D))
+        k = rng.standard_normal((1, Hkv, L, D))
+        v = rng.standard_normal((1, Hkv, L, D))
+        kc, table = _contiguous_paged(k)
+        vc, _ = _contiguous_paged(v)
+        bias = np.zeros((Hq, dmax + 1))
+        scale = 1 / math.sqrt(D)
+        out, _ = orc.relative_attention(q, kc, vc, table, [L], bias, n_query_rows=n, window=W,
+                                        dmax=dmax, softmax_scale=scale)
+        mask = np.full((Hq, n, L), -np.inf)
+        for r in range(n):
+            p = L - n + r
+            for j in range(L):
+                if j <= p and (W == 0 or p - j < W):
+                    mask[:, r, j] = 0.0
+        ref = _sdpa_reference(q[0], k[0], v[0], L, mask, scale)
+        _close(out[0], ref, 1e-12, "zero bias vs SDPA n=%d W=%d" % (n, W))
+
+
+def pin_bias_is_additive_mask(orc):
+    """The relative term equals SDPA's additive float mask B[h][min(p-j, Dmax)]."""
+    rng = _rng(2)
+    for n, W, L, dmax in ((1, 0, 70, 100), (4, 0, 33, 20), (8, 12, 60, 63), (5, 3, 30, 2)):
+        Hq, Hkv, D = 6, 1, 16
+        q = rng.standard_normal((1, n, Hq, D))
+        k = rng.standard_normal((1, Hkv, L, D))
+        v = rng.standard_normal((1, Hkv, L, D))
+        kc, table = _contiguous_paged(k)
+        vc, _ = _contiguous_paged(v)
+        bias = rng.standard_normal((Hq, dmax + 1))
+        scale = 0.3
+        out, lse = orc.relative_attention(q, kc, vc, table, [L], bias, n_query_rows=n,
+                                          window=W, dmax=dmax, softmax_scale=scale)
+        mask = np.full((Hq, n, L), -np.inf)
+        for h in range(Hq):
+            for r in range(n):
+                p = L - n + r
+                for j in range(L):
+                    if j <= p and (W == 0 or p - j < W):
+                        mask[h, r, j] = bias[h, min(p - j, dmax)]
+        ref = _sdpa_reference(q[0], k[0], v[0], L, mask, scale)
+        _close(out[0], ref, 1e-12, "bias vs SDPA float mask")
+        logits = torch.from_numpy(scale * np.einsum("rhd,hjd->hrj", q[0], np.repeat(k[0], Hq // Hkv, 0)) + mask)
+        ref_lse = torch.logsumexp(logits, dim=-1).numpy().transpose(1, 0)
+        _close(lse[0], ref_lse, 1e-12, "lse vs torch.logsumexp")
+
+
+def pin_fp8_decode_is_torch(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3fn_codes_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)), "E4M3 NaN codes differ"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok]), "E4M3 values differ from torch"
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def pin_bf16_decode_is_torch(orc):
+    rng = _rng(3)
+    bits = rng.integers(0, 1 << 16, size=5000, dtype=np.uint16)
+    ours = orc.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.copy()).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok]), "bf16 values differ from torch"
+
+
+# --------------------------------------------------------------------------- closed forms
+
+def pin_single_key(orc):
+    """L = n = 1: out = v_0 and lse = scale q.k_0 + B[h][0]."""
+    rng = _rng(4)
+    Hq, Hkv, D = 8, 2, 24
+    q = rng.standard_normal((1, 1, Hq, D))
+    k = rng.standard_normal((1, Hkv, 1, D))
+    v = rng.standard_normal((1, Hkv, 1, D))
+    kc, table = _contiguous_paged(k)
+    vc, _ = _contiguous_paged(v)
+    bias = rng.standard_normal((Hq, 4))
+    out, lse = orc.relative_attention(q, kc, vc, table, [1], bias, n_query_rows=1, window=0,
+                                      dmax=3, softmax_scale=0.7)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        _close(out[0, 0, h], v[0, g, 0], 0.0, "single key out")
+        _close(lse[0, 0, h], 0.7 * float(q[0, 0, h] @ k[0, g, 0]) + bias[h, 0], 1e-13,
+               "single key lse")
+
+
+def pin_uniform_logits(orc):
+    """q = 0, B = 0: lse = ln |J| and out = mean of the visible values."""
+    rng = _rng(5)
+    n, L, Hq, Hkv, D = 4, 29, 6, 3, 8
+    for W in (0, 1, 5, 100):
+        q = np.zeros((1, n, Hq, D))
+        k = rng.standard_normal((1, Hkv, L, D))
+        v = rng.standard_normal((1, Hkv, L, D))
+        kc, table = _contiguous_paged(k)
+        vc, _ = _contiguous_paged(v)
+        out, lse = orc.relative_attention(q, kc, vc, table, [L], np.zeros((Hq, 40)),
+                                          n_query_rows=n, window=W, dmax=39, softmax_scale=1.0)
+        for r in range(n):
+            p = L - n + r
+            lo = 0 if W == 0 else max(0, p - W + 1)
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                _close(lse[0, r, h], math.log(p + 1 - lo), 1e-13, "uniform lse")
+                _close(out[0, r, h], v[0, g, lo:p + 1].mean(axis=0), 1e-13, "uniform out")
+
+
+def pin_geometric_bias(orc):
+    """q = 0, B[h][d] = -a d: lse and the weighted mean of the distance are closed forms."""
+    L, D = 300, 4
+    for a in (0.01, 0.2):
+        q = np.zeros((1, 1, 1, D))
+        j = np.arange(L, dtype=np.float64)
+        v = np.zeros((1, 1, L, D))
+        v[0, 0, :, 0] = 1.0
+        v[0, 0, :, 1] = (L - 1) - j                      # the distance of key j
+        kc, table = _contiguous_paged(np.zeros((1, 1, L, D)))
+        vc, _ = _contiguous_paged(v)
+        dmax = 500
+        bias = (-a * np.arange(dmax + 1, dtype=np.float64))[None, :]
+        out, lse = orc.relative_attention(q, kc, vc, table, [L], bias, n_query_rows=1,
+                                          window=0, dmax=dmax, softmax_scale=1.0)
+        x = math.exp(-a)
+        total = (1 - x ** L) / (1 - x)
+        mean_d = x * (1 - L * x ** (L - 1) + (L - 1) * x ** L) / (1 - x) ** 2 / total
+        _close(lse[0, 0, 0], math.log(total), 1e-12, "geometric lse")
+        _close(out[0, 0, 0, 0], 1.0, 1e-13, "geometric weights sum")
+        _close(out[0, 0, 0, 1], mean_d, 1e-10, "geometric mean distance")
+
+
+# --------------------------------------------------------------------------- invariants
+
+def pin_constant_shift(orc):
+    """B + c leaves out unchanged and adds c to lse."""
+    case = synth.make_case(synth.spec("tiny", batch=2, n_rows=3, seq_len=("uniform", 20, 70),
+                                      dmax=80, head_dim=32, permute_pages=True), seed=6)
+    a = _case_arrays(case)
+    kw = dict(n_query_rows=3, window=0, dmax=80, softmax_scale=case.softmax_scale)
+    bias = a["bias"].astype(np.float64)
+    out0, lse0 = orc.relative_attention(a["q"], a["k_cache"], a["v_cache"], a["page_table"],
+                                        a["seq_lens"], bias, **kw)
+    c = 3.25
+    out1, lse1 = orc.relative_attention(a["q"], a["k_cache"], a["v_cache"], a["page_table"],
+                                        a["seq_lens"], bias + c, **kw)
+    _close(out1, out0, 1e-12, "shift out")
+    _close(lse1, lse0 + c, 1e-12, "shift lse")
+
+
+def pin_page_permutation(orc):
+    """Permuted pages give the same result as contiguous pages; NaN poison is never read."""
+    sp = synth.spec("tiny", batch=3, n_rows=2, num_q_heads=12, num_kv_heads=2,
+                    seq_len=("uniform", 10, 90), dmax=120, head_dim=16, permute_pages=True)
+    case = synth.make_case(sp, seed=7, poison=True)
+    out, lse = _run_case(orc, case)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse)), "poison leaked"
+    k, v = _contiguous_values(orc, case)
+    B, Lmax = k.shape[0], k.shape[2]
+    kc = k.reshape(B, 2, Lmax, 16)
+    vc = v.reshape(B, 2, Lmax, 16)
+    table = np.arange(B)[:, None]
+    bias = np.nan_to_num(case.bias.numpy().astype(np.float64), nan=1e300)
+    out2, lse2 = orc.relative_attention(case.q.view(torch.uint16).numpy(), kc, vc, table,
+                                        case.seq_lens.numpy(), bias, n_query_rows=2, window=0,
+                                        dmax=120, softmax_scale=case.softmax_scale)
+    _close(out, out2, 1e-12, "paged vs contiguous out")
+    _close(lse, lse2, 1e-12, "paged vs contiguous lse")
+
+
+def pin_gqa_expansion(orc):
+    """Expanding K/V to one KV head per query head (head h uses h div G) changes nothing."""
+    rng = _rng(8)
+    n, L, Hq, Hkv, D = 3, 45, 12, 3, 16
+    q = rng.standard_normal((2, n, Hq, D))
+    k = rng.standard_normal((2, Hkv, L, D))
+    v = rng.standard_normal((2, Hkv, L, D))
+    bias = rng.standard_normal((Hq, 50))
+    kc, table = _contiguous_paged(k)
+    vc, _ = _contiguous_paged(v)
+    out, lse = orc.relative_attention(q, kc, vc, table, [L, L - 7], bias, n_query_rows=n,
+                                      window=9, dmax=49, softmax_scale=0.25)
+    G = Hq // Hkv
+    ke = np.repeat(k, G, axis=1)
+    ve = np.repeat(v, G, axis=1)
+    kce, _ = _contiguous_paged(ke)
+    vce, _ = _contiguous_paged(ve)
+    out2, lse2 = orc.relative_attention(q, kce, vce, table, [L, L - 7], bias, n_query_rows=n,
+                                        window=9, dmax=49, softmax_scale=0.25)
+    _close(out, out2, 1e-13, "GQA expansion out")
+    _close(lse, lse2, 1e-13, "GQA expansion lse")
+    # and against SDPA's own GQA mapping, sequence 0, zero bias
+    z = np.zeros_like(bias)
+    out3, _ = orc.relative_attention(q, kc, vc, table, [L, L], z, n_query_rows=n, window=0,
+                                     dmax=49, softmax_scale=0.25)
+    mask = np.full((Hq, n, L), -np.inf)
+    for r in range(n):
+        mask[:, r, :L - n + r + 1] = 0.0
+    ref = _sdpa_reference(q[0], k[0], v[0], L, mask, 0.25)
+    _close(out3[0], ref, 1e-12, "GQA vs SDPA enable_gqa")
+
+
+def pin_split_merge(orc):
+    """Any partition of the keys, merged by the log-sum-exp rule, equals one pass."""
+    case = synth.make_case(synth.spec("tiny", batch=2, n_rows=4, seq_len=("uniform", 30, 100),
+                                      dmax=200, head_dim=16, window=37), seed=9)
+    a = _case_arrays(case)
+    full_out, full_lse = _run_case(orc, case)
+    rng = _rng(10)
+    for trial in range(4):
+        Lmax = int(a["seq_lens"].max())
+        cuts = sorted(set([0, Lmax] + list(rng.integers(0, Lmax, size=trial + 2))))
+        if trial == 1:
+            cuts = sorted(set(cuts + [cuts[1], cuts[1] + 1]))       # a size-1 part
+        parts_o, parts_l = [], []
+        for lo, hi in zip(cuts[:-1], cuts[1:]):
+            for lo2, hi2 in ((lo, hi), (hi, hi)):                      # and an empty part
+                o, l = orc.partial_attention(a["q"], a["k_cache"], a["v_cache"], a["page_table"],
+                                             a["seq_lens"], a["bias"], n_query_rows=4, window=37,
+                                             dmax=200, softmax_scale=case.softmax_scale,
+                                             key_lo=lo2, key_hi=hi2)
+                parts_o.append(o)
+                parts_l.append(l)
+        out, lse = orc.combine_partials(np.stack(parts_o), np.stack(parts_l))
+        _close(out, full_out, 1e-12, "merged out")
+        _close(lse, full_lse, 1e-12, "merged lse")
+
+
+# --------------------------------------------------------------------------- brute force
+
+def _brute_vs_oracle(orc, case, tol=1e-12):
+    out, lse = _run_case(orc, case)
+    k, v = _contiguous_values(orc, case)
+    q = case.q.double().numpy()
+    sp = case.spec
+    bo, bl = orc.bruteforce_attention(q.tolist(), k.tolist(), v.tolist(),
+                                      case.seq_lens.tolist(), case.bias.double().numpy().tolist(),
+                                      window=sp.window, dmax=sp.dmax,
+                                      softmax_scale=case.softmax_scale)
+    _close(out, np.array(bo), tol, "brute out W=%d n=%d" % (sp.window, sp.n_rows))
+    _close(lse, np.array(bl), tol, "brute lse W=%d n=%d" % (sp.window, sp.n_rows))
+
+
+def pin_window_brute_force(orc):
+    """Sliding windows of W keys including the token itself, every verify row count."""
+    L = 23
+    for n in (1, 2, 5, 8):
+        for W in (1, 2, 3, 16, L - 1, L, L + 5):
+            sp = synth.spec("tiny", batch=1, n_rows=n, num_q_heads=2, num_kv_heads=1,
+                            seq_len=L, dmax=40, head_dim=8, window=W, permute_pages=True)
+            _brute_vs_oracle(orc, synth.make_case(sp, seed=100 * n + W))
+
+
+def pin_dmax_clamp(orc):
+    """Distances beyond Dmax read column Dmax; Dmax = 0 is a per-head constant."""
+    for dmax in (0, 1, 3):
+        sp = synth.spec("tiny", batch=2, n_rows=3, num_q_heads=4, num_kv_heads=2,
+                        seq_len=("uniform", 8, 20), dmax=dmax, head_dim=8, window=0)
+        case = synth.make_case(sp, seed=200 + dmax, poison=False)
+        _brute_vs_oracle(orc, case)
+    case0 = synth.make_case(synth.spec("tiny", batch=1, n_rows=2, seq_len=30, dmax=0,
+                                       head_dim=16), seed=3, poison=False)
+    out0, _ = _run_case(orc, case0)
+    zero = dataclasses.replace(case0, bias=torch.zeros_like(case0.bias))
+    outz, _ = _run_case(orc, zero)
+    _close(out0, outz, 1e-12, "Dmax = 0 equals zero bias")
+
+
+def pin_verify_rows_are_shorter_decodes(orc):
+    """Row r of an n-row verify equals a 1-row decode of the first L-(n-1-r) keys."""
+    for W in (0, 6):
+        sp = synth.spec("tiny", batch=2, n_rows=8, num_q_heads=6, num_kv_heads=1,
+                        seq_len=("uniform", 12, 40), dmax=50, head_dim=16, window=W)
+        case = synth.make_case(sp, seed=300 + W)
+        out, lse = _run_case(orc, case)
+        for r in range(8):
+            q1 = case.q[:, r:r + 1].contiguous()
+            lens1 = case.seq_lens - (8 - 1 - r)
+            c1 = dataclasses.replace(case, q=q1, seq_lens=lens1,
+                                     spec=dataclasses.replace(sp, n_rows=1))
+            o1, l1 = _run_case(orc, c1)
+            _close(out[:, r], o1[:, 0], 1e-12, "verify row %d out" % r)
+            _close(lse[:, r], l1[:, 0], 1e-12, "verify row %d lse" % r)
+
+
+def pin_fp8_cache(orc):
+    """An FP8 cache reads code value times scale; brute force on the decoded values."""
+    sp = synth.spec("tiny", batch=2, n_rows=2, num_q_heads=4, num_kv_heads=2,
+                    seq_len=("uniform", 40, 130), dmax=150, head_dim=16, page_size=64,
+                    kv_format=synth.KV_FP8, permute_pages=True)
+    case = synth.make_case(sp, seed=11)
+    _brute_vs_oracle(orc, case)
+
+
+ALL_PINS = [
+    pin_zero_bias_is_sdpa,
+    pin_bias_is_additive_mask,
+    pin_fp8_decode_is_torch,
+    pin_bf16_decode_is_torch,
+    pin_single_key,
+    pin_uniform_logits,
+    pin_geometric_bias,
+    pin_constant_shift,
+    pin_page_permutation,
+    pin_gqa_expansion,
+    pin_split_merge,
+    pin_window_brute_force,
+    pin_dmax_clamp,
+    pin_verify_rows_are_shorter_decodes,
+    pin_fp8_cache,
+]
