@@ -1,0 +1,230 @@
+// C ABI of librattn: plan, decode, free, plus instrumentation. Host code.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+struct rattn_plan_s {
+  rattn_problem prob;
+  rattn::Plan plan;
+  int device;
+  void* workspace;          // partials, then the flag word
+  int32_t* flags;
+  // instrumentation
+  int32_t prof_max;
+  int32_t prof_count;
+  std::vector<hipEvent_t> prof_events;   // 3 per call: before split, after split, after combine
+};
+
+namespace {
+
+bool log_enabled() {
+  const char* e = std::getenv("RATTN_LOG");
+  return e != nullptr && e[0] != '\0' && e[0] != '0';
+}
+
+void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* info) {
+  info->num_splits = pl.num_splits;
+  info->keys_per_split = pl.keys_per_split;
+  info->tile_keys = rattn::kTileKeys;
+  info->row_tiles = pl.row_tiles;
+  info->grid_x = pl.num_splits;
+  info->grid_y = p.num_kv_heads;
+  info->grid_z = p.batch;
+  info->combine_blocks = pl.num_splits > 1 ? p.batch * p.n_query_rows * p.num_q_heads : 0;
+  info->num_cus = pl.num_cus;
+  info->reserved = 0;
+  info->workspace_bytes = pl.workspace_bytes;
+}
+
+void destroy_events(rattn_plan_s* p) {
+  for (hipEvent_t e : p->prof_events) (void)hipEventDestroy(e);
+  p->prof_events.clear();
+  p->prof_max = 0;
+  p->prof_count = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rattn_abi_version(void) { return RATTN_ABI_VERSION; }
+
+const char* rattn_status_string(rattn_status s) {
+  switch (s) {
+    case RATTN_OK: return "ok";
+    case RATTN_E_INVALID: return "invalid argument";
+    case RATTN_E_UNSUPPORTED: return "unsupported problem";
+    case RATTN_E_HIP: return "HIP error";
+    case RATTN_E_NOMEM: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+rattn_status rattn_plan_describe(const rattn_problem* prob, int32_t num_cus,
+                                 rattn_plan_info* info) {
+  if (info == nullptr || num_cus < 1) return RATTN_E_INVALID;
+  rattn_status st = rattn::validate_problem(prob);
+  if (st != RATTN_OK) return st;
+  fill_info(*prob, rattn::make_plan(*prob, num_cus), info);
+  return RATTN_OK;
+}
+
+rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
+  if (plan_out == nullptr) return RATTN_E_INVALID;
+  *plan_out = nullptr;
+  rattn_status st = rattn::validate_problem(prob);
+  if (st != RATTN_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RATTN_E_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return RATTN_E_HIP;
+  rattn_plan_s* p = new (std::nothrow) rattn_plan_s();
+  if (p == nullptr) return RATTN_E_NOMEM;
+  p->prob = *prob;
+  p->plan = rattn::make_plan(*prob, cus);
+  p->device = dev;
+  if (hipMalloc(&p->workspace, (size_t)p->plan.workspace_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    return RATTN_E_NOMEM;
+  }
+  p->flags = (int32_t*)((char*)p->workspace + p->plan.workspace_bytes - 256);
+  if (hipMemset(p->flags, 0, 256) != hipSuccess) {
+    (void)hipFree(p->workspace);
+    delete p;
+    return RATTN_E_HIP;
+  }
+  if (log_enabled()) {
+    std::fprintf(stderr,
+                 "[rattn] plan: batch=%d n=%d Hq=%d Hkv=%d W=%d max_seq_len=%d kv=%s CUs=%d -> "
+                 "splits=%d keys/split=%d row_tiles=%d grid=(%d,%d,%d) workspace=%lld B\n",
+                 prob->batch, prob->n_query_rows, prob->num_q_heads, prob->num_kv_heads,
+                 prob->window, prob->max_seq_len, prob->kv_dtype ? "e4m3" : "bf16", cus,
+                 p->plan.num_splits, p->plan.keys_per_split, p->plan.row_tiles,
+                 p->plan.num_splits, prob->num_kv_heads, prob->batch,
+                 (long long)p->plan.workspace_bytes);
+  }
+  *plan_out = p;
+  return RATTN_OK;
+}
+
+rattn_status rattn_plan_get_info(rattn_plan_t plan, rattn_plan_info* info) {
+  if (plan == nullptr || info == nullptr) return RATTN_E_INVALID;
+  fill_info(plan->prob, plan->plan, info);
+  return RATTN_OK;
+}
+
+rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const float* bias, void* out, float* lse, void* stream) {
+  if (plan == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr ||
+      page_table == nullptr || seq_lens == nullptr || bias == nullptr || out == nullptr)
+    return RATTN_E_INVALID;
+  const rattn_problem& pr = plan->prob;
+  const bool fp8 = pr.kv_dtype == RATTN_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return RATTN_E_INVALID;
+
+  rattn::KernelArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.bias = bias;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.part_o = (float*)plan->workspace;
+  a.part_lse = a.part_o + plan->plan.part_o_floats;
+  a.flags = plan->flags;
+  a.batch = pr.batch;
+  a.n = pr.n_query_rows;
+  a.num_q_heads = pr.num_q_heads;
+  a.num_kv_heads = pr.num_kv_heads;
+  a.group = pr.num_q_heads / pr.num_kv_heads;
+  a.page_size = pr.page_size;
+  a.page_shift = __builtin_ctz((unsigned)pr.page_size);
+  a.num_pages = pr.num_pages;
+  a.max_pages = pr.max_pages_per_seq;
+  a.max_seq_len = pr.max_seq_len;
+  a.window = pr.window;
+  a.dmax = pr.dmax;
+  a.softmax_scale = pr.softmax_scale;
+  a.num_splits = plan->plan.num_splits;
+  a.keys_per_split = plan->plan.keys_per_split;
+
+  hipEvent_t* ev = nullptr;
+  if (plan->prof_count < plan->prof_max) ev = &plan->prof_events[3 * plan->prof_count++];
+  hipStream_t st = (hipStream_t)stream;
+  if (ev && hipEventRecord(ev[0], st) != hipSuccess) return RATTN_E_HIP;
+  if (rattn::launch_split_kv(a, plan->plan.row_tiles, fp8, stream) != 0) return RATTN_E_HIP;
+  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return RATTN_E_HIP;
+  if (plan->plan.num_splits > 1 && rattn::launch_combine(a, stream) != 0) return RATTN_E_HIP;
+  if (ev && hipEventRecord(ev[2], st) != hipSuccess) return RATTN_E_HIP;
+  return RATTN_OK;
+}
+
+rattn_status rattn_free(rattn_plan_t plan) {
+  if (plan == nullptr) return RATTN_OK;
+  destroy_events(plan);
+  rattn_status st = RATTN_OK;
+  if (plan->workspace != nullptr && hipFree(plan->workspace) != hipSuccess) st = RATTN_E_HIP;
+  delete plan;
+  return st;
+}
+
+rattn_status rattn_debug_flags(rattn_plan_t plan, int32_t* flags, void* stream) {
+  if (plan == nullptr || flags == nullptr) return RATTN_E_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(flags, plan->flags, sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return RATTN_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return RATTN_E_HIP;
+  if (hipMemsetAsync(plan->flags, 0, sizeof(int32_t), st) != hipSuccess) return RATTN_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return RATTN_E_HIP;
+  return RATTN_OK;
+}
+
+rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls) {
+  if (plan == nullptr || max_calls < 1 || max_calls > (1 << 20)) return RATTN_E_INVALID;
+  destroy_events(plan);
+  plan->prof_events.resize((size_t)3 * max_calls);
+  for (size_t i = 0; i < plan->prof_events.size(); ++i) {
+    if (hipEventCreate(&plan->prof_events[i]) != hipSuccess) {
+      plan->prof_events.resize(i);
+      destroy_events(plan);
+      return RATTN_E_HIP;
+    }
+  }
+  plan->prof_max = max_calls;
+  plan->prof_count = 0;
+  return RATTN_OK;
+}
+
+rattn_status rattn_profile_end(rattn_plan_t plan, float* split_ms, float* combine_ms,
+                               int32_t* ncalls) {
+  if (plan == nullptr || split_ms == nullptr || combine_ms == nullptr || ncalls == nullptr)
+    return RATTN_E_INVALID;
+  const int32_t n = plan->prof_count;
+  rattn_status st = RATTN_OK;
+  for (int32_t i = 0; i < n && st == RATTN_OK; ++i) {
+    hipEvent_t* ev = &plan->prof_events[3 * i];
+    if (hipEventSynchronize(ev[2]) != hipSuccess ||
+        hipEventElapsedTime(&split_ms[i], ev[0], ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&combine_ms[i], ev[1], ev[2]) != hipSuccess)
+      st = RATTN_E_HIP;
+  }
+  *ncalls = n;
+  destroy_events(plan);
+  return st;
+}
+
+}  // extern "C"

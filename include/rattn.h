@@ -1,0 +1,164 @@
+/*
+ * rattn -- relative-position GQA decode/verify attention over a paged KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What one rattn_decode call computes (one attention layer, one decode or verify
+ * step): for every sequence b, query row r in [0, n) and query head h,
+ *
+ *   p   = seq_lens[b] - n + r                 absolute position of row r
+ *   g   = h / (num_q_heads / num_kv_heads)    the KV head this query head reads
+ *   J   = { j : j <= p  and (window == 0 or p - j <= window - 1) }
+ *   s_j = softmax_scale * (q . k_j) + bias[h][min(p - j, dmax)]
+ *   out = sum_{j in J} exp(s_j - m) v_j / sum_{j in J} exp(s_j - m),  m = max s_j
+ *   lse = m + ln(sum_{j in J} exp(s_j - m))
+ *
+ * Sources (the text of three web pages on serving the Inkling models with vLLM):
+ *   - "vLLM TML Inkling support" (page 2), model architecture section: attention uses
+ *     a learned relative-position term added to the logits before the softmax, in
+ *     place of rotary embeddings; GQA with head size 128 in every layer; a hybrid of
+ *     sliding-window and full-attention layers.
+ *   - "vLLM supports Inkling 2 Small" (page 1), model table: 48 query / 8 KV heads,
+ *     sliding window 1,024; section on trying the model: 7 speculative tokens per step,
+ *     verified by the target model (so up to 8 query rows per sequence, causal among
+ *     themselves); section on vLLM's optimisations: a decode kernel that packs the 6
+ *     query heads of a GQA group into one tile so K/V are read once per group.
+ *   - page 2, technical-optimisation section (FA4 kernel): a "sheared-bias" access
+ *     pattern for the relative term, and a split count chosen from batch size and KV
+ *     length; roadmap: FP8 global attention. Page 3 ("vLLM supports Reflection Beam"),
+ *     support section: an FP8 KV cache.
+ * The pages do not fix how the relative term is parameterised; here it is a per-head
+ * float32 table indexed by the query-key distance, clamped at dmax.
+ *
+ * Conventions
+ *   - Every tensor pointer is DEVICE memory owned by the caller. A plan owns only its
+ *     workspace (split partials), allocated by rattn_plan and released by rattn_free.
+ *   - Layouts (row-major, innermost last):
+ *       q          bf16  [batch][n][num_q_heads][head_dim]
+ *       k_cache    bf16 or E4M3 codes  [num_pages][num_kv_heads][page_size][head_dim]
+ *       v_cache    same as k_cache
+ *       k_scale    fp32  [num_pages][num_kv_heads][page_size]   (E4M3 cache only)
+ *       v_scale    same as k_scale
+ *       page_table int32 [batch][max_pages_per_seq]; key j of sequence b is slot
+ *                  j % page_size of physical page page_table[b][j / page_size]
+ *       seq_lens   int32 [batch]; each length counts the n query rows, whose keys and
+ *                  values are already in the cache; n <= seq_lens[b] <= max_seq_len
+ *       bias       fp32  [num_q_heads][dmax + 1]
+ *       out        bf16  [batch][n][num_q_heads][head_dim]   (round to nearest even)
+ *       lse        fp32  [batch][n][num_q_heads], natural log (may be NULL)
+ *   - The E4M3 cache holds OCP 8-bit E4M3 ("e4m3fn") codes; the value of a key or value
+ *     element is code value * scale of its (page, KV head, slot).
+ *   - rattn_decode is asynchronous on `stream` (a hipStream_t; NULL = default stream),
+ *     never synchronises the host and allocates nothing, so it can be captured in a HIP
+ *     graph. Calls that share a plan share its workspace: use one plan per stream.
+ *   - Errors: all calls return a status and never throw across the ABI. Problem and
+ *     pointer checks happen on the host before any HIP call (RATTN_E_INVALID,
+ *     RATTN_E_UNSUPPORTED). A failed launch returns RATTN_E_HIP; a failed workspace
+ *     allocation RATTN_E_NOMEM. Device-side bad data (a length outside [n, max_seq_len],
+ *     a page id outside [0, num_pages)) is clamped so nothing is read out of bounds, and
+ *     is recorded in a flag word readable with rattn_debug_flags.
+ */
+#ifndef RATTN_H
+#define RATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RATTN_ABI_VERSION 1
+
+typedef struct rattn_plan_s* rattn_plan_t;
+
+typedef enum {
+  RATTN_OK = 0,
+  RATTN_E_INVALID = 1,      /* a null pointer or an inconsistent problem            */
+  RATTN_E_UNSUPPORTED = 2,  /* a valid problem outside what the kernels implement   */
+  RATTN_E_HIP = 3,          /* a HIP runtime call or a kernel launch failed          */
+  RATTN_E_NOMEM = 4         /* the workspace allocation failed                      */
+} rattn_status;
+
+typedef enum {
+  RATTN_KV_BF16 = 0,
+  RATTN_KV_FP8_E4M3 = 1     /* OCP E4M3 codes plus fp32 per-token-per-head scales   */
+} rattn_kv_dtype;
+
+/* Debug flag bits reported by rattn_debug_flags. */
+#define RATTN_FLAG_SEQ_LEN_CLAMPED 1   /* a seq_lens entry was outside [n, max_seq_len] */
+#define RATTN_FLAG_PAGE_CLAMPED 2      /* a page id was outside [0, num_pages)          */
+
+typedef struct {
+  int32_t batch;             /* sequences, >= 1                                          */
+  int32_t num_q_heads;       /* query heads (48 in the Inkling 2 Small layers)            */
+  int32_t num_kv_heads;      /* KV heads (8); num_q_heads % num_kv_heads == 0             */
+  int32_t head_dim;          /* 128 (the only supported value)                            */
+  int32_t n_query_rows;      /* rows per sequence: 1 for decode, 1 + drafts for verify;   */
+                             /* (num_q_heads/num_kv_heads) * n_query_rows <= 64            */
+  int32_t page_size;         /* slots per page: a power of two >= 16                      */
+  int32_t num_pages;         /* physical pages in the cache                               */
+  int32_t max_pages_per_seq; /* page_table row length                                     */
+  int32_t max_seq_len;       /* upper bound on seq_lens[]; <= max_pages_per_seq*page_size */
+  int32_t window;            /* 0 = full context; W > 0 = W keys including the token      */
+  int32_t dmax;              /* largest distance with its own bias column (>= 0)          */
+  float softmax_scale;       /* multiplies q . k (1/sqrt(head_dim) for the pages' models) */
+  int32_t kv_dtype;          /* rattn_kv_dtype                                            */
+  int32_t num_splits;        /* 0 = chosen by the planner; > 0 forces the split count     */
+} rattn_problem;
+
+typedef struct {
+  int32_t num_splits;        /* key-range splits per (sequence, KV head)                  */
+  int32_t keys_per_split;    /* a multiple of tile_keys                                   */
+  int32_t tile_keys;         /* keys per inner-loop step                                  */
+  int32_t row_tiles;         /* 16-row MFMA tiles covering the G * n packed query rows    */
+  int32_t grid_x, grid_y, grid_z;   /* split kernel grid: splits x KV heads x batch       */
+  int32_t combine_blocks;    /* 0 when num_splits == 1 (no combine launch)                */
+  int32_t num_cus;           /* compute units the plan was sized for                      */
+  int32_t reserved;
+  int64_t workspace_bytes;   /* partial outputs and log-sum-exps (0 when num_splits == 1) */
+} rattn_plan_info;
+
+/* Validate `prob`, size the launch for the current HIP device and allocate the
+ * workspace. On success *plan_out owns the workspace until rattn_free. */
+rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out);
+
+/* Validate `prob` and run the planner for a device with `num_cus` compute units,
+ * without touching HIP (host-only; used to inspect and test planner decisions). */
+rattn_status rattn_plan_describe(const rattn_problem* prob, int32_t num_cus,
+                                 rattn_plan_info* info);
+
+/* The decisions of an existing plan. */
+rattn_status rattn_plan_get_info(rattn_plan_t plan, rattn_plan_info* info);
+
+/* One layer's attention for one decode/verify step (see the top of this file for the
+ * arithmetic and the layouts). k_scale / v_scale must be non-NULL exactly for the
+ * E4M3 cache; lse may be NULL. */
+rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const float* bias, void* out, float* lse, void* stream);
+
+/* Release the plan and its workspace (NULL is accepted). */
+rattn_status rattn_free(rattn_plan_t plan);
+
+/* Read and clear the plan's device flag word (RATTN_FLAG_*). Synchronises `stream`. */
+rattn_status rattn_debug_flags(rattn_plan_t plan, int32_t* flags, void* stream);
+
+/* Instrumentation: record HIP events around the kernels of the next `max_calls`
+ * rattn_decode calls of this plan (on their streams). */
+rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls);
+
+/* Stop recording; waits for the recorded events and writes, per call, the split
+ * kernel's and the combine kernel's durations in milliseconds (combine 0 when there
+ * is no combine launch). Arrays hold at least max_calls entries; *ncalls receives the
+ * number of calls recorded. */
+rattn_status rattn_profile_end(rattn_plan_t plan, float* split_ms, float* combine_ms,
+                               int32_t* ncalls);
+
+const char* rattn_status_string(rattn_status status);
+int32_t rattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RATTN_H */

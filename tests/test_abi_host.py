@@ -1,0 +1,109 @@
+"""The C-ABI library on the host: it loads, exports what include/rattn.h declares,
+rejects invalid problems before any HIP call, and plans sensibly (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_verify_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rattn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    names = declared_functions()
+    assert {"rattn_plan", "rattn_decode", "rattn_free"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), "librattn.so does not export %s" % name
+    assert lib.rattn_abi_version() == binding.ABI_VERSION
+
+
+def headline(**kw):
+    base = dict(batch=1, num_q_heads=48, num_kv_heads=8, n_query_rows=1, page_size=16,
+                num_pages=6251, max_pages_per_seq=6250, max_seq_len=100000, window=0,
+                dmax=131071, softmax_scale=128 ** -0.5)
+    base.update(kw)
+    return binding.make_problem(**base)
+
+
+INVALID = [
+    dict(batch=0), dict(num_q_heads=0), dict(num_kv_heads=0), dict(num_q_heads=47),
+    dict(n_query_rows=0), dict(page_size=0), dict(num_pages=0), dict(max_pages_per_seq=0),
+    dict(max_seq_len=0), dict(max_seq_len=100001), dict(window=-1), dict(dmax=-1),
+    dict(softmax_scale=float("inf")), dict(softmax_scale=float("nan")), dict(kv_dtype=2),
+    dict(num_splits=-1),
+]
+UNSUPPORTED = [
+    dict(head_dim=64), dict(n_query_rows=11), dict(page_size=24, max_pages_per_seq=6250),
+    dict(page_size=8, max_pages_per_seq=12500), dict(num_splits=4097),
+]
+
+
+@pytest.mark.parametrize("bad", INVALID)
+def test_invalid_problems_rejected(bad):
+    prob = headline(**bad)
+    with pytest.raises(binding.RattnError) as e:
+        binding.rattn_plan_describe(prob, 256)
+    assert e.value.status == binding.RATTN_E_INVALID
+    # rattn_plan validates before touching HIP, so this is safe without a GPU
+    with pytest.raises(binding.RattnError) as e:
+        binding.rattn_plan(prob)
+    assert e.value.status == binding.RATTN_E_INVALID
+
+
+@pytest.mark.parametrize("bad", UNSUPPORTED)
+def test_unsupported_problems_rejected(bad):
+    with pytest.raises(binding.RattnError) as e:
+        binding.rattn_plan_describe(headline(**bad), 256)
+    assert e.value.status == binding.RATTN_E_UNSUPPORTED
+
+
+def test_null_arguments():
+    lib = binding.load()
+    assert lib.rattn_plan(None, None) == binding.RATTN_E_INVALID
+    assert lib.rattn_plan_describe(None, 256, None) == binding.RATTN_E_INVALID
+    assert lib.rattn_decode(*([None] * 12)) == binding.RATTN_E_INVALID
+    assert lib.rattn_free(None) == binding.RATTN_OK
+    assert lib.rattn_plan_get_info(None, None) == binding.RATTN_E_INVALID
+
+
+def test_planner_headline_fills_the_chip():
+    info = binding.rattn_plan_describe(headline(), 256)
+    assert info.row_tiles == 1
+    assert info.grid_y == 8 and info.grid_z == 1
+    waves = info.grid_x * info.grid_y * info.grid_z
+    assert waves >= 1024, waves
+    assert info.keys_per_split % info.tile_keys == 0
+    assert info.num_splits * info.keys_per_split >= 100000
+    assert info.combine_blocks == 48
+
+
+def test_planner_covers_every_key():
+    for kw in (dict(), dict(window=1024, max_seq_len=32768, max_pages_per_seq=2048),
+               dict(batch=64, window=1024, max_seq_len=32768, max_pages_per_seq=2048),
+               dict(batch=16, n_query_rows=8, max_seq_len=262144, max_pages_per_seq=16384,
+                    dmax=262143),
+               dict(num_splits=7), dict(num_splits=4096), dict(max_seq_len=1,
+                                                                max_pages_per_seq=1)):
+        p = headline(**kw)
+        for cus in (1, 80, 256, 304):
+            info = binding.rattn_plan_describe(p, cus)
+            span = (min(p.max_seq_len, p.window + p.n_query_rows - 1) if p.window
+                    else p.max_seq_len) + info.tile_keys - 1
+            assert info.num_splits * info.keys_per_split >= span
+            if p.num_splits:
+                assert info.num_splits == p.num_splits
+            assert 1 <= info.num_splits <= 4096
+            assert info.row_tiles == -(-(6 * p.n_query_rows) // 16)
+            if info.num_splits == 1:
+                assert info.combine_blocks == 0

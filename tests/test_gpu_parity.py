@@ -1,0 +1,121 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Bar (floating point): max-abs(out) <= 2e-2, mean-abs(out) <= 2e-3, and
+|lse - lse_ref| / max(|lse_ref|, 1) <= 1e-3, over every compared element. Inputs are
+NaN-poisoned wherever the method must not read, so a stray read fails the check.
+"""
+
+import dataclasses
+
+import pytest
+import torch
+
+from decode_attention_verify_amd import synth
+from tests.parity import check_case, run_hip, say
+
+pytestmark = pytest.mark.gpu
+
+
+def small(base, **kw):
+    return dataclasses.replace(synth.spec(base), **kw)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_full_context(seed):
+    check_case(synth.spec("tiny"), seed=seed)
+
+
+@pytest.mark.parametrize("name", ["window_b1", "window_b16", "window_b64"])
+def test_sliding_window(name):
+    check_case(synth.spec(name), seed=0, gen_device="cuda")
+
+
+def test_full_context_100k():
+    check_case(synth.spec("full_100k"), seed=0, gen_device="cuda")
+
+
+def test_verify_b16_sampled():
+    sp = synth.spec("verify_b16")
+    # all KV heads of sequences 0 and 5, plus KV head 3 of every sequence
+    check_case(sp, seed=0, gen_device="cuda", batches=[0, 5], kv_heads=None)
+    check_case(sp, seed=0, gen_device="cuda", batches=None, kv_heads=[3])
+
+
+def test_fp8_1m_sampled():
+    check_case(synth.spec("fp8_1m"), seed=0, gen_device="cuda", kv_heads=[0, 7])
+
+
+# ---------------------------------------------------------------- sweeps at small sizes
+
+@pytest.mark.parametrize("n", range(1, 9))
+@pytest.mark.parametrize("window", [0, 1, 17, 1024])
+def test_rows_and_windows(n, window):
+    sp = small("window_b16", batch=3, n_rows=n, window=window, dmax=1500,
+               seq_len=("uniform", n, 300), name="sweep")
+    check_case(sp, seed=10 * n + window)
+
+
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 1000, 1023, 1024, 1025])
+def test_page_boundaries(L):
+    n = min(L, 3)
+    sp = small("full_100k", batch=2, n_rows=n, seq_len=L, dmax=2000, bias_decay=0.0,
+               name="boundary")
+    check_case(sp, seed=L)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 4096])
+def test_forced_splits(splits):
+    sp = small("full_100k", batch=2, n_rows=2, seq_len=("uniform", 500, 3000), dmax=4000,
+               name="splits")
+    check_case(sp, seed=5, num_splits=splits)
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 64, 256])
+@pytest.mark.parametrize("fmt", [synth.KV_BF16, synth.KV_FP8])
+def test_page_sizes_and_formats(page_size, fmt):
+    sp = small("full_100k", batch=3, n_rows=4, page_size=page_size, kv_format=fmt,
+               seq_len=("uniform", 100, 2500), dmax=3000, name="pages")
+    check_case(sp, seed=page_size)
+
+
+@pytest.mark.parametrize("hq,hkv,n", [(64, 8, 8), (64, 16, 8), (48, 8, 9), (32, 8, 16),
+                                      (8, 8, 8), (6, 1, 10)])
+def test_gqa_ratios(hq, hkv, n):
+    sp = small("full_100k", batch=2, n_rows=n, num_q_heads=hq, num_kv_heads=hkv,
+               seq_len=("uniform", 200, 1500), dmax=2000, name="gqa")
+    check_case(sp, seed=hq + hkv + n)
+
+
+def test_dmax_clamp_on_gpu():
+    sp = small("full_100k", batch=2, n_rows=5, seq_len=("uniform", 300, 900), dmax=37,
+               name="dmax")
+    check_case(sp, seed=3, poison=False)
+
+
+def test_window_fp8():
+    sp = small("window_b16", batch=4, n_rows=8, kv_format=synth.KV_FP8, page_size=64,
+               name="window_fp8")
+    check_case(sp, seed=4)
+
+
+# ---------------------------------------------------------------- properties
+
+def test_deterministic():
+    sp = small("full_100k", batch=2, n_rows=8, seq_len=("uniform", 3000, 9000), name="det")
+    case = synth.make_case(sp, seed=7).to("cuda")
+    o1, l1, _, _ = run_hip(case)
+    o2, l2, _, _ = run_hip(case)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "two runs differ"
+
+
+def test_nonzero_stream():
+    sp = small("full_100k", batch=2, n_rows=3, seq_len=2000, name="stream")
+    case = synth.make_case(sp, seed=8).to("cuda")
+    o1, l1, _, _ = run_hip(case)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2, _, _ = run_hip(case, stream=s)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
