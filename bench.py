@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode/verify attention call through the C ABI (librattn).
+
+A step is one ``rattn_decode`` call: one attention layer for one decode (or verify)
+step over the whole batch, i.e. the split-KV kernel and, when the planner splits the
+key range, the log-sum-exp combine. Inputs are synthetic, seeded, and resident in HBM
+before the timed region starts.
+
+Default workload: full-context layer decode, 48 query / 8 KV heads, head size 128,
+batch 1, one query row, 100,000 keys in a bf16 cache paged by 16 tokens (random page
+permutation), bias table of 131,072 distances (page 1, "vLLM supports Inkling 2 Small",
+section on vLLM's optimisations: batch-1 decode at 100K context).
+
+Cache hygiene: the inputs are cloned into enough copies that the steps rotate over at
+least 1 GiB, four times the 256 MiB Infinity Cache, so every step streams its K/V from
+HBM. The K timed steps run back to back, bracketed by device synchronisations; HIP
+events recorded by the library around each kernel give the per-kernel durations used
+for the roofline figure.
+
+Output: one JSON line (rank 0, N = 1) with the step time, the achieved HBM bandwidth
+over the algorithmic bytes, the roofline of the dominant kernel and the CPU oracle's
+time on the host cores.
+"""
+
+import argparse
+import ctypes
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + achieved HBM GB/s; 48q/8kv GQA, d=128, 100K ctx, b=1"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+CACHE_EVICT_BYTES = 1 << 30     # rotate over at least this many input bytes
+KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/internal.h", "csrc/planner.cpp")
+
+WORKLOADS = {
+    "full_100k": "full-context layer decode, 48q/8kv, d=128, batch 1, 1 row, 100,000 keys, "
+                 "bf16 paged KV (page 16), Dmax=131071",
+    "window_b1": "sliding-window (W=1024) layer decode, 48q/8kv, d=128, batch 1, 1 row, "
+                 "seq_lens U[2048,32768], bf16 paged KV (page 16)",
+    "window_b16": "sliding-window (W=1024) layer decode, 48q/8kv, d=128, batch 16, 1 row, "
+                  "seq_lens U[2048,32768], bf16 paged KV (page 16)",
+    "window_b64": "sliding-window (W=1024) layer decode, 48q/8kv, d=128, batch 64, 1 row, "
+                  "seq_lens U[2048,32768], bf16 paged KV (page 16)",
+    "verify_b16": "speculative verify, 8 causal rows, 48q/8kv, d=128, batch 16, full layer, "
+                  "seq_lens log-uniform [32768,262144], bf16 paged KV (page 16)",
+    "fp8_1m": "full-context layer decode, 48q/8kv, d=128, batch 1, 1 row, 1,048,576 keys, "
+              "E4M3 KV + fp32 per-token-per-head scales, paged (page 64)",
+    "tiny": "full-context decode, 6q/1kv, d=128, batch 1, 1 row, 2048 keys, contiguous bf16",
+}
+
+
+def say(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_verify_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, digest):
+    """HBM bytes per split-kernel launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_split_kv_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_digest") != digest or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def copy_probe(mib, reps):
+    """A plain device-to-device copy of known size, for scaling the HBM counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "reps": reps}), flush=True)
+
+
+def cpu_baseline(case_cpu, tr, budget_s):
+    """Time the fp64 oracle on the host cores over (sequence, KV head) units, in order,
+    until ``budget_s`` is spent; scale to one full step by visible-key work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads", 1) for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:                                   # threadpoolctl missing
+        cores = 1
+    a = case_cpu
+    sp = a.spec
+    view = np.uint16 if a.k_cache.dtype.itemsize == 2 else np.uint8
+    import torch
+    tv = torch.uint16 if a.k_cache.dtype == torch.bfloat16 else torch.uint8
+    q = a.q.view(torch.uint16).numpy()
+    kc = a.k_cache.view(tv).numpy()
+    vc = a.v_cache.view(tv).numpy()
+    assert kc.dtype == view
+    pt, sl, bias = a.page_table.numpy(), a.seq_lens.numpy(), a.bias.numpy()
+    ks = None if a.k_scale is None else a.k_scale.numpy()
+    vs = None if a.v_scale is None else a.v_scale.numpy()
+    from decode_attention_verify_amd import accounting
+    lens = [int(x) for x in sl]
+    unit_work = [accounting.rows_keys(L, sp.n_rows, sp.window) for L in lens]
+    total_work = sum(unit_work) * sp.num_kv_heads
+    done_work = 0
+    out = np.full((sp.batch, sp.n_rows, sp.num_q_heads, sp.head_dim), np.nan)
+    lse = np.full((sp.batch, sp.n_rows, sp.num_q_heads), np.nan)
+    units = 0
+    t0 = time.perf_counter()
+    for b in range(sp.batch):
+        for g in range(sp.num_kv_heads):
+            o, l = oracle.relative_attention(
+                q, kc, vc, pt, sl, bias, n_query_rows=sp.n_rows, window=sp.window,
+                dmax=sp.dmax, softmax_scale=a.softmax_scale, k_scale=ks, v_scale=vs,
+                batches=[b], kv_heads=[g])
+            G = sp.num_q_heads // sp.num_kv_heads
+            out[b, :, g * G:(g + 1) * G] = o[b, :, g * G:(g + 1) * G]
+            lse[b, :, g * G:(g + 1) * G] = l[b, :, g * G:(g + 1) * G]
+            done_work += unit_work[b]
+            units += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    frac = done_work / total_work
+    us_step = secs / frac * 1e6
+    return {
+        "value": us_step,
+        "unit": "us/step",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d (sequence, KV head) units of the same step (%.1f%% of its "
+                  "visible-key work) in %.1f s, scaled to the whole step; fp64 numpy, BLAS "
+                  "threads=%d, elementwise work single-threaded" % (
+                      units, sp.batch * sp.num_kv_heads, 100 * frac, secs, cores),
+        "GBps": tr.total / (us_step * 1e-6) / 1e9,
+    }, out, lse
+
+
+def parity_of(out_gpu, lse_gpu, ref_out, ref_lse):
+    import numpy as np
+    sel = ~np.isnan(ref_lse)
+    if not sel.any():
+        return None
+    o = out_gpu.float().cpu().numpy().astype(np.float64)
+    l = lse_gpu.cpu().numpy().astype(np.float64)
+    osel = np.broadcast_to(sel[..., None], ref_out.shape)
+    d = np.abs(o[osel] - ref_out[osel])
+    rel = np.abs(l[sel] - ref_lse[sel]) / np.maximum(np.abs(ref_lse[sel]), 1.0)
+    return {"rows_checked": int(sel.sum()), "max_abs": float(d.max()),
+            "mean_abs": float(d.mean()), "lse_rel": float(rel.max())}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="full_100k", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0, help="force the split count (0 = planner)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without the per-kernel HIP events (no roofline)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention path runs on a single "
+              "device and has no multi-GPU mode (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_attention_verify_amd import accounting, binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+
+    lib = binding.load()              # raises if librattn.so is missing: no fallback
+    sp = synth.spec(args.workload)
+    say("workload", args.workload, "seed", args.seed)
+    t = time.perf_counter()
+    case = synth.make_case(sp, seed=args.seed, device="cuda", poison=False)
+    torch.cuda.synchronize()
+    say("inputs drawn in %.1fs" % (time.perf_counter() - t))
+    fp8 = sp.kv_format == synth.KV_FP8
+    tr = accounting.traffic(case.seq_lens.tolist(), n_rows=sp.n_rows,
+                            num_q_heads=sp.num_q_heads, num_kv_heads=sp.num_kv_heads,
+                            head_dim=sp.head_dim, window=sp.window, dmax=sp.dmax,
+                            page_size=sp.page_size, kv_bytes_per_elem=1 if fp8 else 2)
+
+    prob = binding.problem_from_case(case, args.splits)
+    plan = binding.Plan(prob)
+    info = plan.info.as_dict()
+    say("plan", info)
+
+    # copies of the streamed inputs, so consecutive steps never hit in the caches
+    per_copy = sum(t.numel() * t.element_size() for t in
+                   (case.q, case.k_cache, case.v_cache, case.bias) +
+                   ((case.k_scale, case.v_scale) if fp8 else ()))
+    ncopies = max(1, min(8, math.ceil(CACHE_EVICT_BYTES / per_copy)))
+    copies = [case]
+    for _ in range(ncopies - 1):
+        copies.append(dataclasses.replace(
+            case, q=case.q.clone(), k_cache=case.k_cache.clone(),
+            v_cache=case.v_cache.clone(), bias=case.bias.clone(),
+            k_scale=None if case.k_scale is None else case.k_scale.clone(),
+            v_scale=None if case.v_scale is None else case.v_scale.clone()))
+    out = torch.empty((sp.batch, sp.n_rows, sp.num_q_heads, sp.head_dim),
+                      dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((sp.batch, sp.n_rows, sp.num_q_heads), dtype=torch.float32,
+                      device="cuda")
+    binding.check_shapes(prob, case.q, case.k_cache, case.v_cache, case.k_scale,
+                         case.v_scale, case.page_table, case.seq_lens, case.bias, out, lse)
+    stream = torch.cuda.current_stream()
+    vp = ctypes.c_void_p
+
+    def argv(c):
+        p = lambda t: None if t is None else vp(t.data_ptr())   # noqa: E731
+        return (plan.handle, p(c.q), p(c.k_cache), p(c.v_cache), p(c.k_scale), p(c.v_scale),
+                p(c.page_table), p(c.seq_lens), p(c.bias), p(out), p(lse),
+                vp(stream.cuda_stream))
+    calls = [argv(c) for c in copies]
+    decode = lib.rattn_decode
+
+    def step(i):
+        st = decode(*calls[i % ncopies])
+        if st != binding.RATTN_OK:
+            raise binding.RattnError(st, "rattn_decode")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    say("warmup done (%d steps, %d input copies, %.0f MB each)" % (
+        args.warmup, ncopies, per_copy / 1e6))
+
+    K = args.steps
+    if not args.no_kernel_events:
+        binding.rattn_profile_begin(plan.handle, K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if args.no_kernel_events:
+        split_ms, comb_ms = [float("nan")], [float("nan")]
+    else:
+        split_ms, comb_ms = binding.rattn_profile_end(plan.handle, K)
+    flags = plan.debug_flags()
+    if flags:
+        raise RuntimeError("device flags %d on valid input" % flags)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    us = ms_per_step * 1e3
+    say("timed %d steps: %.2f us/step" % (K, us))
+
+    split_mean_s = sum(split_ms) / len(split_ms) * 1e-3
+    srt = sorted(split_ms)
+    split_bytes = tr.kv + tr.scales + tr.bias + tr.q + tr.page_table + tr.seq_lens
+    if info["num_splits"] == 1:
+        split_bytes += tr.out + tr.lse
+    achieved = split_bytes / split_mean_s / 1e9
+    digest = kernel_digest()
+    traffic = read_traffic(args.workload, digest)
+    result = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOADS[args.workload],
+            "name": args.workload,
+            "batch": sp.batch,
+            "n_query_rows": sp.n_rows,
+            "q_heads": sp.num_q_heads,
+            "kv_heads": sp.num_kv_heads,
+            "head_dim": sp.head_dim,
+            "seq_lens": (case.seq_lens.tolist() if sp.batch <= 16
+                         else "%d sequences, sum %d" % (sp.batch, int(case.seq_lens.sum()))),
+            "window": sp.window,
+            "dmax": sp.dmax,
+            "page_size": sp.page_size,
+            "kv_cache": sp.kv_format,
+            "num_splits": info["num_splits"],
+            "keys_per_split": info["keys_per_split"],
+            "parallelism": "single GPU",
+            "seed": args.seed,
+        },
+        "algorithmic_bytes": tr.total,
+        "hbm_GBps": round(tr.total / (us * 1e-6) / 1e9, 1),
+        "hbm_frac_of_peak": round(tr.total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernels_us": {
+            "split_kv_mean": round(split_mean_s * 1e6, 3),
+            "split_kv_median": round(srt[len(srt) // 2] * 1e3, 3),
+            "combine_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_kv_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": split_bytes,
+            "kernel_digest": digest,
+        },
+        "input_copies": ncopies,
+    }
+
+    if not args.no_cpu_baseline:
+        say("cpu baseline: oracle on the host cores (budget %.0fs)" % args.cpu_budget)
+        case_cpu = case.to("cpu")
+        cb, ref_out, ref_lse = cpu_baseline(case_cpu, tr, args.cpu_budget)
+        result["cpu_baseline"] = cb
+        # the last step's output against the oracle on the units it computed
+        result["parity_vs_oracle"] = parity_of(out, lse, ref_out, ref_lse)
+    else:
+        result["cpu_baseline"] = None
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,7 +35,8 @@ void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* i
   info->grid_x = pl.num_splits;
   info->grid_y = p.num_kv_heads;
   info->grid_z = p.batch;
-  info->combine_blocks = pl.num_splits > 1 ? p.batch * p.n_query_rows * p.num_q_heads : 0;
+  info->combine_blocks =
+      pl.num_splits > 1 ? p.batch * p.n_query_rows * p.num_q_heads * rattn::kCombineSlices : 0;
   info->num_cus = pl.num_cus;
   info->reserved = 0;
   info->workspace_bytes = pl.workspace_bytes;
@@ -198,7 +199,9 @@ rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls) {
   destroy_events(plan);
   plan->prof_events.resize((size_t)3 * max_calls);
   for (size_t i = 0; i < plan->prof_events.size(); ++i) {
-    if (hipEventCreate(&plan->prof_events[i]) != hipSuccess) {
+    // timing-only events: without the system-scope fence a record costs a few hundred
+    // nanoseconds of stream time instead of a cache writeback and invalidation
+    if (hipEventCreateWithFlags(&plan->prof_events[i], hipEventDisableSystemFence) != hipSuccess) {
       plan->prof_events.resize(i);
       destroy_events(plan);
       return RATTN_E_HIP;

@@ -12,6 +12,8 @@ constexpr int kHeadDim = 128;     // head size of every layer (page 2, model arc
 constexpr int kTileKeys = 32;     // keys per inner-loop step: two 16-key MFMA subtiles
 constexpr int kMaxRows = 64;      // packed query rows per (sequence, KV head): 4 row tiles
 constexpr int kMaxSplits = 4096;
+constexpr int kChunkPages = 512;   // page ids staged in LDS per chunk of a split
+constexpr int kCombineSlices = 4;   // combine work-groups per output row (32 dims each)
 
 // Planner output: how one rattn_decode call is launched.
 struct Plan {

@@ -38,10 +38,27 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 5.545177444479562f;   // 8 ln 2: p = exp(s - m) <= 256
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Streaming loads for data that one call reads exactly once (K/V pages, their scales,
+// bias entries): the non-temporal hint keeps them from displacing reusable lines and,
+// measured on MI355X over permuted 4 KiB pages, raises the sustained read rate from
+// about 5.7 to 6.4 TB/s.
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ f32x4_t ldf4_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+}
+
+__device__ __forceinline__ float ldf_stream(const float* p) {
+  return __builtin_nontemporal_load(p);
 }
 
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
@@ -66,8 +83,10 @@ __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(unsigned int w) {
   return r;
 }
 
+// The 4 lanes lr, lr+16, lr+32, lr+48 hold the same query row. (The gfx950 permlane
+// swaps would keep this in the VALU, but this compiler folds the two results of a swap
+// whose operands are the same value into one, so the reductions use lane shuffles.)
 __device__ __forceinline__ float wave_max_rows(float x) {
-  // max over the 4 lanes lr, lr+16, lr+32, lr+48 that hold the same query row
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
@@ -82,13 +101,27 @@ __device__ __forceinline__ float wave_sum_rows(float x) {
 // Byte offset in the LDS V tile of 16-byte chunk `cc` (0..15) of key row `k` (0..31).
 // Rows are 256 bytes; the chunk index is XOR-swizzled by the row so that the 16 rows
 // one transpose read touches fall into distinct banks.
+// Byte offset in the LDS K tile of 16-byte chunk `c` (0..15) of key row `k` (0..31):
+// the chunk is XOR-swizzled by the row's low 4 bits, so the 16 lanes of one pass of a
+// 16-byte LDS access (one row written, or 16 rows read at one chunk) hit distinct banks.
+__device__ __forceinline__ int klds_off(int k, int c) {
+  return k * 256 + ((c ^ (k & 15)) << 4);
+}
+
 __device__ __forceinline__ int vlds_off(int k, int cc) {
   return k * 256 + ((cc ^ ((k & 7) << 1)) << 4);
 }
 
+#ifndef RATTN_SPLIT_WAVES_PER_EU
+#define RATTN_SPLIT_WAVES_PER_EU 1
+#endif
+
 template <int NRT, bool FP8>
-__global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RATTN_SPLIT_WAVES_PER_EU)))
+void split_kv_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char klds[kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[kTileKeys * 256];
+  __shared__ int pages_lds[kChunkPages + 1];
 
   const int lane = threadIdx.x;
   const int lr = lane & 15;        // key (A operand) / query row (B operand) within a tile
@@ -110,13 +143,26 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
   const int k_lo = W > 0 ? max(0, L - n + 1 - W) : 0;
   const int base = k_lo & ~(kTileKeys - 1);
   const int j_begin = base + split * a.keys_per_split;
-  if (j_begin >= L) return;                  // empty split: the combine skips it
+  if (j_begin >= L) {
+    // an empty split (a short sequence in a batch planned for longer ones) marks its
+    // rows with lse = -inf, which the combine skips
+    if (a.num_splits > 1) {
+      for (int rho = lane; rho < R; rho += 64) {
+        const int r = rho / G;
+        const int64_t row = (int64_t)(b * n + r) * a.num_q_heads + g * G + (rho - r * G);
+        a.part_lse[row * a.num_splits + split] = kNegInf;
+      }
+    }
+    return;
+  }
   const int j_end = min(j_begin + a.keys_per_split, L);
-  const int ntiles = (j_end - j_begin + kTileKeys - 1) / kTileKeys;
   // tiles at or after `fast_lo` and before `fast_hi` need no mask: every key is
   // visible to every row at a distance in [0, W-1]
   const int fast_lo = W > 0 ? max(0, L - W) : 0;
   const int fast_hi = L - n - (kTileKeys - 1);   // j0 <= fast_hi
+  // tiles with bias_lo <= j0 <= fast_hi see only distances in [0, Dmax]: their bias
+  // entries are addressed without clamping
+  const int bias_lo = L - 1 - a.dmax;
 
   // ---- the packed query rows of this lane (row rho = 16 t + lr) ----
   int row_h[NRT], row_p[NRT];
@@ -133,38 +179,42 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
     const uint16_t* qrow = a.q + ((int64_t)(b * n + r) * a.num_q_heads + row_h[t]) * kHeadDim;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      // the d-permutation must match the K operand: bf16 K gives each lane 8 dims at
-      // 32 s + 8 lq; an E4M3 K row gives 16 dims at 64 (s/2) + 16 lq
-      const int d0 = FP8 ? 64 * (s >> 1) + 16 * lq + 8 * (s & 1) : 32 * s + 8 * lq;
+      // the K operand of MFMA s gives lane (lr, lq) the dims 32 s + 8 lq .. + 7
+      const int d0 = 32 * s + 8 * lq;
       u32x4_t v = row_ok[t] ? ld16(qrow + d0) : u32x4_t{0, 0, 0, 0};
       qreg[t][s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  const float* brow[NRT];
+  // bias entry of this lane's row at distance row_p - 4 lq - j, as an element offset
+  // from the table start once j is subtracted (the table has fewer than 2^31 entries)
+  int bias_row[NRT], bias_off[NRT];
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) brow[t] = a.bias + (int64_t)row_h[t] * (a.dmax + 1);
-
-  // ---- page ids: one vector of up to 64 consecutive page-table entries ----
-  const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
-  const int last_page = (L - 1) >> a.page_shift;
-  int pt_first = j_begin >> a.page_shift;
-  int pt_vec = 0;
-  {
-    const int pi = pt_first + lane;
-    pt_vec = pi <= last_page ? pt_row[pi] : 0;
+  for (int t = 0; t < NRT; ++t) {
+    bias_row[t] = row_h[t] * (a.dmax + 1);
+    bias_off[t] = bias_row[t] + row_p[t] - 4 * lq;
   }
-  auto phys_of = [&](int pidx) -> int {
-    if (pidx - pt_first >= 64) {               // uniform: refresh the window of ids
-      pt_first = pidx;
-      const int pi = pt_first + lane;
-      pt_vec = pi <= last_page ? pt_row[pi] : 0;
+
+  // ---- page ids ----
+  // The ids of the pages a chunk of the split touches are staged in LDS before its tile
+  // loop, so that the loop looks them up with an LDS read: a page-table load inside the
+  // loop would make every tile wait for all of its predecessors' K/V loads.
+  const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
+  int chunk_p0 = 0;
+  auto stage_pages = [&](int c0, int c1) {
+    chunk_p0 = c0 >> a.page_shift;
+    const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
+    for (int i = lane; i < np; i += 64) {
+      int ph = pt_row[chunk_p0 + i];
+      if (ph < 0 || ph >= a.num_pages) {
+        atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
+        ph = min(max(ph, 0), a.num_pages - 1);
+      }
+      pages_lds[i] = ph;
     }
-    int ph = __builtin_amdgcn_readlane(pt_vec, pidx - pt_first);
-    if (ph < 0 || ph >= a.num_pages) {
-      if (lane == 0) atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
-      ph = min(max(ph, 0), a.num_pages - 1);
-    }
-    return ph;
+  };
+  auto phys_at = [&](int jt) -> int {      // physical page of key jt of the current chunk
+    const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
+    return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
   };
 
   // ---- per-tile registers ----
@@ -178,60 +228,73 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
   };
 
   const int64_t Hkv = a.num_kv_heads;
+  const int sub_lo = k_lo & ~15;         // first 16-key subtile holding a visible key
+  const int sub_hi = (L - 1) & ~15;      // last subtile holding a key of the sequence
+  // Every load of a tile is issued unconditionally, so that the compiler can count the
+  // loads in flight and wait for exactly one tile at a time. A subtile with no key in
+  // [k_lo, L) (at the two ends of the visible range) reads the nearest subtile that has
+  // one instead; the masks of process_tile discard its keys.
+  // 32-bit lane offsets from a page's (uniform) base address, so that the loads take
+  // the scalar-base + vector-offset form and need no per-tile address arithmetic
+  constexpr int ROW_BYTES = FP8 ? kHeadDim : 2 * kHeadDim;
+  const unsigned kv_off = FP8 ? (lane >> 3) * 128 + 16 * (lane & 7) : lq * 256 + 16 * lr;
+  const unsigned sc_off = 16 * lq;
+  const unsigned char* kc = (const unsigned char*)a.k_cache;
+  const unsigned char* vc = (const unsigned char*)a.v_cache;
   auto load_tile = [&](Tile& T, int j0) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int jt = j0 + 16 * kt;
-      const bool valid = (jt < L) && (jt + 16 > k_lo);      // uniform
-      if (valid) {
-        const int ph = phys_of(jt >> a.page_shift);
-        const int64_t tok0 = ((int64_t)ph * Hkv + g) * S + (jt & (S - 1));
-        if (!FP8) {
-          const unsigned char* kp =
-              (const unsigned char*)a.k_cache + (tok0 + lr) * 256 + 16 * lq;
+      const int js = min(max(jt, sub_lo), sub_hi);
+      const int ph = phys_at(js);
+      const int64_t tok0 = ((int64_t)ph * Hkv + g) * S + (js & (S - 1));
+      const unsigned char* kb = kc + tok0 * ROW_BYTES;
+      const unsigned char* vb = vc + tok0 * ROW_BYTES;
+      // K and V alike: each 16-lane pass of a load reads 256 contiguous bytes (one bf16
+      // row, two E4M3 rows); a pass spread over 16 rows caps the read rate near 5.2 TB/s
+      if (!FP8) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) T.k[kt][s] = ld16(kp + 64 * s);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {   // V keys 4u + lq of this subtile, chunk lr
-            const unsigned char* vp = (const unsigned char*)a.v_cache +
-                                      (tok0 + 4 * u + lq) * 256 + 16 * lr;
-            T.v[4 * kt + u] = ld16(vp);
-          }
-        } else {
-          const unsigned char* kp =
-              (const unsigned char*)a.k_cache + (tok0 + lr) * 128 + 16 * lq;
-          T.k[kt][0] = ld16(kp);
-          T.k[kt][1] = ld16(kp + 64);
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {   // V keys 8u + lane/8 of this subtile, chunk lane%8
-            const unsigned char* vp = (const unsigned char*)a.v_cache +
-                                      (tok0 + 8 * u + (lane >> 3)) * 128 + 16 * (lane & 7);
-            T.v[2 * kt + u] = ld16(vp);
-          }
-          T.ks[kt] = *reinterpret_cast<const f32x4_t*>(a.k_scale + tok0 + 4 * lq);
-          T.vs[kt] = *reinterpret_cast<const f32x4_t*>(a.v_scale + tok0 + 4 * lq);
+        for (int u = 0; u < 4; ++u) {    // keys 4u + lq of this subtile, chunk lr
+          T.k[kt][u] = ld16_stream(kb + kv_off + 1024 * u);
+          T.v[4 * kt + u] = ld16_stream(vb + kv_off + 1024 * u);
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < KV_REGS; ++s) T.k[kt][s] = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < V_LOADS / 2; ++u) T.v[(V_LOADS / 2) * kt + u] = u32x4_t{0, 0, 0, 0};
-        if (FP8) {
-          T.ks[kt] = f32x4_t{0, 0, 0, 0};
-          T.vs[kt] = f32x4_t{0, 0, 0, 0};
+        for (int u = 0; u < 2; ++u) {    // keys 8u + lane/8 of this subtile, chunk lane%8
+          T.k[kt][u] = ld16_stream(kb + kv_off + 1024 * u);
+          T.v[2 * kt + u] = ld16_stream(vb + kv_off + 1024 * u);
         }
+        const unsigned char* ksb = (const unsigned char*)(a.k_scale + tok0);
+        const unsigned char* vsb = (const unsigned char*)(a.v_scale + tok0);
+        T.ks[kt] = __builtin_nontemporal_load((const f32x4_t*)(ksb + sc_off));
+        T.vs[kt] = __builtin_nontemporal_load((const f32x4_t*)(vsb + sc_off));
       }
-      // bias: row r of head h reads B[h][p_r - j] for its 4 keys; rows of one head are
-      // the same slice shifted by their offset r (the sheared access)
+    }
+    // bias: row r of head h reads B[h][p_r - j] for its 4 keys; rows of one head read
+    // the same slice shifted by their offset r (the sheared access)
+    if (j0 >= bias_lo && j0 <= fast_hi) {       // uniform: no clamping needed
+      const unsigned char* bb = (const unsigned char*)a.bias;
 #pragma unroll
       for (int t = 0; t < NRT; ++t) {
+        const unsigned o = (unsigned)(bias_off[t] - j0) * 4u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int dist = row_p[t] - (jt + 4 * lq + i);
-          dist = min(max(dist, 0), a.dmax);
-          T.bias[t][kt][i] = (row_ok[t] && valid) ? brow[t][dist] : 0.f;
-        }
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            T.bias[t][kt][i] = __builtin_nontemporal_load(
+                (const float*)(bb + o - 4 * (16 * kt + i)));
       }
+    } else {                                    // distances clamped to [0, Dmax]
+#pragma unroll
+      for (int t = 0; t < NRT; ++t)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int dist = row_p[t] - (j0 + 16 * kt + 4 * lq + i);
+            dist = min(max(dist, 0), a.dmax);
+            T.bias[t][kt][i] = ldf_stream(a.bias + (unsigned)(bias_row[t] + dist));
+          }
     }
   };
 
@@ -277,23 +340,36 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
       }
     }
 
-    // S^T = K Q^T : lane holds row lr (+16 t), keys 4 lq + i of each 16-key subtile
-    bf16x8_t kop[2][4];
+    // K -> LDS as bf16 (swizzled), then the MFMA A operands: lane (lr, lq) of MFMA s
+    // reads key 16 kt + lr, dims 32 s + 8 lq .. + 7
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       if (!FP8) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kop[kt][s] = __builtin_bit_cast(bf16x8_t, T.k[kt][s]);
+        for (int u = 0; u < 4; ++u)
+          *reinterpret_cast<u32x4_t*>(klds + klds_off(16 * kt + 4 * u + lq, lr)) = T.k[kt][u];
       } else {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          u32x2_t c0 = e4m3x4_to_bf16x4(T.k[kt][u].x), c1 = e4m3x4_to_bf16x4(T.k[kt][u].y);
-          u32x2_t c2 = e4m3x4_to_bf16x4(T.k[kt][u].z), c3 = e4m3x4_to_bf16x4(T.k[kt][u].w);
-          kop[kt][2 * u] = __builtin_bit_cast(bf16x8_t, u32x4_t{c0.x, c0.y, c1.x, c1.y});
-          kop[kt][2 * u + 1] = __builtin_bit_cast(bf16x8_t, u32x4_t{c2.x, c2.y, c3.x, c3.y});
+          const int kk = 16 * kt + 8 * u + (lane >> 3);
+          const int c8 = lane & 7;
+          const u32x4_t raw = T.k[kt][u];
+          u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
+          u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
+          *reinterpret_cast<u32x4_t*>(klds + klds_off(kk, 2 * c8)) = u32x4_t{c0.x, c0.y, c1.x, c1.y};
+          *reinterpret_cast<u32x4_t*>(klds + klds_off(kk, 2 * c8 + 1)) =
+              u32x4_t{c2.x, c2.y, c3.x, c3.y};
         }
       }
     }
+    // S^T = K Q^T : lane holds row lr (+16 t), keys 4 lq + i of each 16-key subtile
+    bf16x8_t kop[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kop[kt][s] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(klds + klds_off(16 * kt + lr, 4 * s + lq)));
     f32x4_t sacc[NRT][2];
 #pragma unroll
     for (int t = 0; t < NRT; ++t) {
@@ -329,10 +405,21 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
         }
       }
       mt = wave_max_rows(mt);
-      const float m_new = fmaxf(m_run[t], mt);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      // The reference point m of a row moves only when the tile's maximum exceeds it by
+      // more than kRescaleSlack, so that the accumulators are rescaled on few tiles;
+      // p = exp(s - m) then stays below exp(kRescaleSlack). O and l share m, so the
+      // quotient O / l and lse = m + ln l are unchanged by the choice of m.
+      const bool grow = mt > m_run[t] + kRescaleSlack;    // false while mt = -inf
+      if (__ballot(grow) != 0) {                          // wave-uniform
+        const float m_new = grow ? mt : m_run[t];
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[t] - m_new) * kLog2e) : 1.f;
+        l_run[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
+        m_run[t] = m_new;
+      }
+      const float m_use = m_run[t] == kNegInf ? 0.f : m_run[t];
       const float mb = -m_use * kLog2e;
-      const float alpha = __builtin_amdgcn_exp2f(__builtin_fmaf(m_run[t], kLog2e, mb));
       float psum = 0.f;
       float pv[2][4];
 #pragma unroll
@@ -344,10 +431,7 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
           pv[kt][i] = FP8 ? (p > 0.f ? p * T.vs[kt][i] : 0.f) : p;
         }
       }
-      l_run[t] = __builtin_fmaf(l_run[t], alpha, psum);
-      m_run[t] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
+      l_run[t] += psum;
       u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
                     pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
       pop[t] = __builtin_bit_cast(bf16x8_t, pk);
@@ -375,18 +459,31 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
     }
   };
 
-  // ---- main loop, two tiles in flight ----
+  // ---- main loop: two tiles in flight, chunks of at most kChunkPages pages ----
+  const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
   Tile A, B;
-  load_tile(A, j_begin);
-  int i = 0;
-  for (; i + 2 <= ntiles; i += 2) {
-    const int j0 = j_begin + i * kTileKeys;
-    load_tile(B, j0 + kTileKeys);
-    process_tile(A, j0);
-    if (i + 2 < ntiles) load_tile(A, j0 + 2 * kTileKeys);
-    process_tile(B, j0 + kTileKeys);
+  for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+    const int c1 = min(c0 + chunk_keys, j_end);
+    stage_pages(c0, c1);
+    const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+    load_tile(A, c0);
+    int i = 0;
+    for (; i + 3 <= nt; i += 2) {
+      const int j0 = c0 + i * kTileKeys;
+      load_tile(B, j0 + kTileKeys);
+      process_tile(A, j0);
+      load_tile(A, j0 + 2 * kTileKeys);
+      process_tile(B, j0 + kTileKeys);
+    }
+    if (i + 2 == nt) {              // the last one or two tiles of the chunk
+      const int j0 = c0 + i * kTileKeys;
+      load_tile(B, j0 + kTileKeys);
+      process_tile(A, j0);
+      process_tile(B, j0 + kTileKeys);
+    } else {
+      process_tile(A, c0 + i * kTileKeys);
+    }
   }
-  if (i < ntiles) process_tile(A, j_begin + i * kTileKeys);
 
   // ---- epilogue ----
 #pragma unroll
@@ -420,70 +517,77 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
 
 // Merge of the split partials (page 2, FA4 kernel: split count from batch, heads and
 // KV length): out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max lse), and
-// lse = max + ln sum w_s. One 256-thread work-group per (sequence, row, query head).
-constexpr int kCombineThreads = 256;
+// lse = max + ln sum w_s. Parts with lse = -inf (no visible key) are skipped.
+//
+// One wave per (sequence, row, query head, 32-dim slice). Lane (stripe, c4) merges
+// splits stripe, stripe + 8, ... for dims 4 c4 .. 4 c4 + 3 with a running maximum,
+// issuing the loads of kCombineUnroll splits at once, so that a row's partials arrive
+// in one memory round trip for up to 8 * kCombineUnroll splits; the 8 stripes are then
+// merged with lane shuffles by the same rule.
+constexpr int kCombineThreads = 64;
+constexpr int kCombineStripes = 8;
+constexpr int kCombineUnroll = 16;
+
+__device__ __forceinline__ void merge_part(float& m, float& l, f32x4_t& acc, float m2,
+                                           float l2, f32x4_t acc2) {
+  const float M = fmaxf(m, m2);
+  const float w1 = m == kNegInf ? 0.f : __expf(m - M);
+  const float w2 = m2 == kNegInf ? 0.f : __expf(m2 - M);
+  l = l * w1 + l2 * w2;
+  acc = acc * w1 + acc2 * w2;
+  m = M;
+}
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) {
-  __shared__ float w_s[kMaxSplits];
-  __shared__ float red[kCombineThreads / 64];
-  __shared__ f32x2_t acc_s[kCombineThreads / 64][64];
-  const int tid = threadIdx.x;
-  const int wid = tid >> 6;
-  const int lane = tid & 63;
-  const int64_t row = blockIdx.x;                  // (b * n + r) * Hq + h
-  const int b = (int)(row / ((int64_t)a.n * a.num_q_heads));
-  const int n = a.n;
-  int L = a.seq_lens[b];
-  L = min(max(L, n), a.max_seq_len);
-  const int W = a.window;
-  const int k_lo = W > 0 ? max(0, L - n + 1 - W) : 0;
-  const int base = k_lo & ~(kTileKeys - 1);
-  const int ns = min(a.num_splits, (L - base + a.keys_per_split - 1) / a.keys_per_split);
-  const float* lp = a.part_lse + row * a.num_splits;
-  const float* op = a.part_o + row * a.num_splits * kHeadDim;
+  const int lane = threadIdx.x;
+  const int c4 = lane & 7;
+  const int stripe = lane >> 3;
+  const int64_t row = blockIdx.x / kCombineSlices;      // (b * n + r) * Hq + h
+  const int slice = blockIdx.x % kCombineSlices;
+  const int ns = a.num_splits;
+  const float* lp = a.part_lse + row * ns;
+  const float* op = a.part_o + row * ns * kHeadDim + 32 * slice + 4 * c4;
 
-  float m = kNegInf;
-  for (int s = tid; s < ns; s += kCombineThreads) m = fmaxf(m, lp[s]);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) red[wid] = m;
-  __syncthreads();
-  m = red[0];
+  float m = kNegInf, l = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = stripe; s0 < ns; s0 += kCombineStripes * kCombineUnroll) {
+    float ls[kCombineUnroll];
+    f32x4_t ov[kCombineUnroll];
 #pragma unroll
-  for (int w = 1; w < kCombineThreads / 64; ++w) m = fmaxf(m, red[w]);
-  __syncthreads();
-
-  float den = 0.f;
-  for (int s = tid; s < ns; s += kCombineThreads) {
-    const float ls = lp[s];
-    const float w = ls == kNegInf ? 0.f : __expf(ls - m);
-    w_s[s] = w;
-    den += w;
-  }
-  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
-  if (lane == 0) red[wid] = den;
-  __syncthreads();
-  den = 0.f;
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const int s = s0 + kCombineStripes * u;
+      ls[u] = s < ns ? lp[s] : kNegInf;
+    }
 #pragma unroll
-  for (int w = 0; w < kCombineThreads / 64; ++w) den += red[w];
-
-  f32x2_t acc = {0.f, 0.f};
-  for (int s = wid; s < ns; s += kCombineThreads / 64) {
-    const float w = w_s[s];
-    if (w != 0.f) {
-      const f32x2_t v = *reinterpret_cast<const f32x2_t*>(op + (int64_t)s * kHeadDim + 2 * lane);
-      acc += w * v;
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const int s = s0 + kCombineStripes * u;
+      ov[u] = s < ns ? *reinterpret_cast<const f32x4_t*>(op + (int64_t)s * kHeadDim)
+                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      if (ls[u] == kNegInf) continue;          // never touch the O of an empty part
+      merge_part(m, l, acc, ls[u], 1.f, ov[u]);
     }
   }
-  acc_s[wid][lane] = acc;
-  __syncthreads();
-  if (wid == 0) {
-    f32x2_t t = acc_s[0][lane];
 #pragma unroll
-    for (int w = 1; w < kCombineThreads / 64; ++w) t += acc_s[w][lane];
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    *reinterpret_cast<unsigned int*>(a.out + row * kHeadDim + 2 * lane) =
-        pack_bf16x2(t.x * inv, t.y * inv);
-    if (lane == 0 && a.lse != nullptr) a.lse[row] = m + __logf(den);
+  for (int off = 8; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    f32x4_t a2;
+    a2[0] = __shfl_xor(acc[0], off);
+    a2[1] = __shfl_xor(acc[1], off);
+    a2[2] = __shfl_xor(acc[2], off);
+    a2[3] = __shfl_xor(acc[3], off);
+    merge_part(m, l, acc, m2, l2, a2);
+  }
+  if (stripe == 0) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const f32x4_t v = acc * inv;
+    u32x2_t wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2_t*>(a.out + row * kHeadDim + 32 * slice + 4 * c4) = wv;
+    if (slice == 0 && c4 == 0 && a.lse != nullptr)
+      a.lse[row] = l > 0.f ? m + __logf(l) : kNegInf;
   }
 }
 
@@ -510,8 +614,8 @@ int launch_split_kv(const KernelArgs& a, int row_tiles, bool fp8, void* stream) 
 
 int launch_combine(const KernelArgs& a, void* stream) {
   const int64_t rows = (int64_t)a.batch * a.n * a.num_q_heads;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)rows), dim3(kCombineThreads), 0,
-                     (hipStream_t)stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(rows * kCombineSlices)),
+                     dim3(kCombineThreads), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

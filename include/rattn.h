@@ -111,7 +111,7 @@ typedef struct {
   int32_t tile_keys;         /* keys per inner-loop step                                  */
   int32_t row_tiles;         /* 16-row MFMA tiles covering the G * n packed query rows    */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: splits x KV heads x batch       */
-  int32_t combine_blocks;    /* 0 when num_splits == 1 (no combine launch)                */
+  int32_t combine_blocks;    /* combine work-groups; 0 when num_splits == 1 (no launch)  */
   int32_t num_cus;           /* compute units the plan was sized for                      */
   int32_t reserved;
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps (0 when num_splits == 1) */
