@@ -29,11 +29,11 @@ class Problem(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_splits", "keys_per_split", "tile_keys", "row_tiles", "grid_x", "grid_y",
-        "grid_z", "combine_blocks", "num_cus", "reserved")] + [
+        "grid_z", "combine_blocks", "num_cus", "blocks_per_cu")] + [
         ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class RattnError(RuntimeError):
@@ -70,7 +70,7 @@ def load(path=None):
     lib.rattn_decode.argtypes = [vp] * 12
     lib.rattn_free.argtypes = [vp]
     lib.rattn_debug_flags.argtypes = [vp, i32p, vp]
-    lib.rattn_profile_begin.argtypes = [vp, i32]
+    lib.rattn_profile_begin.argtypes = [vp, i32, i32]
     lib.rattn_profile_end.argtypes = [vp, f32p, f32p, i32p]
     lib.rattn_status_string.argtypes = [ctypes.c_int]
     lib.rattn_status_string.restype = ctypes.c_char_p
@@ -225,8 +225,8 @@ def rattn_debug_flags(plan, stream=None):
     return flags.value
 
 
-def rattn_profile_begin(plan, max_calls):
-    st = load().rattn_profile_begin(plan, int(max_calls))
+def rattn_profile_begin(plan, max_calls, stride=1):
+    st = load().rattn_profile_begin(plan, int(max_calls), int(stride))
     if st != RATTN_OK:
         raise RattnError(st, "rattn_profile_begin")
 

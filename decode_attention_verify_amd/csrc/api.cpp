@@ -17,6 +17,8 @@ struct rattn_plan_s {
   // instrumentation
   int32_t prof_max;
   int32_t prof_count;
+  int32_t prof_stride;      // record every prof_stride-th call
+  int64_t prof_calls;       // calls since rattn_profile_begin
   std::vector<hipEvent_t> prof_events;   // 3 per call: before split, after split, after combine
 };
 
@@ -38,7 +40,7 @@ void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* i
   info->combine_blocks =
       pl.num_splits > 1 ? p.batch * p.n_query_rows * p.num_q_heads * rattn::kCombineSlices : 0;
   info->num_cus = pl.num_cus;
-  info->reserved = 0;
+  info->blocks_per_cu = pl.blocks_per_cu;
   info->workspace_bytes = pl.workspace_bytes;
 }
 
@@ -47,6 +49,8 @@ void destroy_events(rattn_plan_s* p) {
   p->prof_events.clear();
   p->prof_max = 0;
   p->prof_count = 0;
+  p->prof_stride = 1;
+  p->prof_calls = 0;
 }
 
 }  // namespace
@@ -71,7 +75,7 @@ rattn_status rattn_plan_describe(const rattn_problem* prob, int32_t num_cus,
   if (info == nullptr || num_cus < 1) return RATTN_E_INVALID;
   rattn_status st = rattn::validate_problem(prob);
   if (st != RATTN_OK) return st;
-  fill_info(*prob, rattn::make_plan(*prob, num_cus), info);
+  fill_info(*prob, rattn::make_plan(*prob, num_cus, rattn::kDefaultBlocksPerCU), info);
   return RATTN_OK;
 }
 
@@ -88,7 +92,10 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   rattn_plan_s* p = new (std::nothrow) rattn_plan_s();
   if (p == nullptr) return RATTN_E_NOMEM;
   p->prob = *prob;
-  p->plan = rattn::make_plan(*prob, cus);
+  const int32_t rows = prob->num_q_heads / prob->num_kv_heads * prob->n_query_rows;
+  int bpc = rattn::split_kv_blocks_per_cu((rows + 15) / 16, prob->kv_dtype == RATTN_KV_FP8_E4M3);
+  if (bpc < 1) bpc = rattn::kDefaultBlocksPerCU;
+  p->plan = rattn::make_plan(*prob, cus, bpc);
   p->device = dev;
   if (hipMalloc(&p->workspace, (size_t)p->plan.workspace_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -104,11 +111,12 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   if (log_enabled()) {
     std::fprintf(stderr,
                  "[rattn] plan: batch=%d n=%d Hq=%d Hkv=%d W=%d max_seq_len=%d kv=%s CUs=%d -> "
-                 "splits=%d keys/split=%d row_tiles=%d grid=(%d,%d,%d) workspace=%lld B\n",
+                 "splits=%d keys/split=%d row_tiles=%d blocks/CU=%d grid=(%d,%d,%d) "
+                 "workspace=%lld B\n",
                  prob->batch, prob->n_query_rows, prob->num_q_heads, prob->num_kv_heads,
                  prob->window, prob->max_seq_len, prob->kv_dtype ? "e4m3" : "bf16", cus,
                  p->plan.num_splits, p->plan.keys_per_split, p->plan.row_tiles,
-                 p->plan.num_splits, prob->num_kv_heads, prob->batch,
+                 p->plan.blocks_per_cu, p->plan.num_splits, prob->num_kv_heads, prob->batch,
                  (long long)p->plan.workspace_bytes);
   }
   *plan_out = p;
@@ -163,7 +171,8 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
   a.keys_per_split = plan->plan.keys_per_split;
 
   hipEvent_t* ev = nullptr;
-  if (plan->prof_count < plan->prof_max) ev = &plan->prof_events[3 * plan->prof_count++];
+  if (plan->prof_count < plan->prof_max && plan->prof_calls++ % plan->prof_stride == 0)
+    ev = &plan->prof_events[3 * plan->prof_count++];
   hipStream_t st = (hipStream_t)stream;
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return RATTN_E_HIP;
   if (rattn::launch_split_kv(a, plan->plan.row_tiles, fp8, stream) != 0) return RATTN_E_HIP;
@@ -194,8 +203,9 @@ rattn_status rattn_debug_flags(rattn_plan_t plan, int32_t* flags, void* stream) 
   return RATTN_OK;
 }
 
-rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls) {
-  if (plan == nullptr || max_calls < 1 || max_calls > (1 << 20)) return RATTN_E_INVALID;
+rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls, int32_t stride) {
+  if (plan == nullptr || max_calls < 1 || max_calls > (1 << 20) || stride < 1)
+    return RATTN_E_INVALID;
   destroy_events(plan);
   plan->prof_events.resize((size_t)3 * max_calls);
   for (size_t i = 0; i < plan->prof_events.size(); ++i) {
@@ -209,6 +219,8 @@ rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls) {
   }
   plan->prof_max = max_calls;
   plan->prof_count = 0;
+  plan->prof_stride = stride;
+  plan->prof_calls = 0;
   return RATTN_OK;
 }
 

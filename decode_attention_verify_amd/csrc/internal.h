@@ -21,6 +21,7 @@ struct Plan {
   int32_t keys_per_split;
   int32_t row_tiles;
   int32_t num_cus;
+  int32_t blocks_per_cu;
   int64_t workspace_bytes;
   int64_t part_o_floats;    // [batch][n][Hq][splits][D]
   int64_t part_lse_floats;  // [batch][n][Hq][splits]
@@ -29,8 +30,12 @@ struct Plan {
 // Host-side validation of a problem; no HIP call.
 rattn_status validate_problem(const rattn_problem* p);
 
+// Split-kernel work-groups that stay resident on one CU at a time, as measured for
+// the gfx950 build (one wave per SIMD); rattn_plan queries the runtime instead.
+constexpr int kDefaultBlocksPerCU = 4;
+
 // Host-side planner; no HIP call. `p` must be valid.
-Plan make_plan(const rattn_problem& p, int32_t num_cus);
+Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu);
 
 // Arguments of the split-KV kernel and of the combine kernel.
 struct KernelArgs {
@@ -57,5 +62,7 @@ struct KernelArgs {
 // Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value.
 int launch_split_kv(const KernelArgs& a, int row_tiles, bool fp8, void* stream);
 int launch_combine(const KernelArgs& a, void* stream);
+// Resident split-kernel work-groups per CU for this variant (0 if the query fails).
+int split_kv_blocks_per_cu(int row_tiles, bool fp8);
 
 }  // namespace rattn

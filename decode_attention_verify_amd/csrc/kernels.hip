@@ -112,13 +112,8 @@ __device__ __forceinline__ int vlds_off(int k, int cc) {
   return k * 256 + ((cc ^ ((k & 7) << 1)) << 4);
 }
 
-#ifndef RATTN_SPLIT_WAVES_PER_EU
-#define RATTN_SPLIT_WAVES_PER_EU 1
-#endif
-
 template <int NRT, bool FP8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(RATTN_SPLIT_WAVES_PER_EU)))
-void split_kv_kernel(KernelArgs a) {
+__global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char klds[kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[kTileKeys * 256];
   __shared__ int pages_lds[kChunkPages + 1];
@@ -610,6 +605,26 @@ int launch_split_kv(const KernelArgs& a, int row_tiles, bool fp8, void* stream) 
   }
 #undef RATTN_LAUNCH
   return (int)hipGetLastError();
+}
+
+int split_kv_blocks_per_cu(int row_tiles, bool fp8) {
+  int nb = 0;
+  hipError_t e = hipErrorInvalidValue;
+#define RATTN_OCC(NRT, F8) \
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kv_kernel<NRT, F8>, 64, 0)
+  switch (row_tiles * 2 + (fp8 ? 1 : 0)) {
+    case 2: RATTN_OCC(1, false); break;
+    case 3: RATTN_OCC(1, true); break;
+    case 4: RATTN_OCC(2, false); break;
+    case 5: RATTN_OCC(2, true); break;
+    case 6: RATTN_OCC(3, false); break;
+    case 7: RATTN_OCC(3, true); break;
+    case 8: RATTN_OCC(4, false); break;
+    case 9: RATTN_OCC(4, true); break;
+    default: return 0;
+  }
+#undef RATTN_OCC
+  return e == hipSuccess ? nb : 0;
 }
 
 int launch_combine(const KernelArgs& a, void* stream) {

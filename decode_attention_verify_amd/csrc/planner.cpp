@@ -37,12 +37,13 @@ rattn_status validate_problem(const rattn_problem* p) {
   return RATTN_OK;
 }
 
-Plan make_plan(const rattn_problem& p, int32_t num_cus) {
+Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int32_t G = p.num_q_heads / p.num_kv_heads;
   const int32_t rows = G * p.n_query_rows;
   Plan pl{};
   pl.row_tiles = (rows + 15) / 16;
   pl.num_cus = num_cus;
+  pl.blocks_per_cu = blocks_per_cu;
   // keys visible to at least one row, plus the slack of aligning the first key down
   // to a tile boundary
   int64_t span = p.window > 0 ? std::min<int64_t>(p.max_seq_len, (int64_t)p.window +
@@ -54,11 +55,13 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus) {
   if (p.num_splits > 0) {
     splits = p.num_splits;
   } else {
+    // One single-wave work-group per split. The grid is sized to one round of resident
+    // work-groups, filled to three quarters: on MI355X a 100K-key batch-1 decode streams
+    // fastest with 3 of the 4 resident waves per CU busy (6.26 TB/s, against 6.16 at 4
+    // and 6.06 at 2), and one round avoids a partly idle second round.
     const int64_t units = (int64_t)p.batch * p.num_kv_heads;
-    // one single-wave work-group per split; aim for ~8 resident waves per CU
-    // (fewer when many row tiles make each wave heavier)
-    const int64_t waves_per_cu = pl.row_tiles <= 1 ? 8 : (pl.row_tiles == 2 ? 6 : 4);
-    const int64_t target = (int64_t)std::max(num_cus, 1) * waves_per_cu;
+    const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
+    const int64_t target = std::max<int64_t>(1, slots * 3 / 4);
     splits = (target + units - 1) / units;
     const int64_t min_tiles = 4;   // at least 128 keys per split
     splits = std::min<int64_t>(splits, std::max<int64_t>(1, tiles / min_tiles));

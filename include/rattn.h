@@ -113,7 +113,7 @@ typedef struct {
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: splits x KV heads x batch       */
   int32_t combine_blocks;    /* combine work-groups; 0 when num_splits == 1 (no launch)  */
   int32_t num_cus;           /* compute units the plan was sized for                      */
-  int32_t reserved;
+  int32_t blocks_per_cu;     /* resident split-kernel work-groups per CU assumed          */
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps (0 when num_splits == 1) */
 } rattn_plan_info;
 
@@ -122,7 +122,9 @@ typedef struct {
 rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out);
 
 /* Validate `prob` and run the planner for a device with `num_cus` compute units,
- * without touching HIP (host-only; used to inspect and test planner decisions). */
+ * without touching HIP (host-only; used to inspect and test planner decisions). It
+ * assumes the split kernel's gfx950 occupancy (4 resident work-groups per CU), which
+ * rattn_plan instead queries from the runtime. */
 rattn_status rattn_plan_describe(const rattn_problem* prob, int32_t num_cus,
                                  rattn_plan_info* info);
 
@@ -143,9 +145,12 @@ rattn_status rattn_free(rattn_plan_t plan);
 /* Read and clear the plan's device flag word (RATTN_FLAG_*). Synchronises `stream`. */
 rattn_status rattn_debug_flags(rattn_plan_t plan, int32_t* flags, void* stream);
 
-/* Instrumentation: record HIP events around the kernels of the next `max_calls`
- * rattn_decode calls of this plan (on their streams). */
-rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls);
+/* Instrumentation: record HIP events around the kernels of every `stride`-th
+ * rattn_decode call of this plan (the first call after this one, then every stride-th),
+ * on the call's stream, for at most `max_calls` calls. The events are timing-only
+ * (no system-scope fence); each record still adds a little stream time, which a stride
+ * above 1 spreads over the calls in between. */
+rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls, int32_t stride);
 
 /* Stop recording; waits for the recorded events and writes, per call, the split
  * kernel's and the combine kernel's durations in milliseconds (combine 0 when there
