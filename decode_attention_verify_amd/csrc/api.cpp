@@ -29,16 +29,21 @@ bool log_enabled() {
   return e != nullptr && e[0] != '\0' && e[0] != '0';
 }
 
+// Some unit is shared by several work-groups, so a combine launch merges partials.
+bool needs_combine(const rattn::Plan& pl) {
+  return pl.splits_per_unit > 1 || (pl.splits_per_unit == 0 && pl.split_groups > 1);
+}
+
 void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* info) {
   info->num_splits = pl.num_splits;
   info->keys_per_split = pl.keys_per_split;
   info->tile_keys = rattn::kTileKeys;
-  info->row_tiles = pl.row_tiles;
-  info->grid_x = pl.num_splits;
-  info->grid_y = p.num_kv_heads;
-  info->grid_z = p.batch;
+  info->row_tiles = pl.waves;
+  info->grid_x = pl.split_groups;
+  info->grid_y = 1;
+  info->grid_z = 1;
   info->combine_blocks =
-      pl.num_splits > 1 ? p.batch * p.n_query_rows * p.num_q_heads * rattn::kCombineSlices : 0;
+      needs_combine(pl) ? p.batch * p.n_query_rows * p.num_q_heads * rattn::kCombineSlices : 0;
   info->num_cus = pl.num_cus;
   info->blocks_per_cu = pl.blocks_per_cu;
   info->workspace_bytes = pl.workspace_bytes;
@@ -93,7 +98,9 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   if (p == nullptr) return RATTN_E_NOMEM;
   p->prob = *prob;
   const int32_t rows = prob->num_q_heads / prob->num_kv_heads * prob->n_query_rows;
-  int bpc = rattn::split_kv_blocks_per_cu((rows + 15) / 16, prob->kv_dtype == RATTN_KV_FP8_E4M3);
+  int bpc = rattn::split_kv_blocks_per_cu(rattn::waves_for_rows(rows),
+                                          prob->kv_dtype == RATTN_KV_FP8_E4M3,
+                                          rattn::uses_even_shares(*prob));
   if (bpc < 1) bpc = rattn::kDefaultBlocksPerCU;
   p->plan = rattn::make_plan(*prob, cus, bpc);
   p->device = dev;
@@ -111,12 +118,12 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   if (log_enabled()) {
     std::fprintf(stderr,
                  "[rattn] plan: batch=%d n=%d Hq=%d Hkv=%d W=%d max_seq_len=%d kv=%s CUs=%d -> "
-                 "splits=%d keys/split=%d row_tiles=%d blocks/CU=%d grid=(%d,%d,%d) "
+                 "groups=%d (%d per unit, %d keys each) waves=%d blocks/CU=%d "
                  "workspace=%lld B\n",
                  prob->batch, prob->n_query_rows, prob->num_q_heads, prob->num_kv_heads,
                  prob->window, prob->max_seq_len, prob->kv_dtype ? "e4m3" : "bf16", cus,
-                 p->plan.num_splits, p->plan.keys_per_split, p->plan.row_tiles,
-                 p->plan.blocks_per_cu, p->plan.num_splits, prob->num_kv_heads, prob->batch,
+                 p->plan.split_groups, p->plan.num_splits, p->plan.keys_per_split,
+                 p->plan.waves, p->plan.blocks_per_cu,
                  (long long)p->plan.workspace_bytes);
   }
   *plan_out = p;
@@ -153,6 +160,7 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
   a.lse = lse;
   a.part_o = (float*)plan->workspace;
   a.part_lse = a.part_o + plan->plan.part_o_floats;
+  a.unit_info = (int32_t*)(a.part_lse + plan->plan.part_lse_floats);
   a.flags = plan->flags;
   a.batch = pr.batch;
   a.n = pr.n_query_rows;
@@ -167,17 +175,17 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
   a.window = pr.window;
   a.dmax = pr.dmax;
   a.softmax_scale = pr.softmax_scale;
-  a.num_splits = plan->plan.num_splits;
-  a.keys_per_split = plan->plan.keys_per_split;
+  a.split_groups = plan->plan.split_groups;
+  a.splits_per_unit = plan->plan.splits_per_unit;
 
   hipEvent_t* ev = nullptr;
   if (plan->prof_count < plan->prof_max && plan->prof_calls++ % plan->prof_stride == 0)
     ev = &plan->prof_events[3 * plan->prof_count++];
   hipStream_t st = (hipStream_t)stream;
   if (ev && hipEventRecord(ev[0], st) != hipSuccess) return RATTN_E_HIP;
-  if (rattn::launch_split_kv(a, plan->plan.row_tiles, fp8, stream) != 0) return RATTN_E_HIP;
+  if (rattn::launch_split_kv(a, plan->plan.waves, fp8, stream) != 0) return RATTN_E_HIP;
   if (ev && hipEventRecord(ev[1], st) != hipSuccess) return RATTN_E_HIP;
-  if (plan->plan.num_splits > 1 && rattn::launch_combine(a, stream) != 0) return RATTN_E_HIP;
+  if (needs_combine(plan->plan) && rattn::launch_combine(a, stream) != 0) return RATTN_E_HIP;
   if (ev && hipEventRecord(ev[2], st) != hipSuccess) return RATTN_E_HIP;
   return RATTN_OK;
 }

@@ -10,21 +10,29 @@ namespace rattn {
 
 constexpr int kHeadDim = 128;     // head size of every layer (page 2, model architecture)
 constexpr int kTileKeys = 32;     // keys per inner-loop step: two 16-key MFMA subtiles
-constexpr int kMaxRows = 64;      // packed query rows per (sequence, KV head): 4 row tiles
-constexpr int kMaxSplits = 4096;
-constexpr int kChunkPages = 512;   // page ids staged in LDS per chunk of a split
-constexpr int kCombineSlices = 4;   // combine work-groups per output row (32 dims each)
+constexpr int kMaxRows = 64;      // packed query rows per (sequence, KV head): 4 waves
+constexpr int kMaxSplits = 4096;  // largest forced split count per (sequence, KV head)
+constexpr int kMaxGroups = 1 << 16;   // largest split-kernel grid
+constexpr int kChunkPages = 512;  // page ids staged in LDS per chunk of a piece
+constexpr int kCombineSlices = 4; // combine work-groups per output row (32 dims each)
+
+// Waves per split work-group for `rows` packed query rows: each wave owns one 16-row
+// MFMA tile of ceil(rows / waves) rows.
+inline int waves_for_rows(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
 // Planner output: how one rattn_decode call is launched.
 struct Plan {
-  int32_t num_splits;
-  int32_t keys_per_split;
-  int32_t row_tiles;
+  int32_t split_groups;     // split-kernel work-groups (the grid)
+  int32_t waves;            // waves per split work-group
+  int32_t num_splits;       // nominal work-groups per (sequence, KV head) unit
+  int32_t keys_per_split;   // nominal keys per work-group at the planning length
   int32_t num_cus;
   int32_t blocks_per_cu;
   int64_t workspace_bytes;
-  int64_t part_o_floats;    // [batch][n][Hq][splits][D]
-  int64_t part_lse_floats;  // [batch][n][Hq][splits]
+  int32_t splits_per_unit;  // > 0: per-unit split into this many pieces; 0: even shares
+  int64_t part_o_floats;    // [pieces][rows per unit][D]
+  int64_t part_lse_floats;  // [pieces][rows per unit]
+  int64_t unit_info_ints;   // even shares: [units][2] (first work-group, pieces)
 };
 
 // Host-side validation of a problem; no HIP call.
@@ -33,6 +41,10 @@ rattn_status validate_problem(const rattn_problem* p);
 // Split-kernel work-groups that stay resident on one CU at a time, as measured for
 // the gfx950 build (one wave per SIMD); rattn_plan queries the runtime instead.
 constexpr int kDefaultBlocksPerCU = 4;
+
+// Whether the planner shares the whole call's tiles evenly among the work-groups (else
+// it splits every (sequence, KV head) unit into the same number of pieces).
+bool uses_even_shares(const rattn_problem& p);
 
 // Host-side planner; no HIP call. `p` must be valid.
 Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu);
@@ -51,18 +63,20 @@ struct KernelArgs {
   float* lse;
   float* part_o;
   float* part_lse;
+  int32_t* unit_info;
   int32_t* flags;
   int32_t batch, n, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
   int32_t page_size, page_shift, num_pages, max_pages;
   int32_t max_seq_len, window, dmax;
   float softmax_scale;
-  int32_t num_splits, keys_per_split;
+  int32_t split_groups;     // grid of the split kernel
+  int32_t splits_per_unit;  // > 0: pieces per unit; 0: even shares of all tiles
 };
 
 // Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value.
-int launch_split_kv(const KernelArgs& a, int row_tiles, bool fp8, void* stream);
+int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream);
 int launch_combine(const KernelArgs& a, void* stream);
 // Resident split-kernel work-groups per CU for this variant (0 if the query fails).
-int split_kv_blocks_per_cu(int row_tiles, bool fp8);
+int split_kv_blocks_per_cu(int waves, bool fp8, bool even);
 
 }  // namespace rattn

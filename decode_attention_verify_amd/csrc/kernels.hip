@@ -112,291 +112,382 @@ __device__ __forceinline__ int vlds_off(int k, int cc) {
   return k * 256 + ((cc ^ ((k & 7) << 1)) << 4);
 }
 
-template <int NRT, bool FP8>
-__global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char klds[kTileKeys * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char vlds[kTileKeys * 256];
+// ---------------------------------------------------------------------------------
+// Work partition. Sequence b contributes, for each of its KV heads, the 32-key tiles
+// of its visible range [base_b, L_b); a (sequence, KV head) pair is a unit. Two ways of
+// sharing the units among the split work-groups:
+//  * per unit (splits_per_unit = k > 0): work-group w takes the s-th of k near-equal
+//    tile ranges of unit u = w / k (s = w % k); its partials live under piece id w.
+//    Suits units of equal length (batch-1 decode, sliding-window layers).
+//  * evenly (k = 0): the (sequence, KV head, tile) space, sequences outermost, is cut
+//    into P equal contiguous shares. A share may cover the end of one unit and the
+//    start of the next: each such piece is attended separately and its partial lives
+//    under the piece id w + u, which is unique because walking the tile axis advances
+//    w, u or both at every piece boundary. Suits batches of very different lengths.
+// A work-group whose piece is a whole unit writes the final output itself.
+// ---------------------------------------------------------------------------------
+struct SeqGeom {
+  int L;       // length (clamped into [n, max_seq_len])
+  int k_lo;    // first key visible to the earliest query row
+  int base;    // k_lo rounded down to a tile boundary
+  int tiles;   // tiles of [base, L)
+};
+
+__device__ __forceinline__ SeqGeom seq_geom(const KernelArgs& a, int b, bool flag_bad) {
+  int L = a.seq_lens[b];
+  if (L < a.n || L > a.max_seq_len) {
+    if (flag_bad) atomicOr(a.flags, RATTN_FLAG_SEQ_LEN_CLAMPED);
+    L = min(max(L, a.n), a.max_seq_len);
+  }
+  SeqGeom g;
+  g.L = L;
+  g.k_lo = a.window > 0 ? max(0, L - a.n + 1 - a.window) : 0;
+  g.base = g.k_lo & ~(kTileKeys - 1);
+  g.tiles = (L - g.base + kTileKeys - 1) / kTileKeys;
+  return g;
+}
+
+// Tiles of all units (every lane returns the total; below 2^31 by validation).
+__device__ int total_tiles(const KernelArgs& a, int lane) {
+  int sum = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int b = b0 + lane;
+    int v = b < a.batch ? seq_geom(a, b, true).tiles * a.num_kv_heads : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    sum += v;
+  }
+  return sum;
+}
+
+// The sequence whose units hold tile t (t < total), and the tiles before it.
+__device__ void locate_tile(const KernelArgs& a, int lane, int t, int& b_out, int& before_out) {
+  int carry = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int v = b < a.batch ? seq_geom(a, b, false).tiles * a.num_kv_heads : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int chunk = __shfl(incl, 63);
+    if (t < carry + chunk) {                                 // uniform
+      const unsigned long long hit = __ballot(carry + incl > t);
+      const int idx = __ffsll(hit) - 1;
+      b_out = b0 + idx;
+      before_out = carry + __shfl(incl - v, idx);
+      return;
+    }
+    carry += chunk;
+  }
+  b_out = a.batch - 1;                                       // not reached for t < total
+  before_out = carry;
+}
+
+// ---------------------------------------------------------------------------------
+// Split kernel: WR waves per work-group, each owning one 16-row MFMA tile of the G*n
+// packed query rows of a (sequence, KV head) unit (rows per wave: ceil(G*n / WR)).
+// The waves load equal shares of every 32-key K/V tile into registers, store them to
+// a double-buffered LDS tile and meet at one barrier per tile; each wave then attends
+// its rows over the whole tile. Each K/V byte is read from HBM once per unit.
+// ---------------------------------------------------------------------------------
+// Multi-wave work-groups ask for two waves per SIMD (at most 256 VGPRs each): on the
+// 8-row verify workload that beat one wave per SIMD by 1.4x despite a few spilled
+// registers, since every tile's barrier waits on the slowest of the group's waves.
+template <int WR, bool FP8, bool EVEN>
+__global__ __launch_bounds__(64 * WR)
+__attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char klds[WR > 1 ? 2 : 1][kTileKeys * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[WR > 1 ? 2 : 1][kTileKeys * 256];
   __shared__ int pages_lds[kChunkPages + 1];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lr = lane & 15;        // key (A operand) / query row (B operand) within a tile
   const int lq = lane >> 4;        // k-group of the MFMA operands
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
   const int n = a.n;
   const int G = a.group;
   const int R = G * n;
   const int S = a.page_size;
-
-  int L = a.seq_lens[b];
-  if (L < n || L > a.max_seq_len) {
-    if (lane == 0) atomicOr(a.flags, RATTN_FLAG_SEQ_LEN_CLAMPED);
-    L = min(max(L, n), a.max_seq_len);
-  }
   const int W = a.window;
-  const int k_lo = W > 0 ? max(0, L - n + 1 - W) : 0;
-  const int base = k_lo & ~(kTileKeys - 1);
-  const int j_begin = base + split * a.keys_per_split;
-  if (j_begin >= L) {
-    // an empty split (a short sequence in a batch planned for longer ones) marks its
-    // rows with lse = -inf, which the combine skips
-    if (a.num_splits > 1) {
-      for (int rho = lane; rho < R; rho += 64) {
-        const int r = rho / G;
-        const int64_t row = (int64_t)(b * n + r) * a.num_q_heads + g * G + (rho - r * G);
-        a.part_lse[row * a.num_splits + split] = kNegInf;
-      }
-    }
-    return;
-  }
-  const int j_end = min(j_begin + a.keys_per_split, L);
-  // tiles at or after `fast_lo` and before `fast_hi` need no mask: every key is
-  // visible to every row at a distance in [0, W-1]
-  const int fast_lo = W > 0 ? max(0, L - W) : 0;
-  const int fast_hi = L - n - (kTileKeys - 1);   // j0 <= fast_hi
-  // tiles with bias_lo <= j0 <= fast_hi see only distances in [0, Dmax]: their bias
-  // entries are addressed without clamping
-  const int bias_lo = L - 1 - a.dmax;
-
-  // ---- the packed query rows of this lane (row rho = 16 t + lr) ----
-  int row_h[NRT], row_p[NRT];
-  bool row_ok[NRT];
-  bf16x8_t qreg[NRT][4];
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    const int rho = 16 * t + lr;
-    row_ok[t] = rho < R;
-    const int r = row_ok[t] ? rho / G : 0;
-    const int hl = row_ok[t] ? rho - r * G : 0;
-    row_h[t] = g * G + hl;
-    row_p[t] = L - n + r;
-    const uint16_t* qrow = a.q + ((int64_t)(b * n + r) * a.num_q_heads + row_h[t]) * kHeadDim;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // the K operand of MFMA s gives lane (lr, lq) the dims 32 s + 8 lq .. + 7
-      const int d0 = 32 * s + 8 * lq;
-      u32x4_t v = row_ok[t] ? ld16(qrow + d0) : u32x4_t{0, 0, 0, 0};
-      qreg[t][s] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-  // bias entry of this lane's row at distance row_p - 4 lq - j, as an element offset
-  // from the table start once j is subtracted (the table has fewer than 2^31 entries)
-  int bias_row[NRT], bias_off[NRT];
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    bias_row[t] = row_h[t] * (a.dmax + 1);
-    bias_off[t] = bias_row[t] + row_p[t] - 4 * lq;
-  }
-
-  // ---- page ids ----
-  // The ids of the pages a chunk of the split touches are staged in LDS before its tile
-  // loop, so that the loop looks them up with an LDS read: a page-table load inside the
-  // loop would make every tile wait for all of its predecessors' K/V loads.
-  const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
-  int chunk_p0 = 0;
-  auto stage_pages = [&](int c0, int c1) {
-    chunk_p0 = c0 >> a.page_shift;
-    const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
-    for (int i = lane; i < np; i += 64) {
-      int ph = pt_row[chunk_p0 + i];
-      if (ph < 0 || ph >= a.num_pages) {
-        atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
-        ph = min(max(ph, 0), a.num_pages - 1);
-      }
-      pages_lds[i] = ph;
-    }
-  };
-  auto phys_at = [&](int jt) -> int {      // physical page of key jt of the current chunk
-    const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
-    return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
-  };
-
-  // ---- per-tile registers ----
-  constexpr int KV_REGS = FP8 ? 2 : 4;   // 16-byte loads per lane per subtile (K)
-  constexpr int V_LOADS = FP8 ? 4 : 8;   // 16-byte loads per lane per tile (V)
-  struct Tile {
-    u32x4_t k[2][KV_REGS];
-    u32x4_t v[V_LOADS];
-    f32x4_t ks[2], vs[2];
-    float bias[NRT][2][4];
-  };
-
   const int64_t Hkv = a.num_kv_heads;
-  const int sub_lo = k_lo & ~15;         // first 16-key subtile holding a visible key
-  const int sub_hi = (L - 1) & ~15;      // last subtile holding a key of the sequence
-  // Every load of a tile is issued unconditionally, so that the compiler can count the
-  // loads in flight and wait for exactly one tile at a time. A subtile with no key in
-  // [k_lo, L) (at the two ends of the visible range) reads the nearest subtile that has
-  // one instead; the masks of process_tile discard its keys.
-  // 32-bit lane offsets from a page's (uniform) base address, so that the loads take
-  // the scalar-base + vector-offset form and need no per-tile address arithmetic
+  const int rpw = (R + WR - 1) / WR;
+
+  const int64_t wg = blockIdx.x;
+  const int k_split = a.splits_per_unit;     // used when !EVEN
+  int T = 0;
+  int64_t P = 0, t_begin = 0, t_end = 0;
+  if (EVEN) {                                // even shares of the whole tile space
+    T = total_tiles(a, lane);
+    P = min((int64_t)gridDim.x, (int64_t)T);
+    if (wg >= P) return;                     // uniform over the work-group
+    t_begin = wg * T / P;
+    t_end = (wg + 1) * T / P;
+  }
+
+  // ---- this wave's query row (row rho of the unit's packed rows) ----
+  const int rho = wave * rpw + lr;
+  const bool row_ok = lr < rpw && rho < R;
+  const int r_of_row = row_ok ? rho / G : 0;
+  const int hl_of_row = row_ok ? rho - r_of_row * G : 0;
+
+  // ---- per-tile registers: this wave's share of the tile's 16-byte loads ----
+  constexpr int SLOTS = FP8 ? 8 : 16;        // 16-byte loads per lane for one whole tile
+  constexpr int NSLOT = SLOTS / WR;
+  struct Tile {
+    u32x4_t x[NSLOT];
+    f32x4_t ks[2], vs[2];
+    float bias[2][4];
+  };
   constexpr int ROW_BYTES = FP8 ? kHeadDim : 2 * kHeadDim;
+  // lane offset within a 16-key subtile block: each 16-lane pass of a load reads 256
+  // contiguous bytes (one bf16 row, two E4M3 rows); a pass spread over 16 rows caps the
+  // read rate near 5.2 TB/s on MI355X, against 6.4 TB/s for contiguous passes
   const unsigned kv_off = FP8 ? (lane >> 3) * 128 + 16 * (lane & 7) : lq * 256 + 16 * lr;
   const unsigned sc_off = 16 * lq;
   const unsigned char* kc = (const unsigned char*)a.k_cache;
   const unsigned char* vc = (const unsigned char*)a.v_cache;
-  auto load_tile = [&](Tile& T, int j0) {
+
+  for (bool more = true; more;) {
+    // ---- the next piece: tiles [tile0, tile1) of unit (b, g) ----
+    int b, g, tile0, tile1;
+    SeqGeom sg;
+    bool whole;
+    int64_t prow0;                           // partial row of packed row 0 of the unit
+    if (!EVEN) {
+      const int64_t u = wg / k_split;
+      const int sidx = (int)(wg - u * k_split);
+      b = (int)(u / Hkv);
+      g = (int)(u - (int64_t)b * Hkv);
+      sg = seq_geom(a, b, true);
+      tile0 = (int)((int64_t)sidx * sg.tiles / k_split);
+      tile1 = (int)((int64_t)(sidx + 1) * sg.tiles / k_split);
+      whole = k_split == 1;
+      prow0 = wg * R;
+      more = false;
+      if (tile1 == tile0) {
+        // fewer tiles than splits: an empty piece marks its rows, which the combine skips
+        if (row_ok) a.part_lse[prow0 + rho] = kNegInf;
+        return;
+      }
+    } else {
+      int before;
+      locate_tile(a, lane, (int)t_begin, b, before);
+      sg = seq_geom(a, b, false);
+      g = (t_begin - before) / sg.tiles;
+      const int64_t ustart = before + (int64_t)g * sg.tiles;
+      const int64_t uend = ustart + sg.tiles;
+      const int64_t piece_end = min(t_end, uend);
+      tile0 = (int)(t_begin - ustart);
+      tile1 = (int)(piece_end - ustart);
+      whole = t_begin == ustart && piece_end == uend;
+      const int64_t u = (int64_t)b * Hkv + g;
+      prow0 = (wg + u) * R;
+      if (t_begin == ustart && lane == 0 && wave == 0) {
+        // the unit's first work-group records where its pieces are, for the combine
+        // (one piece: the unit is whole and its output final)
+        const int64_t w_last = (uend * P - 1) / T;
+        a.unit_info[2 * u] = (int)wg;
+        a.unit_info[2 * u + 1] = (int)(w_last - wg + 1);
+      }
+      t_begin = piece_end;
+      more = t_begin < t_end;
+    }
+    const int L = sg.L;
+    const int k_lo = sg.k_lo;
+    const int j_begin = sg.base + tile0 * kTileKeys;
+    const int j_end = min(sg.base + tile1 * kTileKeys, L);
+
+    // tiles at or after `fast_lo` and at or before `fast_hi` need no mask: every key is
+    // visible to every row at a distance in [0, W-1]
+    const int fast_lo = W > 0 ? max(0, L - W) : 0;
+    const int fast_hi = L - n - (kTileKeys - 1);
+    // tiles with bias_lo <= j0 <= fast_hi see only distances in [0, Dmax]: their bias
+    // entries are addressed without clamping
+    const int bias_lo = L - 1 - a.dmax;
+    const int sub_lo = k_lo & ~15;           // first 16-key subtile holding a visible key
+    const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
+
+    const int row_h = g * G + hl_of_row;
+    const int row_p = L - n + r_of_row;
+    bf16x8_t qreg[4];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)(b * n + r_of_row) * a.num_q_heads + row_h) * kHeadDim;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int jt = j0 + 16 * kt;
-      const int js = min(max(jt, sub_lo), sub_hi);
-      const int ph = phys_at(js);
-      const int64_t tok0 = ((int64_t)ph * Hkv + g) * S + (js & (S - 1));
-      const unsigned char* kb = kc + tok0 * ROW_BYTES;
-      const unsigned char* vb = vc + tok0 * ROW_BYTES;
-      // K and V alike: each 16-lane pass of a load reads 256 contiguous bytes (one bf16
-      // row, two E4M3 rows); a pass spread over 16 rows caps the read rate near 5.2 TB/s
-      if (!FP8) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {    // keys 4u + lq of this subtile, chunk lr
-          T.k[kt][u] = ld16_stream(kb + kv_off + 1024 * u);
-          T.v[4 * kt + u] = ld16_stream(vb + kv_off + 1024 * u);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {    // keys 8u + lane/8 of this subtile, chunk lane%8
-          T.k[kt][u] = ld16_stream(kb + kv_off + 1024 * u);
-          T.v[2 * kt + u] = ld16_stream(vb + kv_off + 1024 * u);
-        }
-        const unsigned char* ksb = (const unsigned char*)(a.k_scale + tok0);
-        const unsigned char* vsb = (const unsigned char*)(a.v_scale + tok0);
-        T.ks[kt] = __builtin_nontemporal_load((const f32x4_t*)(ksb + sc_off));
-        T.vs[kt] = __builtin_nontemporal_load((const f32x4_t*)(vsb + sc_off));
+      for (int s = 0; s < 4; ++s) {
+        // the K operand of MFMA s gives lane (lr, lq) the dims 32 s + 8 lq .. + 7
+        const u32x4_t v = row_ok ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
+        qreg[s] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
-    // bias: row r of head h reads B[h][p_r - j] for its 4 keys; rows of one head read
-    // the same slice shifted by their offset r (the sheared access)
-    if (j0 >= bias_lo && j0 <= fast_hi) {       // uniform: no clamping needed
-      const unsigned char* bb = (const unsigned char*)a.bias;
+    // bias entry of this lane's row at distance row_p - 4 lq - j, as an element offset
+    // from the table start once j is subtracted (the table has fewer than 2^31 entries)
+    const int bias_row = row_h * (a.dmax + 1);
+    const int bias_off = bias_row + row_p - 4 * lq;
+
+    // ---- page ids ----
+    // The ids of the pages a chunk of the piece touches are staged in LDS before its
+    // tile loop, so that the loop looks them up with an LDS read: a page-table load in
+    // the loop would make every tile wait for all of its predecessors' K/V loads.
+    const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
+    int chunk_p0 = 0;
+    auto stage_pages = [&](int c0, int c1) {
+      if (WR > 1) __syncthreads();           // the previous chunk's ids and tiles are done
+      chunk_p0 = c0 >> a.page_shift;
+      const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
+      for (int i = (int)threadIdx.x; i < np; i += 64 * WR) {
+        int ph = pt_row[chunk_p0 + i];
+        if (ph < 0 || ph >= a.num_pages) {
+          atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
+          ph = min(max(ph, 0), a.num_pages - 1);
+        }
+        pages_lds[i] = ph;
+      }
+      if (WR > 1) __syncthreads();
+    };
+    auto phys_at = [&](int jt) -> int {     // physical page of key jt of the current chunk
+      const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
+      return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
+    };
+
+    // Every load of a tile is issued unconditionally, so that the compiler can count the
+    // loads in flight and wait for exactly one tile at a time. A subtile with no key in
+    // [k_lo, L) (at the two ends of the visible range) reads the nearest subtile that
+    // has one instead; the masks of process_tile discard its keys.
+    auto load_tile = [&](Tile& X, int j0) {
+      int64_t tok0[2];
 #pragma unroll
-      for (int t = 0; t < NRT; ++t) {
-        const unsigned o = (unsigned)(bias_off[t] - j0) * 4u;
+      for (int kt = 0; kt < 2; ++kt) {
+        const int js = min(max(j0 + 16 * kt, sub_lo), sub_hi);
+        tok0[kt] = ((int64_t)phys_at(js) * Hkv + g) * S + (js & (S - 1));
+      }
+#pragma unroll
+      for (int m = 0; m < NSLOT; ++m) {
+        // slot = (K|V, subtile, 1 KiB block of the subtile)
+        const int slot = wave + WR * m;
+        const int kv = FP8 ? slot >> 2 : slot >> 3;
+        const int kt = FP8 ? (slot >> 1) & 1 : (slot >> 2) & 1;
+        const int u = FP8 ? slot & 1 : slot & 3;
+        const unsigned char* base = (kv ? vc : kc) + tok0[kt] * ROW_BYTES;
+        X.x[m] = ld16_stream(base + kv_off + 1024 * u);
+      }
+      if (FP8) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          X.ks[kt] = __builtin_nontemporal_load(
+              (const f32x4_t*)((const unsigned char*)(a.k_scale + tok0[kt]) + sc_off));
+          X.vs[kt] = __builtin_nontemporal_load(
+              (const f32x4_t*)((const unsigned char*)(a.v_scale + tok0[kt]) + sc_off));
+        }
+      }
+      // bias: row r of head h reads B[h][p_r - j] for its 4 keys; rows of one head read
+      // the same slice shifted by their offset r (the sheared access)
+      if (j0 >= bias_lo && j0 <= fast_hi) {     // uniform: no clamping needed
+        const unsigned char* bb = (const unsigned char*)a.bias;
+        const unsigned o = (unsigned)(bias_off - j0) * 4u;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            T.bias[t][kt][i] = __builtin_nontemporal_load(
-                (const float*)(bb + o - 4 * (16 * kt + i)));
-      }
-    } else {                                    // distances clamped to [0, Dmax]
-#pragma unroll
-      for (int t = 0; t < NRT; ++t)
+            X.bias[kt][i] =
+                __builtin_nontemporal_load((const float*)(bb + o - 4 * (16 * kt + i)));
+      } else {                                  // distances clamped to [0, Dmax]
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            int dist = row_p[t] - (j0 + 16 * kt + 4 * lq + i);
+            int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
             dist = min(max(dist, 0), a.dmax);
-            T.bias[t][kt][i] = ldf_stream(a.bias + (unsigned)(bias_row[t] + dist));
+            X.bias[kt][i] = ldf_stream(a.bias + (unsigned)(bias_row + dist));
           }
-    }
-  };
-
-  // ---- running state ----
-  f32x4_t o[NRT][8];
-  float m_run[NRT], l_run[NRT];
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    m_run[t] = kNegInf;
-    l_run[t] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4_t{0, 0, 0, 0};
-  }
-
-  auto process_tile = [&](const Tile& T, int j0) {
-    const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
-
-    // V -> LDS (bf16, swizzled); keys outside [k_lo, L) become zero so that P = 0
-    // times a stale or NaN value cannot reach the accumulator
-    if (!FP8) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int kk = 4 * u + lq;
-        const int j = j0 + kk;
-        u32x4_t v = T.v[u];
-        if (!fast && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t*>(vlds + vlds_off(kk, lr)) = v;
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = 8 * u + (lane >> 3);
-        const int j = j0 + kk;
-        const int c8 = lane & 7;
-        u32x4_t raw = T.v[u];
-        if (!fast && (j < k_lo || j >= L)) raw = u32x4_t{0, 0, 0, 0};
-        u32x2_t a0 = e4m3x4_to_bf16x4(raw.x), a1 = e4m3x4_to_bf16x4(raw.y);
-        u32x2_t a2 = e4m3x4_to_bf16x4(raw.z), a3 = e4m3x4_to_bf16x4(raw.w);
-        *reinterpret_cast<u32x4_t*>(vlds + vlds_off(kk, 2 * c8)) =
-            u32x4_t{a0.x, a0.y, a1.x, a1.y};
-        *reinterpret_cast<u32x4_t*>(vlds + vlds_off(kk, 2 * c8 + 1)) =
-            u32x4_t{a2.x, a2.y, a3.x, a3.y};
-      }
-    }
+    };
 
-    // K -> LDS as bf16 (swizzled), then the MFMA A operands: lane (lr, lq) of MFMA s
-    // reads key 16 kt + lr, dims 32 s + 8 lq .. + 7
+    // ---- running state of this lane's row ----
+    f32x4_t o[8];
+    float m_run = kNegInf, l_run = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (!FP8) {
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0, 0, 0, 0};
+
+    auto process_tile = [&](const Tile& X, int j0, int buf) {
+      const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
+      // a single wave reuses one LDS buffer (its LDS accesses execute in order); several
+      // waves alternate two, so that one barrier per tile separates writes from reads
+      unsigned char* kl = klds[WR > 1 ? buf : 0];
+      unsigned char* vl = vlds[WR > 1 ? buf : 0];
+      // this wave's share -> LDS as bf16 (swizzled). V of keys outside [k_lo, L) becomes
+      // zero, so that P = 0 times a stale or NaN value cannot reach the accumulator.
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          *reinterpret_cast<u32x4_t*>(klds + klds_off(16 * kt + 4 * u + lq, lr)) = T.k[kt][u];
-      } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+      for (int m = 0; m < NSLOT; ++m) {
+        const int slot = wave + WR * m;
+        const int kv = FP8 ? slot >> 2 : slot >> 3;
+        const int kt = FP8 ? (slot >> 1) & 1 : (slot >> 2) & 1;
+        const int u = FP8 ? slot & 1 : slot & 3;
+        if (!FP8) {
+          const int kk = 16 * kt + 4 * u + lq;
+          u32x4_t v = X.x[m];
+          if (kv == 0) {
+            *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, lr)) = v;
+          } else {
+            const int j = j0 + kk;
+            if (!fast && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, lr)) = v;
+          }
+        } else {
           const int kk = 16 * kt + 8 * u + (lane >> 3);
           const int c8 = lane & 7;
-          const u32x4_t raw = T.k[kt][u];
-          u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
-          u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
-          *reinterpret_cast<u32x4_t*>(klds + klds_off(kk, 2 * c8)) = u32x4_t{c0.x, c0.y, c1.x, c1.y};
-          *reinterpret_cast<u32x4_t*>(klds + klds_off(kk, 2 * c8 + 1)) =
-              u32x4_t{c2.x, c2.y, c3.x, c3.y};
+          u32x4_t raw = X.x[m];
+          if (kv == 1) {
+            const int j = j0 + kk;
+            if (!fast && (j < k_lo || j >= L)) raw = u32x4_t{0, 0, 0, 0};
+          }
+          const u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
+          const u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
+          const u32x4_t lo = {c0.x, c0.y, c1.x, c1.y}, hi = {c2.x, c2.y, c3.x, c3.y};
+          if (kv == 0) {
+            *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, 2 * c8)) = lo;
+            *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, 2 * c8 + 1)) = hi;
+          } else {
+            *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, 2 * c8)) = lo;
+            *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, 2 * c8 + 1)) = hi;
+          }
         }
       }
-    }
-    // S^T = K Q^T : lane holds row lr (+16 t), keys 4 lq + i of each 16-key subtile
-    bf16x8_t kop[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kop[kt][s] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(klds + klds_off(16 * kt + lr, 4 * s + lq)));
-    f32x4_t sacc[NRT][2];
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
+      if (WR > 1) __syncthreads();            // the whole tile is in LDS buffer `buf`
+
+      // S^T = K Q^T : lane (lr, lq) of MFMA s reads key 16 kt + lr, dims 32 s + 8 lq ..;
+      // the result gives lane (lr, lq) row lr and keys 4 lq + i of each 16-key subtile
+      f32x4_t sacc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4_t acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kt][s], qreg[t][s], acc, 0, 0, 0);
-        sacc[t][kt] = acc;
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t kop = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[s], acc, 0, 0, 0);
+        }
+        sacc[kt] = acc;
       }
-    }
 
-    // logits, mask, online softmax; P packed as the B operand of O^T += V^T P^T
-    bf16x8_t pop[NRT];
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
+      // logits, mask, online softmax; P packed as the B operand of O^T += V^T P^T
       float sv[2][4];
       float mt = kNegInf;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float scl = FP8 ? a.softmax_scale * T.ks[kt][i] : a.softmax_scale;
-          float s = __builtin_fmaf(sacc[t][kt][i], scl, T.bias[t][kt][i]);
+          const float scl = FP8 ? a.softmax_scale * X.ks[kt][i] : a.softmax_scale;
+          float sc = __builtin_fmaf(sacc[kt][i], scl, X.bias[kt][i]);
           if (!fast) {
-            const int dist = row_p[t] - (j0 + 16 * kt + 4 * lq + i);
-            const bool vis = row_ok[t] && dist >= 0 && (W == 0 || dist < W);
-            s = vis ? s : kNegInf;
+            const int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
+            const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
+            sc = vis ? sc : kNegInf;
           }
-          sv[kt][i] = s;
-          mt = fmaxf(mt, s);
+          sv[kt][i] = sc;
+          mt = fmaxf(mt, sc);
         }
       }
       mt = wave_max_rows(mt);
@@ -404,17 +495,16 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
       // more than kRescaleSlack, so that the accumulators are rescaled on few tiles;
       // p = exp(s - m) then stays below exp(kRescaleSlack). O and l share m, so the
       // quotient O / l and lse = m + ln l are unchanged by the choice of m.
-      const bool grow = mt > m_run[t] + kRescaleSlack;    // false while mt = -inf
-      if (__ballot(grow) != 0) {                          // wave-uniform
-        const float m_new = grow ? mt : m_run[t];
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[t] - m_new) * kLog2e) : 1.f;
-        l_run[t] *= alpha;
+      const bool grow = mt > m_run + kRescaleSlack;      // false while mt = -inf
+      if (__ballot(grow) != 0) {                         // wave-uniform
+        const float m_new = grow ? mt : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
-        m_run[t] = m_new;
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        m_run = m_new;
       }
-      const float m_use = m_run[t] == kNegInf ? 0.f : m_run[t];
-      const float mb = -m_use * kLog2e;
+      const float mb = -(m_run == kNegInf ? 0.f : m_run) * kLog2e;
       float psum = 0.f;
       float pv[2][4];
 #pragma unroll
@@ -423,102 +513,100 @@ __global__ __launch_bounds__(64) void split_kv_kernel(KernelArgs a) {
         for (int i = 0; i < 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][i], kLog2e, mb));
           psum += p;
-          pv[kt][i] = FP8 ? (p > 0.f ? p * T.vs[kt][i] : 0.f) : p;
+          pv[kt][i] = FP8 ? (p > 0.f ? p * X.vs[kt][i] : 0.f) : p;
         }
       }
-      l_run[t] += psum;
-      u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                    pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
-      pop[t] = __builtin_bit_cast(bf16x8_t, pk);
-    }
+      l_run += psum;
+      const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                          pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pk);
 
-    // O^T += V^T P^T : V^T operand by transpose reads of the LDS tile. Lane (lr, lq)
-    // supplies the address of 4 dims of key 16 e + 4 lq + lr/4; the read returns to lane
-    // lr the dim 16 dt + lr of keys 16 e + 4 lq + 0..3.
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int cc = 2 * dt + ((lr & 3) >> 1);
-      const int k0 = 4 * lq + (lr >> 2);
-      const int k1 = 16 + k0;
-      const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
-      const int off1 = vlds_off(k1, cc) + 8 * (lr & 1);
-      i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(vlds + off0));
-      i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(vlds + off1));
-      u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
-      bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
-#pragma unroll
-      for (int t = 0; t < NRT; ++t)
-        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], o[t][dt], 0, 0, 0);
-    }
-  };
-
-  // ---- main loop: two tiles in flight, chunks of at most kChunkPages pages ----
-  const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-  Tile A, B;
-  for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
-    const int c1 = min(c0 + chunk_keys, j_end);
-    stage_pages(c0, c1);
-    const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
-    load_tile(A, c0);
-    int i = 0;
-    for (; i + 3 <= nt; i += 2) {
-      const int j0 = c0 + i * kTileKeys;
-      load_tile(B, j0 + kTileKeys);
-      process_tile(A, j0);
-      load_tile(A, j0 + 2 * kTileKeys);
-      process_tile(B, j0 + kTileKeys);
-    }
-    if (i + 2 == nt) {              // the last one or two tiles of the chunk
-      const int j0 = c0 + i * kTileKeys;
-      load_tile(B, j0 + kTileKeys);
-      process_tile(A, j0);
-      process_tile(B, j0 + kTileKeys);
-    } else {
-      process_tile(A, c0 + i * kTileKeys);
-    }
-  }
-
-  // ---- epilogue ----
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    const float l = wave_sum_rows(l_run[t]);
-    if (!row_ok[t]) continue;
-    const int rho = 16 * t + lr;
-    const int r = rho / G;
-    const int h = row_h[t];
-    const int64_t row = (int64_t)(b * n + r) * a.num_q_heads + h;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse = l > 0.f ? m_run[t] + __logf(l) : kNegInf;
-    if (a.num_splits == 1) {
-      uint16_t* op = a.out + row * kHeadDim;
+      // O^T += V^T P^T : V^T operand by transpose reads of the LDS tile. Lane (lr, lq)
+      // supplies the address of 4 dims of key 16 e + 4 lq + lr/4; the read returns to
+      // lane lr the dim 16 dt + lr of keys 16 e + 4 lq + 0..3.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const f32x4_t v = o[t][dt] * inv;
-        u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2_t*>(op + 16 * dt + 4 * lq) = w;
+        const int cc = 2 * dt + ((lr & 3) >> 1);
+        const int k0 = 4 * lq + (lr >> 2);
+        const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
+        const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(vl + off0));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(vl + off1));
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, o[dt], 0, 0, 0);
       }
-      if (lq == 0 && a.lse != nullptr) a.lse[row] = lse;
-    } else {
-      float* pp = a.part_o + (row * a.num_splits + split) * kHeadDim;
+    };
+
+    // ---- tile loop: two tiles in flight, chunks of at most kChunkPages pages ----
+    const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
+    Tile A, B;
+    for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+      const int c1 = min(c0 + chunk_keys, j_end);
+      stage_pages(c0, c1);
+      const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+      load_tile(A, c0);
+      int i = 0;
+      for (; i + 3 <= nt; i += 2) {
+        const int j0 = c0 + i * kTileKeys;
+        load_tile(B, j0 + kTileKeys);
+        process_tile(A, j0, 0);
+        load_tile(A, j0 + 2 * kTileKeys);
+        process_tile(B, j0 + kTileKeys, 1);
+      }
+      if (i + 2 == nt) {              // the last one or two tiles of the chunk
+        const int j0 = c0 + i * kTileKeys;
+        load_tile(B, j0 + kTileKeys);
+        process_tile(A, j0, 0);
+        process_tile(B, j0 + kTileKeys, 1);
+      } else {
+        process_tile(A, c0 + i * kTileKeys, 0);
+      }
+    }
+
+    // ---- epilogue: the final row when the piece is the whole unit, else a partial ----
+    const float l = wave_sum_rows(l_run);
+    if (row_ok) {
+      const int64_t row = (int64_t)(b * n + r_of_row) * a.num_q_heads + row_h;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float lse = l > 0.f ? m_run + __logf(l) : kNegInf;
+      if (whole) {
+        uint16_t* op = a.out + row * kHeadDim;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * lq) = o[t][dt] * inv;
-      if (lq == 0) a.part_lse[row * a.num_splits + split] = lse;
+        for (int dt = 0; dt < 8; ++dt) {
+          const f32x4_t v = o[dt] * inv;
+          const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2_t*>(op + 16 * dt + 4 * lq) = w;
+        }
+        if (lq == 0 && a.lse != nullptr) a.lse[row] = lse;
+      } else {
+        const int64_t prow = prow0 + rho;
+        float* pp = a.part_o + prow * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * lq) = o[dt] * inv;
+        if (lq == 0) a.part_lse[prow] = lse;
+      }
     }
   }
 }
 
-// Merge of the split partials (page 2, FA4 kernel: split count from batch, heads and
-// KV length): out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max lse), and
-// lse = max + ln sum w_s. Parts with lse = -inf (no visible key) are skipped.
+// ---------------------------------------------------------------------------------
+// Merge of the partials of a unit that several work-groups shared (page 2, FA4
+// kernel: the KV range is split and merged): out = sum_s w_s O_s / sum_s w_s with
+// w_s = exp(lse_s - max lse), and lse = max + ln sum w_s. Parts with lse = -inf (no
+// visible key) are skipped.
 //
-// One wave per (sequence, row, query head, 32-dim slice). Lane (stripe, c4) merges
-// splits stripe, stripe + 8, ... for dims 4 c4 .. 4 c4 + 3 with a running maximum,
-// issuing the loads of kCombineUnroll splits at once, so that a row's partials arrive
-// in one memory round trip for up to 8 * kCombineUnroll splits; the 8 stripes are then
-// merged with lane shuffles by the same rule.
+// One wave per (sequence, row, query head, 32-dim slice). The wave finds the unit's
+// pieces from the same partition as the split kernel; a unit held whole by one
+// work-group was written by it and is left alone. Lane (stripe, c4) merges pieces
+// stripe, stripe + 8, ... for dims 4 c4 .. 4 c4 + 3 with a running maximum, issuing
+// the loads of kCombineUnroll pieces at once, so that a row's partials arrive in one
+// memory round trip for up to 8 * kCombineUnroll pieces; the 8 stripes are then merged
+// with lane shuffles by the same rule.
+// ---------------------------------------------------------------------------------
 constexpr int kCombineThreads = 64;
 constexpr int kCombineStripes = 8;
 constexpr int kCombineUnroll = 16;
@@ -539,30 +627,48 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) 
   const int stripe = lane >> 3;
   const int64_t row = blockIdx.x / kCombineSlices;      // (b * n + r) * Hq + h
   const int slice = blockIdx.x % kCombineSlices;
-  const int ns = a.num_splits;
-  const float* lp = a.part_lse + row * ns;
-  const float* op = a.part_o + row * ns * kHeadDim + 32 * slice + 4 * c4;
+  const int Hq = a.num_q_heads;
+  const int G = a.group;
+  const int R = G * a.n;
+  const int b = (int)(row / ((int64_t)a.n * Hq));
+  const int rem = (int)(row - (int64_t)b * a.n * Hq);
+  const int r = rem / Hq;
+  const int h = rem - r * Hq;
+  const int g = h / G;
+  const int rho = r * G + (h - g * G);
 
+  const int64_t u = (int64_t)b * a.num_kv_heads + g;
+  int64_t npieces, prow0;                                // piece k: row prow0 + k * R
+  if (a.splits_per_unit > 0) {
+    npieces = a.splits_per_unit;
+    if (npieces == 1) return;                            // written by the split kernel
+    prow0 = u * npieces * R + rho;
+  } else {
+    npieces = a.unit_info[2 * u + 1];                    // recorded by the split kernel
+    if (npieces <= 1) return;                            // a whole unit: already final
+    prow0 = (a.unit_info[2 * u] + u) * R + rho;
+  }
   float m = kNegInf, l = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = stripe; s0 < ns; s0 += kCombineStripes * kCombineUnroll) {
+  for (int64_t k0 = stripe; k0 < npieces; k0 += kCombineStripes * kCombineUnroll) {
     float ls[kCombineUnroll];
     f32x4_t ov[kCombineUnroll];
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
-      const int s = s0 + kCombineStripes * u;
-      ls[u] = s < ns ? lp[s] : kNegInf;
+    for (int v = 0; v < kCombineUnroll; ++v) {
+      const int64_t k = k0 + kCombineStripes * v;
+      ls[v] = k < npieces ? a.part_lse[prow0 + k * R] : kNegInf;
     }
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
-      const int s = s0 + kCombineStripes * u;
-      ov[u] = s < ns ? *reinterpret_cast<const f32x4_t*>(op + (int64_t)s * kHeadDim)
-                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < kCombineUnroll; ++v) {
+      const int64_t k = k0 + kCombineStripes * v;
+      ov[v] = ls[v] != kNegInf ? *reinterpret_cast<const f32x4_t*>(
+                                     a.part_o + (prow0 + k * R) * kHeadDim + 32 * slice + 4 * c4)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
-      if (ls[u] == kNegInf) continue;          // never touch the O of an empty part
-      merge_part(m, l, acc, ls[u], 1.f, ov[u]);
+    for (int v = 0; v < kCombineUnroll; ++v) {
+      if (ls[v] == kNegInf) continue;          // never touch the O of an empty part
+      merge_part(m, l, acc, ls[v], 1.f, ov[v]);
     }
   }
 #pragma unroll
@@ -579,52 +685,51 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) 
   if (stripe == 0) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const f32x4_t v = acc * inv;
-    u32x2_t wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    const u32x2_t wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     *reinterpret_cast<u32x2_t*>(a.out + row * kHeadDim + 32 * slice + 4 * c4) = wv;
     if (slice == 0 && c4 == 0 && a.lse != nullptr)
       a.lse[row] = l > 0.f ? m + __logf(l) : kNegInf;
   }
 }
 
-int launch_split_kv(const KernelArgs& a, int row_tiles, bool fp8, void* stream) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-  dim3 block(64);
-  hipStream_t st = (hipStream_t)stream;
-#define RATTN_LAUNCH(NRT, F8) \
-  hipLaunchKernelGGL((split_kv_kernel<NRT, F8>), grid, block, 0, st, a)
-  switch (row_tiles * 2 + (fp8 ? 1 : 0)) {
-    case 2: RATTN_LAUNCH(1, false); break;
-    case 3: RATTN_LAUNCH(1, true); break;
-    case 4: RATTN_LAUNCH(2, false); break;
-    case 5: RATTN_LAUNCH(2, true); break;
-    case 6: RATTN_LAUNCH(3, false); break;
-    case 7: RATTN_LAUNCH(3, true); break;
-    case 8: RATTN_LAUNCH(4, false); break;
-    case 9: RATTN_LAUNCH(4, true); break;
-    default: return (int)hipErrorInvalidValue;
-  }
-#undef RATTN_LAUNCH
-  return (int)hipGetLastError();
+// ---------------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------------
+// variant index: waves (1, 2, 4), KV format, partition
+#define RATTN_VARIANTS(X)                                                               \
+  X(1, false, false) X(1, true, false) X(2, false, false) X(2, true, false)              \
+  X(4, false, false) X(4, true, false) X(1, false, true) X(1, true, true)                \
+  X(2, false, true) X(2, true, true) X(4, false, true) X(4, true, true)
+
+static int variant_key(int waves, bool fp8, bool even) {
+  return waves * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);
 }
 
-int split_kv_blocks_per_cu(int row_tiles, bool fp8) {
-  int nb = 0;
-  hipError_t e = hipErrorInvalidValue;
-#define RATTN_OCC(NRT, F8) \
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kv_kernel<NRT, F8>, 64, 0)
-  switch (row_tiles * 2 + (fp8 ? 1 : 0)) {
-    case 2: RATTN_OCC(1, false); break;
-    case 3: RATTN_OCC(1, true); break;
-    case 4: RATTN_OCC(2, false); break;
-    case 5: RATTN_OCC(2, true); break;
-    case 6: RATTN_OCC(3, false); break;
-    case 7: RATTN_OCC(3, true); break;
-    case 8: RATTN_OCC(4, false); break;
-    case 9: RATTN_OCC(4, true); break;
-    default: return 0;
+int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream) {
+  const dim3 grid((unsigned)a.split_groups);
+  const hipStream_t st = (hipStream_t)stream;
+  const int key = variant_key(waves, fp8, a.splits_per_unit == 0);
+#define RATTN_LAUNCH(WRV, F8, EV)                                                    \
+  if (key == variant_key(WRV, F8, EV)) {                                             \
+    hipLaunchKernelGGL((split_kv_kernel<WRV, F8, EV>), grid, dim3(64 * WRV), 0, st, a); \
+    return (int)hipGetLastError();                                                   \
   }
+  RATTN_VARIANTS(RATTN_LAUNCH)
+#undef RATTN_LAUNCH
+  return (int)hipErrorInvalidValue;
+}
+
+int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
+  const int key = variant_key(waves, fp8, even);
+  int nb = 0;
+#define RATTN_OCC(WRV, F8, EV)                                                          \
+  if (key == variant_key(WRV, F8, EV)) {                                                \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kv_kernel<WRV, F8, EV>, \
+                                                        64 * WRV, 0) == hipSuccess ? nb : 0; \
+  }
+  RATTN_VARIANTS(RATTN_OCC)
 #undef RATTN_OCC
-  return e == hipSuccess ? nb : 0;
+  return 0;
 }
 
 int launch_combine(const KernelArgs& a, void* stream) {

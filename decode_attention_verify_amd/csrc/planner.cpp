@@ -1,18 +1,31 @@
 // Problem validation and the split planner (host only, no HIP calls).
 //
 // The split count follows the idea on page 2 ("vLLM TML Inkling support", technical
-// optimisation section, FA4 kernel): the number of key-range splits is chosen from the
-// batch size, the head count and the KV length. Here the key is
-// (batch * KV heads, packed rows, visible KV span, compute units): enough work-groups
-// to fill every CU several times over, but no split shorter than a few tiles, because
-// every split costs a partial write and a combine read.
+// optimisation section, FA4 kernel): the key range is split, with the number of splits
+// chosen from the batch size, the head count and the KV length. Here the planner picks
+// the number of split work-groups from (batch * KV heads, visible KV span, compute
+// units, resident work-groups per CU): the kernel divides the whole call's tiles evenly
+// among them, so the choice sets occupancy, and no work-group gets fewer than a few
+// tiles, because every piece of a shared unit costs a partial write and a combine read.
+#include <algorithm>
 #include <cmath>
+#include <cstdint>
 
 #include "internal.h"
 
 namespace rattn {
 
 static bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Tiles of one (sequence, KV head) unit at the planning length: the keys visible to at
+// least one row, plus the slack of aligning the first key down to a tile boundary.
+static int64_t unit_tiles_bound(const rattn_problem& p) {
+  int64_t span = p.window > 0
+                     ? std::min<int64_t>(p.max_seq_len, (int64_t)p.window + p.n_query_rows - 1)
+                     : p.max_seq_len;
+  span += kTileKeys - 1;
+  return (span + kTileKeys - 1) / kTileKeys;
+}
 
 rattn_status validate_problem(const rattn_problem* p) {
   if (p == nullptr) return RATTN_E_INVALID;
@@ -34,50 +47,66 @@ rattn_status validate_problem(const rattn_problem* p) {
   if (!is_pow2(p->page_size) || p->page_size < 16) return RATTN_E_UNSUPPORTED;
   if (p->max_seq_len > (1 << 30)) return RATTN_E_UNSUPPORTED;
   if (p->num_splits > kMaxSplits) return RATTN_E_UNSUPPORTED;
+  // the bias table is indexed with 32-bit element offsets
+  if ((int64_t)p->num_q_heads * ((int64_t)p->dmax + 1) > INT32_MAX) return RATTN_E_UNSUPPORTED;
+  // the work partition multiplies tile counts by the grid size in 64-bit arithmetic
+  const int64_t total = (int64_t)p->batch * p->num_kv_heads * unit_tiles_bound(*p);
+  if (total > ((int64_t)1 << 62) / kMaxGroups) return RATTN_E_UNSUPPORTED;
   return RATTN_OK;
+}
+
+bool uses_even_shares(const rattn_problem& p) {
+  // full-context layers over a batch: sequence lengths may differ by a large factor
+  return p.num_splits == 0 && p.window == 0 && p.batch > 1;
 }
 
 Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int32_t G = p.num_q_heads / p.num_kv_heads;
   const int32_t rows = G * p.n_query_rows;
   Plan pl{};
-  pl.row_tiles = (rows + 15) / 16;
+  pl.waves = waves_for_rows(rows);
   pl.num_cus = num_cus;
   pl.blocks_per_cu = blocks_per_cu;
-  // keys visible to at least one row, plus the slack of aligning the first key down
-  // to a tile boundary
-  int64_t span = p.window > 0 ? std::min<int64_t>(p.max_seq_len, (int64_t)p.window +
-                                                  p.n_query_rows - 1)
-                              : p.max_seq_len;
-  span += kTileKeys - 1;
-  const int64_t tiles = (span + kTileKeys - 1) / kTileKeys;
-  int64_t splits;
+  const int64_t units = (int64_t)p.batch * p.num_kv_heads;
+  const int64_t tiles = unit_tiles_bound(p);
+  const int64_t total = units * tiles;       // tiles of the whole call at the bound
+  // The grid is sized to three quarters of one round of resident work-groups: on
+  // MI355X a 100K-key batch-1 decode streams fastest with 3 of the 4 resident
+  // single-wave work-groups per CU busy (6.26 TB/s, against 6.16 at 4 and 6.06 at 2),
+  // and an integral count per CU beats a fractional one. No work-group gets fewer than
+  // 4 tiles (128 keys): every piece of a shared unit costs a partial and a merge.
+  const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
+  const int64_t target = std::max<int64_t>(1, slots * 3 / 4);
+  int64_t k = 0;                             // pieces per unit; 0 = even shares
+  int64_t groups;
   if (p.num_splits > 0) {
-    splits = p.num_splits;
+    k = std::min<int64_t>(p.num_splits, std::max<int64_t>(1, kMaxGroups / units));
+    groups = k * units;
+  } else if (!uses_even_shares(p)) {
+    // every unit spans about the same keys (a window, or a single sequence): an equal
+    // number of pieces per unit is balanced and needs no search for a work-group's unit
+    k = std::max<int64_t>(1, std::min<int64_t>(target / units, tiles / 4));
+    k = std::min<int64_t>(k, std::max<int64_t>(1, kMaxGroups / units));
+    groups = k * units;
   } else {
-    // One single-wave work-group per split. The grid is sized to one round of resident
-    // work-groups, filled to three quarters: on MI355X a 100K-key batch-1 decode streams
-    // fastest with 3 of the 4 resident waves per CU busy (6.26 TB/s, against 6.16 at 4
-    // and 6.06 at 2), and one round avoids a partly idle second round.
-    const int64_t units = (int64_t)p.batch * p.num_kv_heads;
-    const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
-    const int64_t target = std::max<int64_t>(1, slots * 3 / 4);
-    splits = (target + units - 1) / units;
-    const int64_t min_tiles = 4;   // at least 128 keys per split
-    splits = std::min<int64_t>(splits, std::max<int64_t>(1, tiles / min_tiles));
-    splits = std::max<int64_t>(1, std::min<int64_t>(splits, kMaxSplits));
+    // full-context layers over a batch: lengths may differ by a large factor, so the
+    // whole call's tiles are shared evenly
+    groups = std::min<int64_t>(target, std::max<int64_t>(1, total / 4));
+    groups = std::max<int64_t>(1, std::min<int64_t>(groups, kMaxGroups));
   }
-  const int64_t tiles_per_split = (tiles + splits - 1) / splits;
-  if (p.num_splits == 0) splits = (tiles + tiles_per_split - 1) / tiles_per_split;
-  pl.num_splits = (int32_t)splits;
-  pl.keys_per_split = (int32_t)(tiles_per_split * kTileKeys);
-  if (pl.num_splits > 1) {
-    const int64_t rows_total = (int64_t)p.batch * p.n_query_rows * p.num_q_heads;
-    pl.part_o_floats = rows_total * pl.num_splits * kHeadDim;
-    pl.part_lse_floats = rows_total * pl.num_splits;
-  }
-  // partials, then a 256-byte aligned flag word
-  int64_t bytes = (pl.part_o_floats + pl.part_lse_floats) * 4;
+  pl.split_groups = (int32_t)groups;
+  pl.splits_per_unit = (int32_t)k;
+  pl.num_splits = (int32_t)(k > 0 ? k : (groups + units - 1) / units);
+  pl.keys_per_split = (int32_t)std::min<int64_t>(((total + groups - 1) / groups) * kTileKeys,
+                                                 INT32_MAX);
+  int64_t pieces = 0;                        // partial slots
+  if (k > 1) pieces = groups;
+  if (k == 0 && groups > 1) pieces = groups + units;
+  pl.part_o_floats = pieces * rows * kHeadDim;
+  pl.part_lse_floats = pieces * rows;
+  pl.unit_info_ints = k == 0 ? 2 * units : 0;
+  // partials, unit records, then a 256-byte aligned flag word
+  int64_t bytes = (pl.part_o_floats + pl.part_lse_floats + pl.unit_info_ints) * 4;
   bytes = (bytes + 255) / 256 * 256;
   pl.workspace_bytes = bytes + 256;
   return pl;

@@ -102,19 +102,20 @@ typedef struct {
   int32_t dmax;              /* largest distance with its own bias column (>= 0)          */
   float softmax_scale;       /* multiplies q . k (1/sqrt(head_dim) for the pages' models) */
   int32_t kv_dtype;          /* rattn_kv_dtype                                            */
-  int32_t num_splits;        /* 0 = chosen by the planner; > 0 forces the split count     */
+  int32_t num_splits;        /* 0 = planner; > 0 forces num_splits work-groups per        */
+                             /* (sequence, KV head) unit (at most 4096; grid <= 65536)    */
 } rattn_problem;
 
 typedef struct {
-  int32_t num_splits;        /* key-range splits per (sequence, KV head)                  */
-  int32_t keys_per_split;    /* a multiple of tile_keys                                   */
+  int32_t num_splits;        /* split work-groups per (sequence, KV head), nominal        */
+  int32_t keys_per_split;    /* keys per split work-group at max_seq_len, nominal         */
   int32_t tile_keys;         /* keys per inner-loop step                                  */
-  int32_t row_tiles;         /* 16-row MFMA tiles covering the G * n packed query rows    */
-  int32_t grid_x, grid_y, grid_z;   /* split kernel grid: splits x KV heads x batch       */
-  int32_t combine_blocks;    /* combine work-groups; 0 when num_splits == 1 (no launch)  */
+  int32_t row_tiles;         /* waves per split work-group, one 16-row MFMA tile each     */
+  int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (work-groups, 1, 1)             */
+  int32_t combine_blocks;    /* combine work-groups; 0 when the grid is one work-group    */
   int32_t num_cus;           /* compute units the plan was sized for                      */
   int32_t blocks_per_cu;     /* resident split-kernel work-groups per CU assumed          */
-  int64_t workspace_bytes;   /* partial outputs and log-sum-exps (0 when num_splits == 1) */
+  int64_t workspace_bytes;   /* partial outputs and log-sum-exps, and a flag word         */
 } rattn_plan_info;
 
 /* Validate `prob`, size the launch for the current HIP device and allocate the

@@ -79,14 +79,14 @@ def test_null_arguments():
 
 def test_planner_headline_fills_the_chip():
     info = binding.rattn_plan_describe(headline(), 256)
-    assert info.row_tiles == 1
-    assert info.grid_y == 8 and info.grid_z == 1
-    waves = info.grid_x * info.grid_y * info.grid_z
+    assert info.row_tiles == 1                 # 6 packed rows: one wave per work-group
+    assert info.grid_y == 1 and info.grid_z == 1
     # one round of resident work-groups (4 per CU on gfx950), three quarters full
     assert info.blocks_per_cu == 4
-    assert 0.7 * 256 * 4 <= waves <= 256 * 4, waves
+    assert info.grid_x == 256 * 4 * 3 // 4, info.grid_x
+    units = 8
+    assert info.grid_x * info.keys_per_split >= units * 100000
     assert info.keys_per_split % info.tile_keys == 0
-    assert info.num_splits * info.keys_per_split >= 100000
     assert info.combine_blocks == 48 * 4   # 4 work-groups per output row
 
 
@@ -98,14 +98,22 @@ def test_planner_covers_every_key():
                dict(num_splits=7), dict(num_splits=4096), dict(max_seq_len=1,
                                                                 max_pages_per_seq=1)):
         p = headline(**kw)
+        units = p.batch * p.num_kv_heads
+        span = (min(p.max_seq_len, p.window + p.n_query_rows - 1) if p.window
+                else p.max_seq_len) + 31
+        tiles = -(-span // 32)
         for cus in (1, 80, 256, 304):
             info = binding.rattn_plan_describe(p, cus)
-            span = (min(p.max_seq_len, p.window + p.n_query_rows - 1) if p.window
-                    else p.max_seq_len) + info.tile_keys - 1
-            assert info.num_splits * info.keys_per_split >= span
+            assert info.grid_x * info.keys_per_split >= units * tiles * 32
             if p.num_splits:
-                assert info.num_splits == p.num_splits
-            assert 1 <= info.num_splits <= 4096
-            assert info.row_tiles == -(-(6 * p.n_query_rows) // 16)
-            if info.num_splits == 1:
-                assert info.combine_blocks == 0
+                assert info.grid_x == min(p.num_splits * units, 1 << 16)
+            else:
+                assert info.grid_x <= max(units, units * tiles // 4)
+            assert 1 <= info.grid_x <= 1 << 16
+            rows = 6 * p.n_query_rows
+            assert info.row_tiles == (1 if rows <= 16 else 2 if rows <= 32 else 4)
+            if info.combine_blocks == 0:
+                # nothing to merge: one work-group per (sequence, KV head) unit, or one in all
+                assert info.grid_x in (1, units)
+            else:
+                assert info.workspace_bytes >= info.grid_x * rows * 129 * 4

@@ -88,6 +88,16 @@ def test_gqa_ratios(hq, hkv, n):
     check_case(sp, seed=hq + hkv + n)
 
 
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_even_shares_across_units(n):
+    # a full-context batch of mixed lengths is shared evenly among the work-groups, so
+    # a work-group's tiles run across several (sequence, KV head) units and most units
+    # are split between two work-groups at arbitrary tile boundaries
+    sp = small("full_100k", batch=12, n_rows=n, seq_len=("uniform", n, 700), dmax=1000,
+               name="even")
+    check_case(sp, seed=20 + n)
+
+
 def test_dmax_clamp_on_gpu():
     sp = small("full_100k", batch=2, n_rows=5, seq_len=("uniform", 300, 900), dmax=37,
                name="dmax")
