@@ -97,8 +97,8 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   rattn_plan_s* p = new (std::nothrow) rattn_plan_s();
   if (p == nullptr) return RATTN_E_NOMEM;
   p->prob = *prob;
-  const int32_t rows = prob->num_q_heads / prob->num_kv_heads * prob->n_query_rows;
-  int bpc = rattn::split_kv_blocks_per_cu(rattn::waves_for_rows(rows),
+  int bpc = rattn::split_kv_blocks_per_cu(
+      rattn::waves_for(prob->num_q_heads / prob->num_kv_heads, prob->n_query_rows),
                                           prob->kv_dtype == RATTN_KV_FP8_E4M3,
                                           rattn::uses_even_shares(*prob));
   if (bpc < 1) bpc = rattn::kDefaultBlocksPerCU;

@@ -16,9 +16,23 @@ constexpr int kMaxGroups = 1 << 16;   // largest split-kernel grid
 constexpr int kChunkPages = 512;  // page ids staged in LDS per chunk of a piece
 constexpr int kCombineSlices = 4; // combine work-groups per output row (32 dims each)
 
-// Waves per split work-group for `rows` packed query rows: each wave owns one 16-row
-// MFMA tile of ceil(rows / waves) rows.
-inline int waves_for_rows(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+// Bias slice of one tile: G heads x (32 + n - 1) distances, loaded by the work-group's
+// threads with kBiasPerThread loads each.
+constexpr int kBiasPerThread = 4;
+constexpr int kMaxBiasSlice = 4 * 64 * kBiasPerThread;   // at 4 waves
+
+// Waves per split work-group for G query heads per KV head and n rows: each wave owns
+// one 16-row MFMA tile of ceil(G n / waves) rows. A multi-wave group's threads must
+// cover a tile's bias slice with kBiasPerThread loads each (a single wave gathers its
+// own). Returns 0 when 4 waves do not suffice.
+inline int waves_for(int G, int n) {
+  const int rows = G * n;
+  if (rows <= 16) return 1;
+  int w = rows <= 32 ? 2 : 4;
+  const int slice = G * (kTileKeys + n - 1);
+  if (slice > 64 * w * kBiasPerThread) w = 4;
+  return slice <= 64 * w * kBiasPerThread ? w : 0;
+}
 
 // Planner output: how one rattn_decode call is launched.
 struct Plan {

@@ -19,8 +19,9 @@
 //    operand layout that O^T = V^T * P^T needs, so P never moves between lanes;
 //  * V is staged through LDS (XOR-swizzled 16-byte chunks) and read back transposed
 //    with ds_read_b64_tr_b16, the gfx950 LDS transpose read;
-//  * the bias is read per lane as 4 consecutive distances, shifted by one per verify
-//    row (the sheared access): each row of a head reads the same slice one float over;
+//  * the bias is sheared: per tile, each head of the group needs one contiguous slice of
+//    32 + n - 1 distances, which row r reads shifted by r; the work-group loads the
+//    slices once (coalesced) into LDS and each lane reads its row's entries there;
 //  * online softmax in fp32, one row per lane, row max across the 4 lanes of a row;
 //  * FP8 (OCP E4M3) K/V are decoded exactly to bf16 with v_cvt_pk_f32_fp8; the K scale
 //    multiplies the logit column, the V scale multiplies P before its bf16 rounding.
@@ -199,9 +200,17 @@ __device__ void locate_tile(const KernelArgs& a, int lane, int t, int& b_out, in
 template <int WR, bool FP8, bool EVEN>
 __global__ __launch_bounds__(64 * WR)
 __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char klds[WR > 1 ? 2 : 1][kTileKeys * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char vlds[WR > 1 ? 2 : 1][kTileKeys * 256];
+  constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
+  __shared__ __attribute__((aligned(16))) unsigned char klds[TILE_BUFS][kTileKeys * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[TILE_BUFS][kTileKeys * 256];
   __shared__ int pages_lds[kChunkPages + 1];
+  // Several waves load the bias slice of a tile together and share it through LDS; a
+  // single wave gathers its row's entries one tile ahead in registers, which keeps the
+  // read off each tile's critical path. Both the buffer count and every index into the
+  // buffers derive from STAGE_BIAS (two buffers exactly when several waves share one).
+  constexpr bool STAGE_BIAS = WR > 1;
+  constexpr int BIAS_BUFS = STAGE_BIAS ? 2 : 1;
+  __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? kMaxBiasSlice : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -239,7 +248,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
   struct Tile {
     u32x4_t x[NSLOT];
     f32x4_t ks[2], vs[2];
-    float bias[2][4];
+    // multi-wave groups: this thread's elements of the tile's bias slice; one wave:
+    // the bias of its row for keys 4 lq + i of each subtile, gathered directly
+    float bs[STAGE_BIAS ? kBiasPerThread : 8];
   };
   constexpr int ROW_BYTES = FP8 ? kHeadDim : 2 * kHeadDim;
   // lane offset within a 16-key subtile block: each 16-lane pass of a load reads 256
@@ -304,9 +315,14 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
     // visible to every row at a distance in [0, W-1]
     const int fast_lo = W > 0 ? max(0, L - W) : 0;
     const int fast_hi = L - n - (kTileKeys - 1);
-    // tiles with bias_lo <= j0 <= fast_hi see only distances in [0, Dmax]: their bias
-    // entries are addressed without clamping
-    const int bias_lo = L - 1 - a.dmax;
+    // Bias slice (the sheared access): for a tile starting at key j0, head h of the group
+    // needs distances L-1-j0-pos for pos in [0, 32+n-1): row r reads key j at position
+    // pos = (j - j0) + (n-1-r), so the n rows of a head share one slice, shifted by
+    // their offset. The group loads each head's slice once per tile, with distances
+    // clamped to [0, Dmax] (a masked key reads an in-range entry that the mask
+    // discards), and every lane then reads its row's entries from LDS.
+    const int slice_len = kTileKeys + n - 1;
+    const int slice_elems = G * slice_len;     // <= kMaxBiasSlice (validated)
     const int sub_lo = k_lo & ~15;           // first 16-key subtile holding a visible key
     const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
 
@@ -322,10 +338,24 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
         qreg[s] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
-    // bias entry of this lane's row at distance row_p - 4 lq - j, as an element offset
-    // from the table start once j is subtracted (the table has fewer than 2^31 entries)
+    // this lane's position in its head's slice for key 4 lq of subtile 0, and its row's
+    // table offset (for the direct gather)
+    const int bias_pos = hl_of_row * slice_len + 4 * lq + (n - 1 - r_of_row);
     const int bias_row = row_h * (a.dmax + 1);
-    const int bias_off = bias_row + row_p - 4 * lq;
+    // this thread's slice elements: element e = tid + 64 WR q of the group's slices is
+    // position e % slice_len of head e / slice_len; bs_row is that head's table offset
+    // (-1: no element), bs_pos the position
+    int bs_row[kBiasPerThread], bs_pos[kBiasPerThread];
+    {
+      const int tid = wave * 64 + lane;
+#pragma unroll
+      for (int q = 0; q < kBiasPerThread; ++q) {
+        const int e = tid + 64 * WR * q;
+        const int hl = e / slice_len;
+        bs_pos[q] = e - hl * slice_len;
+        bs_row[q] = e < slice_elems ? (g * G + hl) * (a.dmax + 1) : -1;
+      }
+    }
 
     // ---- page ids ----
     // The ids of the pages a chunk of the piece touches are staged in LDS before its
@@ -382,25 +412,21 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
               (const f32x4_t*)((const unsigned char*)(a.v_scale + tok0[kt]) + sc_off));
         }
       }
-      // bias: row r of head h reads B[h][p_r - j] for its 4 keys; rows of one head read
-      // the same slice shifted by their offset r (the sheared access)
-      if (j0 >= bias_lo && j0 <= fast_hi) {     // uniform: no clamping needed
-        const unsigned char* bb = (const unsigned char*)a.bias;
-        const unsigned o = (unsigned)(bias_off - j0) * 4u;
+      if constexpr (STAGE_BIAS) {
+        // the bias slice elements of this thread (a thread without one re-reads entry 0)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            X.bias[kt][i] =
-                __builtin_nontemporal_load((const float*)(bb + o - 4 * (16 * kt + i)));
-      } else {                                  // distances clamped to [0, Dmax]
+        for (int q = 0; q < kBiasPerThread; ++q) {
+          const int d = min(max(L - 1 - j0 - bs_pos[q], 0), a.dmax);
+          X.bs[q] = ldf_stream(a.bias + (bs_row[q] >= 0 ? (unsigned)(bs_row[q] + d) : 0u));
+        }
+      } else {
+        // row r of head h reads B[h][p_r - j] for its keys, distances clamped to [0, Dmax]
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
-            dist = min(max(dist, 0), a.dmax);
-            X.bias[kt][i] = ldf_stream(a.bias + (unsigned)(bias_row + dist));
+            const int d = min(max(row_p - (j0 + 16 * kt + 4 * lq + i), 0), a.dmax);
+            X.bs[4 * kt + i] = ldf_stream(a.bias + (unsigned)(bias_row + d));
           }
       }
     };
@@ -415,8 +441,15 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
       const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
       // a single wave reuses one LDS buffer (its LDS accesses execute in order); several
       // waves alternate two, so that one barrier per tile separates writes from reads
-      unsigned char* kl = klds[WR > 1 ? buf : 0];
-      unsigned char* vl = vlds[WR > 1 ? buf : 0];
+      unsigned char* kl = klds[TILE_BUFS == 2 ? buf : 0];
+      unsigned char* vl = vlds[TILE_BUFS == 2 ? buf : 0];
+      float* bl = bias_lds[BIAS_BUFS == 2 ? buf : 0];
+      if constexpr (STAGE_BIAS) {
+        const int tid = wave * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < kBiasPerThread; ++q)
+          if (bs_row[q] >= 0) bl[tid + 64 * WR * q] = X.bs[q];
+      }
       // this wave's share -> LDS as bf16 (swizzled). V of keys outside [k_lo, L) becomes
       // zero, so that P = 0 times a stale or NaN value cannot reach the accumulator.
 #pragma unroll
@@ -472,6 +505,16 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
         sacc[kt] = acc;
       }
 
+      // the bias of this lane's row for its keys 4 lq + i of each subtile
+      float bv[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (STAGE_BIAS) bv[kt][i] = bl[bias_pos + 16 * kt + i];
+          else bv[kt][i] = X.bs[4 * kt + i];
+        }
+
       // logits, mask, online softmax; P packed as the B operand of O^T += V^T P^T
       float sv[2][4];
       float mt = kNegInf;
@@ -480,7 +523,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(Kerne
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float scl = FP8 ? a.softmax_scale * X.ks[kt][i] : a.softmax_scale;
-          float sc = __builtin_fmaf(sacc[kt][i], scl, X.bias[kt][i]);
+          float sc = __builtin_fmaf(sacc[kt][i], scl, bv[kt][i]);
           if (!fast) {
             const int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
             const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);

@@ -44,6 +44,9 @@ rattn_status validate_problem(const rattn_problem* p) {
   if (p->head_dim != kHeadDim) return RATTN_E_UNSUPPORTED;
   const int64_t rows = (int64_t)(p->num_q_heads / p->num_kv_heads) * p->n_query_rows;
   if (rows > kMaxRows) return RATTN_E_UNSUPPORTED;
+  // a tile's bias slice (G heads x (32 + n - 1) distances) must fit the work-group's loads
+  if (waves_for(p->num_q_heads / p->num_kv_heads, p->n_query_rows) == 0)
+    return RATTN_E_UNSUPPORTED;
   if (!is_pow2(p->page_size) || p->page_size < 16) return RATTN_E_UNSUPPORTED;
   if (p->max_seq_len > (1 << 30)) return RATTN_E_UNSUPPORTED;
   if (p->num_splits > kMaxSplits) return RATTN_E_UNSUPPORTED;
@@ -64,19 +67,22 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int32_t G = p.num_q_heads / p.num_kv_heads;
   const int32_t rows = G * p.n_query_rows;
   Plan pl{};
-  pl.waves = waves_for_rows(rows);
+  pl.waves = waves_for(G, p.n_query_rows);
   pl.num_cus = num_cus;
   pl.blocks_per_cu = blocks_per_cu;
   const int64_t units = (int64_t)p.batch * p.num_kv_heads;
   const int64_t tiles = unit_tiles_bound(p);
   const int64_t total = units * tiles;       // tiles of the whole call at the bound
-  // The grid is sized to three quarters of one round of resident work-groups: on
-  // MI355X a 100K-key batch-1 decode streams fastest with 3 of the 4 resident
-  // single-wave work-groups per CU busy (6.26 TB/s, against 6.16 at 4 and 6.06 at 2),
-  // and an integral count per CU beats a fractional one. No work-group gets fewer than
-  // 4 tiles (128 keys): every piece of a shared unit costs a partial and a merge.
+  // The grid is one round of resident work-groups. Single-wave groups fill three
+  // quarters of it: on MI355X a 100K-key batch-1 decode streams fastest with 3 of the 4
+  // resident single-wave groups per CU busy (6.26 TB/s, against 6.16 at 4 and 6.06 at
+  // 2), and an integral count per CU beats a fractional one. Multi-wave groups (verify
+  // rows) are bound by each group's per-tile latency, so they fill the whole round (the
+  // 8-row verify workload: 2.57 ms at a full round against 3.30 ms at three quarters).
+  // No work-group gets fewer than 4 tiles (128 keys): every piece of a shared unit costs
+  // a partial and a merge.
   const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
-  const int64_t target = std::max<int64_t>(1, slots * 3 / 4);
+  const int64_t target = std::max<int64_t>(1, pl.waves == 1 ? slots * 3 / 4 : slots);
   int64_t k = 0;                             // pieces per unit; 0 = even shares
   int64_t groups;
   if (p.num_splits > 0) {

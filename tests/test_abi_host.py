@@ -46,6 +46,9 @@ INVALID = [
 UNSUPPORTED = [
     dict(head_dim=64), dict(n_query_rows=11), dict(page_size=24, max_pages_per_seq=6250),
     dict(page_size=8, max_pages_per_seq=12500), dict(num_splits=4097),
+    # 64 query heads per KV head: a tile's bias slice (64 x 32 distances) exceeds what
+    # a work-group stages
+    dict(num_q_heads=512, num_kv_heads=8),
 ]
 
 
