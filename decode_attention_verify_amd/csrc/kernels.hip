@@ -23,7 +23,7 @@
 //    32 + n - 1 distances, which row r reads shifted by r; the work-group loads the
 //    slices once (coalesced) into LDS and each lane reads its row's entries there;
 //  * online softmax in fp32, one row per lane, row max across the 4 lanes of a row;
-//  * FP8 (OCP E4M3) K/V are decoded exactly to bf16 with v_cvt_pk_f32_fp8; the K scale
+//  * FP8 (OCP E4M3) K/V are decoded exactly to bf16 with v_cvt_scalef32_pk_bf16_fp8; the K scale
 //    multiplies the logit column, the V scale multiplies P before its bf16 rounding.
 #include <hip/hip_runtime.h>
 
@@ -69,18 +69,14 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
          ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
-// Four E4M3 codes (one dword) -> four bf16 values (two dwords). Exact: every E4M3
-// value, subnormals included, is a bf16 value, so the bf16 word is the upper half of
-// the fp32 word that v_cvt_pk_f32_fp8 produces.
-// The packed result is bit-cast to two dwords as a whole before its halves are used:
-// this compiler folds a float element extracted from that builtin's float2 result into
-// the other element (element y read as x), which the whole-vector bit cast avoids.
+// Four E4M3 codes (one dword) -> four bf16 values (two dwords), in code order. Exact:
+// every E4M3 value, subnormals included, is a bf16 value. v_cvt_scalef32_pk_bf16_fp8
+// (gfx950) converts two codes per instruction (scale 1); checked on MI355X against the
+// format's definition for all 256 codes, NaN codes included.
 __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(unsigned int w) {
-  const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false));
-  const u32x2_t hi = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true));
   u32x2_t r;
-  r.x = __builtin_amdgcn_perm(lo.y, lo.x, 0x07060302u);   // {bf16(b0), bf16(b1)}
-  r.y = __builtin_amdgcn_perm(hi.y, hi.x, 0x07060302u);   // {bf16(b2), bf16(b3)}
+  r.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  r.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   return r;
 }
 
@@ -199,7 +195,7 @@ __device__ void locate_tile(const KernelArgs& a, int lane, int t, int& b_out, in
 // registers, since every tile's barrier waits on the slowest of the group's waves.
 template <int WR, bool FP8, bool EVEN>
 __global__ __launch_bounds__(64 * WR)
-__attribute__((amdgpu_waves_per_eu(WR == 1 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
+__attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
   constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
   __shared__ __attribute__((aligned(16))) unsigned char klds[TILE_BUFS][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[TILE_BUFS][kTileKeys * 256];

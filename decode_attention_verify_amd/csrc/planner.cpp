@@ -73,16 +73,19 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int64_t units = (int64_t)p.batch * p.num_kv_heads;
   const int64_t tiles = unit_tiles_bound(p);
   const int64_t total = units * tiles;       // tiles of the whole call at the bound
-  // The grid is one round of resident work-groups. Single-wave groups fill three
-  // quarters of it: on MI355X a 100K-key batch-1 decode streams fastest with 3 of the 4
-  // resident single-wave groups per CU busy (6.26 TB/s, against 6.16 at 4 and 6.06 at
-  // 2), and an integral count per CU beats a fractional one. Multi-wave groups (verify
-  // rows) are bound by each group's per-tile latency, so they fill the whole round (the
-  // 8-row verify workload: 2.57 ms at a full round against 3.30 ms at three quarters).
+  // The grid is one round of resident work-groups. Single-wave groups over a bf16
+  // cache fill three quarters of it: on MI355X a 100K-key batch-1 decode streams
+  // fastest with 3 of the 4 resident single-wave groups per CU busy (6.26 TB/s, against
+  // 6.16 at 4 and 6.06 at 2), and an integral count per CU beats a fractional one.
+  // Groups whose per-tile work, not HBM, bounds them fill the whole round: multi-wave
+  // groups (the 8-row verify workload: 2.57 ms at a full round against 3.30 ms at three
+  // quarters) and the E4M3 cache, which decodes every element (the 1M-key decode:
+  // 529 us against 542 us).
   // No work-group gets fewer than 4 tiles (128 keys): every piece of a shared unit costs
   // a partial and a merge.
   const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
-  const int64_t target = std::max<int64_t>(1, pl.waves == 1 ? slots * 3 / 4 : slots);
+  const bool latency_bound = pl.waves > 1 || p.kv_dtype == RATTN_KV_FP8_E4M3;
+  const int64_t target = std::max<int64_t>(1, latency_bound ? slots : slots * 3 / 4);
   int64_t k = 0;                             // pieces per unit; 0 = even shares
   int64_t groups;
   if (p.num_splits > 0) {
