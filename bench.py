@@ -55,6 +55,14 @@ WORKLOADS = {
     "fp8_1m": "full-context layer decode, 48q/8kv, d=128, batch 1, 1 row, 1,048,576 keys, "
               "E4M3 KV + fp32 per-token-per-head scales, paged (page 64)",
     "tiny": "full-context decode, 6q/1kv, d=128, batch 1, 1 row, 2048 keys, contiguous bf16",
+    "v1_full_decode": "full-context layer decode, 64q/8kv, d=128, batch 1, 1 row, 100,000 keys, "
+                      "bf16 paged KV (page 16)",
+    "v1_window_decode": "sliding-window (W=512) layer decode, 64q/16kv, d=128, batch 16, 1 row, "
+                        "seq_lens U[2048,32768], bf16 paged KV (page 16)",
+    "v1_full_verify": "verify, 8 causal rows, 64q/8kv, d=128, batch 4, full layer, seq_lens "
+                      "log-uniform [32768,262144], bf16 paged KV (page 16)",
+    "v1_window_verify": "verify, 9 causal rows, 64q/16kv, d=128, batch 16, W=512, seq_lens "
+                        "U[2048,32768], bf16 paged KV (page 16)",
 }
 
 

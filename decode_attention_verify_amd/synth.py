@@ -86,6 +86,17 @@ def _named_specs():
                            ("loguniform", 32768, 262144), bias_decay=1e-5),
         # FP8 cache at 1M context, page 64
         "fp8_1m": Spec("fp8_1m", 1, 1, 48, 8, 128, 0, 1048575, 64, KV_FP8, 1048576),
+        # the previous model generation's layer shapes (page 1, model table, Inkling
+        # column: full layers 64 query / 8 KV heads, sliding layers 64 / 16 with a window
+        # of 512; page 2, model architecture: up to 9 tokens per step with MTP heads)
+        "v1_full_decode": Spec("v1_full_decode", 1, 1, 64, 8, 128, 0, 131071, 16, KV_BF16,
+                               100000, bias_decay=1e-5),
+        "v1_window_decode": Spec("v1_window_decode", 16, 1, 64, 16, 128, 512, 512, 16,
+                                 KV_BF16, ("uniform", 2048, 32768)),
+        "v1_full_verify": Spec("v1_full_verify", 4, 8, 64, 8, 128, 0, 262143, 16, KV_BF16,
+                               ("loguniform", 32768, 262144), bias_decay=1e-5),
+        "v1_window_verify": Spec("v1_window_verify", 16, 9, 64, 16, 128, 512, 520, 16,
+                                 KV_BF16, ("uniform", 2048, 32768)),
     }
 
 

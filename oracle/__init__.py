@@ -32,6 +32,7 @@ from .formats import bf16_bits_to_f64, e4m3fn_codes_to_f64
 from .attention import relative_attention, partial_attention, visible_keys
 from .combine import combine_partials
 from .bruteforce import bruteforce_attention
+from .append import append_kv, e4m3fn_encode, quantise_rows_e4m3
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -41,4 +42,7 @@ __all__ = [
     "visible_keys",
     "combine_partials",
     "bruteforce_attention",
+    "append_kv",
+    "e4m3fn_encode",
+    "quantise_rows_e4m3",
 ]

@@ -396,7 +396,131 @@ def pin_fp8_cache(orc):
     _brute_vs_oracle(orc, case)
 
 
+# --------------------------------------------------------------------------- KV append
+# The encoder is written from the OCP E4M3 definition; torch's float8_e4m3fn cast (round
+# to nearest even) is the independent library routine it must agree with. The append's
+# placement is checked against positions worked out by hand.
+
+def _torch_e4m3(values_f32):
+    t = torch.from_numpy(np.asarray(values_f32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _all_code_values(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = orc.e4m3fn_codes_to_f64(codes)
+    keep = np.isfinite(vals)
+    return codes[keep], vals[keep]
+
+
+def pin_encode_round_trips_every_code(orc):
+    codes, vals = _all_code_values(orc)
+    enc = orc.e4m3fn_encode(vals)
+    # +0 and -0 both encode by sign; every other finite code is its own encoding
+    assert np.array_equal(enc, codes)
+
+
+def pin_encode_ties_go_to_even_codes(orc):
+    _, vals = _all_code_values(orc)
+    pos = np.unique(vals[vals >= 0])
+    mids = (pos[:-1] + pos[1:]) / 2                     # exact midpoints (binary fractions)
+    mids = np.concatenate([mids, -mids]).astype(np.float32)
+    assert np.array_equal(orc.e4m3fn_encode(mids), _torch_e4m3(mids))
+    # and the chosen code is the even one (lowest bit 0)
+    assert np.all((orc.e4m3fn_encode(mids[mids > 0]) & 1) == 0)
+
+
+def pin_encode_matches_torch_on_random_values(orc):
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.uniform(-448, 448, 200000),
+        rng.normal(0, 1, 200000),
+        rng.uniform(-2.0 ** -5, 2.0 ** -5, 100000),        # subnormal region
+        np.nextafter(np.float32(448), np.float32(0)) * np.ones(3),
+    ]).astype(np.float32)
+    assert np.array_equal(orc.e4m3fn_encode(x), _torch_e4m3(x))
+
+
+def pin_encode_rejects_unclamped(orc):
+    try:
+        orc.e4m3fn_encode(np.array([449.0]))
+    except ValueError:
+        return
+    raise AssertionError("a magnitude above 448 was encoded")
+
+
+def pin_quantise_rows_scale_and_bound(orc):
+    rng = np.random.default_rng(1)
+    x = torch.from_numpy(rng.normal(0, 1, (500, 128)).astype(np.float32)).to(torch.bfloat16)
+    bits = x.view(torch.uint16).numpy()
+    codes, scale = orc.quantise_rows_e4m3(bits)
+    xf = x.float().numpy()
+    amax = np.abs(xf).max(axis=1)
+    assert np.array_equal(scale, (amax / np.float32(448)).astype(np.float32))
+    # the largest magnitude of each row becomes +-448 (code 0x7E / 0xFE)
+    imax = np.abs(xf).argmax(axis=1)
+    assert np.all((codes[np.arange(500), imax] & 0x7F) == 0x7E)
+    # dequantised values are within half a code step of x: relative 2**-4 for normals
+    deq = orc.e4m3fn_codes_to_f64(codes) * scale[:, None]
+    err = np.abs(deq - xf)
+    tol = np.maximum(np.abs(xf) * 2.0 ** -4, scale[:, None] * 2.0 ** -10)
+    assert np.all(err <= tol + 1e-12)
+
+
+def pin_quantise_zero_row(orc):
+    codes, scale = orc.quantise_rows_e4m3(np.zeros((2, 128), dtype=np.uint16))
+    assert np.all(codes == 0) and np.all(scale == 1.0)
+
+
+def pin_append_places_tokens_by_hand(orc):
+    # one sequence of length 5 after a step of n = 3, pages of 2 slots: the new tokens
+    # are positions 2, 3, 4 -> (page_table[1], slot 0), (page_table[1], slot 1),
+    # (page_table[2], slot 0)
+    B, n, Hkv, D, S, P = 1, 3, 2, 4, 2, 5
+    k_new = np.arange(B * n * Hkv * D, dtype=np.uint16).reshape(B, n, Hkv, D) + 100
+    v_new = k_new + 1000
+    table = np.array([[4, 0, 3]], dtype=np.int32)
+    kc = np.full((P, Hkv, S, D), 7, dtype=np.uint16)
+    vc = np.full((P, Hkv, S, D), 9, dtype=np.uint16)
+    k2, v2, _, _ = orc.append_kv(k_new, v_new, table, np.array([5]), kc, vc)
+    want_k, want_v = kc.copy(), vc.copy()
+    for r, (page, slot) in enumerate([(0, 0), (0, 1), (3, 0)]):
+        want_k[page, :, slot, :] = k_new[0, r]
+        want_v[page, :, slot, :] = v_new[0, r]
+    assert np.array_equal(k2, want_k) and np.array_equal(v2, want_v)
+    assert np.array_equal(kc, np.full_like(kc, 7))          # inputs left untouched
+
+
+def pin_append_fp8_rows_are_quantised_rows(orc):
+    rng = np.random.default_rng(2)
+    B, n, Hkv, D, S, P = 2, 2, 3, 128, 4, 6
+    x = torch.from_numpy(rng.normal(0, 1, (B, n, Hkv, D)).astype(np.float32)).to(torch.bfloat16)
+    bits = x.view(torch.uint16).numpy()
+    table = np.array([[1, 2], [4, 0]], dtype=np.int32)
+    lens = np.array([5, 2])
+    kc = np.zeros((P, Hkv, S, D), dtype=np.uint8)
+    ks = np.zeros((P, Hkv, S), dtype=np.float32)
+    k2, v2, ks2, vs2 = orc.append_kv(bits, bits, table, lens, kc, kc.copy(), ks, ks.copy())
+    for b in range(B):
+        for r in range(n):
+            t = lens[b] - n + r
+            page, slot = table[b][t // S], t % S
+            codes, sc = orc.quantise_rows_e4m3(bits[b, r])
+            assert np.array_equal(k2[page, :, slot, :], codes)
+            assert np.array_equal(ks2[page, :, slot], sc)
+            assert np.array_equal(v2[page, :, slot, :], codes)
+
+
 ALL_PINS = [
+    pin_encode_round_trips_every_code,
+    pin_encode_ties_go_to_even_codes,
+    pin_encode_matches_torch_on_random_values,
+    pin_encode_rejects_unclamped,
+    pin_quantise_rows_scale_and_bound,
+    pin_quantise_zero_row,
+    pin_append_places_tokens_by_hand,
+    pin_append_fp8_rows_are_quantised_rows,
+
     pin_zero_bias_is_sdpa,
     pin_bias_is_additive_mask,
     pin_fp8_decode_is_torch,

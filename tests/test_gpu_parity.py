@@ -47,6 +47,26 @@ def test_fp8_1m_sampled():
     check_case(synth.spec("fp8_1m"), seed=0, gen_device="cuda", kv_heads=[0, 7])
 
 
+# ------------------------------------ the previous generation's layer shapes (64q heads)
+
+def test_v1_full_decode():
+    check_case(synth.spec("v1_full_decode"), seed=0, gen_device="cuda")
+
+
+def test_v1_window_decode():
+    check_case(synth.spec("v1_window_decode"), seed=0, gen_device="cuda")
+
+
+def test_v1_full_verify_sampled():
+    check_case(synth.spec("v1_full_verify"), seed=0, gen_device="cuda", batches=[1],
+               kv_heads=None)
+    check_case(synth.spec("v1_full_verify"), seed=0, gen_device="cuda", kv_heads=[5])
+
+
+def test_v1_window_verify():
+    check_case(synth.spec("v1_window_verify"), seed=0, gen_device="cuda")
+
+
 # ---------------------------------------------------------------- sweeps at small sizes
 
 @pytest.mark.parametrize("n", range(1, 9))

@@ -54,6 +54,16 @@ MUTANTS = [
      "w = np.where(np.isneginf(lse_parts), 0.0, np.exp(lse_parts))"),
     ("combine.py", "return out / total[..., None], M + np.log(total)",
      "return out / total[..., None], np.log(total)"),
+    # KV append and the E4M3 encoder
+    ("append.py", "kr = np.where((frac > 0.5) | ((frac == 0.5) & (np.fmod(kr, 2) == 1)), kr + 1, kr)",
+     "kr = np.where(frac >= 0.5, kr + 1, kr)"),                          # ties away from zero
+    ("append.py", "quantum = np.exp2(e - 3)", "quantum = np.exp2(e - 2)"),      # 2 fraction bits
+    ("append.py", "e = np.maximum(e, -6.0)", "e = np.maximum(e, -7.0)"),         # subnormal binade
+    ("append.py", "amax / np.float32(E4M3_MAX)", "amax / np.float32(E4M3_MAX - 1)"),   # scale
+    ("append.py", "t = L - n + r", "t = L - n + r + 1"),                          # position
+    ("append.py", "slot = t % S", "slot = (t + 1) % S"),                          # slot
+    ("append.py", "np.float32(-E4M3_MAX), np.float32(E4M3_MAX))",
+     "np.float32(-E4M3_MAX), np.float32(E4M3_MAX) * 0 + np.float32(400))"),  # clamp
 ]
 
 
