@@ -72,12 +72,13 @@ def load(path=None):
     lib.rattn_debug_flags.argtypes = [vp, i32p, vp]
     lib.rattn_profile_begin.argtypes = [vp, i32, i32]
     lib.rattn_profile_end.argtypes = [vp, f32p, f32p, i32p]
+    lib.rattn_append_kv.argtypes = [ctypes.POINTER(Problem)] + [vp] * 10
     lib.rattn_status_string.argtypes = [ctypes.c_int]
     lib.rattn_status_string.restype = ctypes.c_char_p
     lib.rattn_abi_version.argtypes = []
     for fn in ("rattn_plan", "rattn_plan_describe", "rattn_plan_get_info", "rattn_decode",
                "rattn_free", "rattn_debug_flags", "rattn_profile_begin", "rattn_profile_end",
-               "rattn_abi_version"):
+               "rattn_abi_version", "rattn_append_kv"):
         getattr(lib, fn).restype = ctypes.c_int32
     if lib.rattn_abi_version() != ABI_VERSION:
         raise ImportError("librattn ABI %d, binding expects %d" % (lib.rattn_abi_version(),
@@ -154,8 +155,9 @@ def _stream(stream):
 
 
 def check_shapes(problem, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, bias,
-                 out, lse=None):
-    """Raise ValueError unless every tensor has the shape ``problem`` implies."""
+                 out, lse=None, only=None):
+    """Raise ValueError unless every tensor has the shape ``problem`` implies (all of them,
+    or the names in ``only``)."""
     p = problem
     want = {
         "q": (q, (p.batch, p.n_query_rows, p.num_q_heads, p.head_dim)),
@@ -173,6 +175,8 @@ def check_shapes(problem, q, k_cache, v_cache, k_scale, v_scale, page_table, seq
     elif k_scale is not None or v_scale is not None:
         raise ValueError("k_scale / v_scale are only for the E4M3 cache")
     for name, (t, shape) in want.items():
+        if only is not None and name not in only:
+            continue
         if t is None:
             if name == "lse":
                 continue
@@ -215,6 +219,37 @@ def rattn_decode(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_le
     st = load().rattn_decode(*args)
     if st != RATTN_OK:
         raise RattnError(st, "rattn_decode")
+
+
+def rattn_append_kv(problem, k_new, v_new, page_table, seq_lens, k_cache, v_cache,
+                    k_scale=None, v_scale=None, flags=None, stream=None):
+    """Enqueue the write of each sequence's n newest tokens into the paged cache."""
+    import torch
+    p = problem
+    shape = (p.batch, p.n_query_rows, p.num_kv_heads, p.head_dim)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, the problem needs %s" % (name, tuple(t.shape), shape))
+    check_shapes(p, torch.empty(0), k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                 None, None, None, only=("k_cache", "v_cache", "k_scale", "v_scale",
+                                         "page_table", "seq_lens"))
+    dev = k_new.device
+    args = [
+        ctypes.byref(problem),
+        _ptr(k_new, "k_new", (torch.bfloat16,)),
+        _ptr(v_new, "v_new", (torch.bfloat16,), dev),
+        _ptr(page_table, "page_table", (torch.int32,), dev),
+        _ptr(seq_lens, "seq_lens", (torch.int32,), dev),
+        _ptr(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev),
+        _ptr(v_cache, "v_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev),
+        _ptr(k_scale, "k_scale", (torch.float32,), dev),
+        _ptr(v_scale, "v_scale", (torch.float32,), dev),
+        _ptr(flags, "flags", (torch.int32,), dev),
+        _stream(stream),
+    ]
+    st = load().rattn_append_kv(*args)
+    if st != RATTN_OK:
+        raise RattnError(st, "rattn_append_kv")
 
 
 def rattn_debug_flags(plan, stream=None):

@@ -190,6 +190,39 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
   return RATTN_OK;
 }
 
+rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const void* v_new,
+                             const int32_t* page_table, const int32_t* seq_lens, void* k_cache,
+                             void* v_cache, float* k_scale, float* v_scale, int32_t* flags,
+                             void* stream) {
+  const rattn_status st = rattn::validate_problem(prob);
+  if (st != RATTN_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || page_table == nullptr || seq_lens == nullptr ||
+      k_cache == nullptr || v_cache == nullptr)
+    return RATTN_E_INVALID;
+  const bool fp8 = prob->kv_dtype == RATTN_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return RATTN_E_INVALID;
+  rattn::AppendArgs a{};
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.flags = flags;
+  a.batch = prob->batch;
+  a.n = prob->n_query_rows;
+  a.num_kv_heads = prob->num_kv_heads;
+  a.page_size = prob->page_size;
+  a.page_shift = __builtin_ctz((unsigned)prob->page_size);
+  a.num_pages = prob->num_pages;
+  a.max_pages = prob->max_pages_per_seq;
+  a.max_seq_len = prob->max_seq_len;
+  a.fp8 = fp8 ? 1 : 0;
+  return rattn::launch_append_kv(a, stream) == 0 ? RATTN_OK : RATTN_E_HIP;
+}
+
 rattn_status rattn_free(rattn_plan_t plan) {
   if (plan == nullptr) return RATTN_OK;
   destroy_events(plan);

@@ -87,9 +87,27 @@ struct KernelArgs {
   int32_t splits_per_unit;  // > 0: pieces per unit; 0: even shares of all tiles
 };
 
+// Arguments of the KV-cache append kernel.
+struct AppendArgs {
+  const uint16_t* k_new;    // bf16 [batch][n][Hkv][D]
+  const uint16_t* v_new;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* k_cache;            // bf16 or E4M3 codes [num_pages][Hkv][page_size][D]
+  void* v_cache;
+  float* k_scale;           // fp32 [num_pages][Hkv][page_size] (E4M3 only)
+  float* v_scale;
+  int32_t* flags;           // RATTN_FLAG_* bits, or null
+  int32_t batch, n, num_kv_heads, page_size, page_shift, num_pages, max_pages, max_seq_len;
+  int32_t fp8;
+};
+
+constexpr float kE4M3Max = 448.f;
+
 // Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value.
 int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream);
 int launch_combine(const KernelArgs& a, void* stream);
+int launch_append_kv(const AppendArgs& a, void* stream);
 // Resident split-kernel work-groups per CU for this variant (0 if the query fails).
 int split_kv_blocks_per_cu(int waves, bool fp8, bool even);
 

@@ -140,6 +140,29 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
                           const int32_t* page_table, const int32_t* seq_lens,
                           const float* bias, void* out, float* lse, void* stream);
 
+/* Write the n newest tokens of every sequence into the paged cache: the step just
+ * before rattn_decode (page 3, "vLLM supports Reflection Beam", section on speeding up
+ * the implementation: a fused KV-cache update; page 2's roadmap and page 3's support
+ * section: an FP8 KV cache). `prob` gives the shapes (batch, n_query_rows = new tokens
+ * per sequence, num_kv_heads, page_size, num_pages, max_pages_per_seq, max_seq_len,
+ * kv_dtype) and is validated as for rattn_plan; no plan or workspace is needed.
+ *   k_new, v_new  bf16 [batch][n][num_kv_heads][head_dim], device
+ *   seq_lens      lengths after the step (they count the new tokens); token r of
+ *                 sequence b goes to position L_b - n + r, slot (L_b - n + r) % page_size
+ *                 of page page_table[b][(L_b - n + r) / page_size]
+ *   k_cache ...   as for rattn_decode; written in place
+ *   k_scale ...   E4M3 only: the fp32 scale of each written (token, KV head) row
+ *   flags         device int32, RATTN_FLAG_* bits OR-ed in for skipped rows (nullable)
+ * E4M3 rows: s = max_d |x_d| / 448 (1 for an all-zero row) and codes of clamp(x_d / s,
+ * -448, 448) rounded to the nearest E4M3 value (ties to even), the quotients correctly
+ * rounded in fp32. A sequence whose length is outside [n, max_seq_len], or a token whose
+ * page id is outside [0, num_pages), is not written and sets its flag bit. Asynchronous
+ * on `stream`; allocates nothing. */
+rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const void* v_new,
+                             const int32_t* page_table, const int32_t* seq_lens,
+                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             int32_t* flags, void* stream);
+
 /* Release the plan and its workspace (NULL is accepted). */
 rattn_status rattn_free(rattn_plan_t plan);
 
