@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = "decode-attn µs/step + achieved HBM GB/s; 48q/8kv GQA, d=128, 100K ctx, b=1"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 CACHE_EVICT_BYTES = 1 << 30     # rotate over at least this many input bytes
+PLAN_REPS = 20                  # host planning calls timed (rattn_plan + rattn_free)
 KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/internal.h", "csrc/planner.cpp")
 
 WORKLOADS = {
@@ -187,6 +188,58 @@ def parity_of(out_gpu, lse_gpu, ref_out, ref_lse):
             "mean_abs": float(d.mean()), "lse_rel": float(rel.max())}
 
 
+def bench_append(args, sp, case, prob):
+    """Time rattn_append_kv: each sequence's n newest K and V rows written into the
+    paged cache (quantised to E4M3 with per-row scales for the FP8 cache)."""
+    import torch
+    from decode_attention_verify_amd import accounting, binding
+    fp8 = sp.kv_format == "fp8_e4m3"
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    shape = (sp.batch, sp.n_rows, sp.num_kv_heads, sp.head_dim)
+    k_new = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    v_new = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    byts = accounting.append_traffic(case.seq_lens.tolist(), n_rows=sp.n_rows,
+                                     num_kv_heads=sp.num_kv_heads, head_dim=sp.head_dim,
+                                     page_size=sp.page_size, kv_bytes_per_elem=1 if fp8 else 2)
+
+    def call():
+        binding.rattn_append_kv(prob, k_new, v_new, case.page_table, case.seq_lens,
+                                case.k_cache, case.v_cache, case.k_scale, case.v_scale, flags)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    # events on torch's current stream, the stream the binding launches on
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(flags.item()):
+        raise RuntimeError("device flags %d on valid input" % int(flags.item()))
+    us = (t1 - t0) * 1e6 / args.steps
+    dev_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({
+        "metric": "kv-cache append µs/call (n new tokens per sequence, K and V)",
+        "value": round(us, 3), "unit": "us/call", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16->" + sp.kv_format,
+        "data": "synthetic",
+        "config": {"workload": "append before: " + WORKLOADS[args.workload],
+                   "name": args.workload, "batch": sp.batch, "n_new_tokens": sp.n_rows,
+                   "kv_heads": sp.num_kv_heads, "page_size": sp.page_size},
+        "device_us_per_call": round(dev_us, 3),
+        "algorithmic_bytes": byts,
+        "roofline": {"bound": "hbm", "kernel": "append_kv_kernel",
+                     "achieved": round(byts / (dev_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(byts / (dev_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 5),
+                     "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +255,9 @@ def main():
                     help="record per-kernel HIP events on every N-th timed step")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events (no roofline)")
+    ap.add_argument("--op", default="decode", choices=("decode", "append"),
+                    help="decode: the attention call (default); append: the KV-cache write "
+                         "of each sequence's new tokens, on the same workload's shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -236,6 +292,13 @@ def main():
                             page_size=sp.page_size, kv_bytes_per_elem=1 if fp8 else 2)
 
     prob = binding.problem_from_case(case, args.splits)
+    if args.op == "append":
+        bench_append(args, sp, case, prob)
+        return
+    t = time.perf_counter()
+    for _ in range(PLAN_REPS):
+        binding.rattn_free(binding.rattn_plan(prob))
+    plan_us = (time.perf_counter() - t) / PLAN_REPS * 1e6
     plan = binding.Plan(prob)
     info = plan.info.as_dict()
     say("plan", info)
@@ -295,6 +358,13 @@ def main():
         split_ms, comb_ms = [float("nan")], [float("nan")]
     else:
         split_ms, comb_ms = binding.rattn_profile_end(plan.handle, nrec)
+    # secondary: the same steps on one input copy, whose K/V partly stay in the caches
+    torch.cuda.synchronize()
+    th = time.perf_counter()
+    for i in range(K):
+        step(0)
+    torch.cuda.synchronize()
+    hot_us = (time.perf_counter() - th) * 1e6 / K
     flags = plan.debug_flags()
     if flags:
         raise RuntimeError("device flags %d on valid input" % flags)
@@ -348,8 +418,12 @@ def main():
         "kernels_us": {
             "split_kv_mean": round(split_mean_s * 1e6, 3),
             "split_kv_median": round(srt[len(srt) // 2] * 1e3, 3),
+            "split_kv_p10": round(srt[len(srt) // 10] * 1e3, 3),
+            "split_kv_p90": round(srt[(len(srt) * 9) // 10] * 1e3, 3),
             "combine_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 3),
         },
+        "plan_host_us": round(plan_us, 1),
+        "hot_cache_us_per_step": round(hot_us, 3),
         "roofline": {
             "bound": "hbm",
             "kernel": "split_kv_kernel",

@@ -74,3 +74,16 @@ def traffic(seq_lens, *, n_rows, num_q_heads, num_kv_heads, head_dim, window, dm
 def kv_bytes_per_token_per_layer(num_kv_heads, head_dim, kv_bytes_per_elem):
     """Bytes of K and V that one token adds to one attention layer's cache."""
     return 2 * num_kv_heads * head_dim * kv_bytes_per_elem
+
+
+def append_traffic(seq_lens, *, n_rows, num_kv_heads, head_dim, page_size, kv_bytes_per_elem):
+    """Algorithmic bytes of writing each sequence's n newest tokens into the cache: the
+    new K and V rows read (bf16), the cache rows written (bf16, or E4M3 codes plus one
+    fp32 scale per row), and the lengths and page-table entries read."""
+    seq_lens = [int(x) for x in seq_lens]
+    B = len(seq_lens)
+    rows = B * n_rows * num_kv_heads * 2                     # K and V
+    read = rows * head_dim * 2
+    write = rows * head_dim * kv_bytes_per_elem + (rows * 4 if kv_bytes_per_elem == 1 else 0)
+    pages = sum((L - 1) // page_size - (L - n_rows) // page_size + 1 for L in seq_lens)
+    return read + write + pages * 4 + B * 4

@@ -250,3 +250,23 @@ def make_case(sp, seed=0, device="cpu", poison=True, chunk_tokens=1 << 17):
                 seq_lens=seq_lens.to(torch.int32).to(device), bias=bias,
                 softmax_scale=1.0 / math.sqrt(D), max_seq_len=bound,
                 extra={"spare_page": spare, "pages_per_seq": pages_per_seq})
+
+
+def varlen_rows(case, rows_per_seq):
+    """Packed query rows for a call where sequence b brings rows_per_seq[b] rows (at most
+    the case's n): the last rows_per_seq[b] of its drawn rows, laid end to end. Returns
+    (q [T][Hq][D] bf16, cu_rows [B+1] int32), on the case's device."""
+    n = case.spec.n_rows
+    if len(rows_per_seq) != case.spec.batch or any(not 0 <= x <= n for x in rows_per_seq):
+        raise ValueError("rows per sequence must lie in [0, %d]" % n)
+    parts = [case.q[b, n - x:] for b, x in enumerate(rows_per_seq)]
+    q = torch.cat(parts, 0).contiguous()
+    cu = torch.tensor([0] + list(rows_per_seq), dtype=torch.int64).cumsum(0)
+    return q, cu.to(torch.int32).to(case.q.device)
+
+
+def draw_rows_per_seq(batch, n_max, seed, allow_zero=True):
+    """Seeded rows per sequence, uniform in [0 or 1, n_max]."""
+    g = torch.Generator().manual_seed(seed)
+    lo = 0 if allow_zero else 1
+    return torch.randint(lo, n_max + 1, (batch,), generator=g).tolist()

@@ -33,6 +33,7 @@ from .attention import relative_attention, partial_attention, visible_keys
 from .combine import combine_partials
 from .bruteforce import bruteforce_attention
 from .append import append_kv, e4m3fn_encode, quantise_rows_e4m3
+from .varlen import relative_attention_varlen
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -45,4 +46,5 @@ __all__ = [
     "append_kv",
     "e4m3fn_encode",
     "quantise_rows_e4m3",
+    "relative_attention_varlen",
 ]

@@ -511,6 +511,57 @@ def pin_append_fp8_rows_are_quantised_rows(orc):
             assert np.array_equal(v2[page, :, slot, :], codes)
 
 
+# --------------------------------------------------------------------- rows per sequence
+
+def _varlen_run(orc, case, q, cu):
+    a = _case_arrays(case)
+    sp = case.spec
+    return orc.relative_attention_varlen(q.view(torch.uint16).numpy(), cu.numpy(),
+                                         a["k_cache"], a["v_cache"], a["page_table"],
+                                         a["seq_lens"], a["bias"], window=sp.window,
+                                         dmax=sp.dmax, softmax_scale=case.softmax_scale,
+                                         k_scale=a["k_scale"], v_scale=a["v_scale"])
+
+
+def pin_varlen_brute_force(orc):
+    """Each sequence's n_b rows sit at its last n_b positions: brute force per sequence."""
+    for W in (0, 5):
+        sp = synth.spec("tiny", batch=5, n_rows=8, num_q_heads=4, num_kv_heads=2,
+                        seq_len=("uniform", 9, 30), dmax=40, head_dim=8, window=W,
+                        permute_pages=True)
+        case = synth.make_case(sp, seed=500 + W)
+        rows = [3, 0, 1, 8, 5]
+        q, cu = synth.varlen_rows(case, rows)
+        out, lse = _varlen_run(orc, case, q, cu)
+        k, v = _contiguous_values(orc, case)
+        qd = q.double().numpy()
+        for b, nb in enumerate(rows):
+            if nb == 0:
+                continue
+            L = int(case.seq_lens[b])
+            c0 = int(cu[b])
+            bo, bl = orc.bruteforce_attention([qd[c0:c0 + nb].tolist()], [k[b, :, :L].tolist()],
+                                              [v[b, :, :L].tolist()], [L],
+                                              case.bias.double().numpy().tolist(), window=W,
+                                              dmax=sp.dmax, softmax_scale=case.softmax_scale)
+            _close(out[c0:c0 + nb], np.array(bo)[0], 1e-12, "varlen b=%d out" % b)
+            _close(lse[c0:c0 + nb], np.array(bl)[0], 1e-12, "varlen b=%d lse" % b)
+        assert np.all(np.isnan(out[int(cu[-1]):])), "rows past the last sequence are written"
+
+
+def pin_varlen_uniform_rows_are_fixed(orc):
+    """With n rows in every sequence the packed result is the fixed-row result."""
+    sp = synth.spec("tiny", batch=3, n_rows=4, num_q_heads=6, num_kv_heads=2,
+                    seq_len=("uniform", 20, 70), dmax=80, head_dim=16, window=0,
+                    permute_pages=True, page_size=16)
+    case = synth.make_case(sp, seed=510)
+    q, cu = synth.varlen_rows(case, [4, 4, 4])
+    out, lse = _varlen_run(orc, case, q, cu)
+    ref, ref_lse = _run_case(orc, case)
+    _close(out, ref.reshape(12, 6, 16), 1e-13, "uniform varlen out")
+    _close(lse, ref_lse.reshape(12, 6), 1e-13, "uniform varlen lse")
+
+
 ALL_PINS = [
     pin_encode_round_trips_every_code,
     pin_encode_ties_go_to_even_codes,
@@ -536,4 +587,6 @@ ALL_PINS = [
     pin_dmax_clamp,
     pin_verify_rows_are_shorter_decodes,
     pin_fp8_cache,
+    pin_varlen_brute_force,
+    pin_varlen_uniform_rows_are_fixed,
 ]

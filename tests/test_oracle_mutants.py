@@ -64,6 +64,12 @@ MUTANTS = [
     ("append.py", "slot = t % S", "slot = (t + 1) % S"),                          # slot
     ("append.py", "np.float32(-E4M3_MAX), np.float32(E4M3_MAX))",
      "np.float32(-E4M3_MAX), np.float32(E4M3_MAX) * 0 + np.float32(400))"),  # clamp
+    # rows per sequence
+    ("varlen.py", "o, s = relative_attention(q[cu[b]:cu[b + 1]][None]",
+     "o, s = relative_attention(q[cu[b] + 1:cu[b + 1] + 1][None]"),       # row offset
+    ("varlen.py", "out[cu[b]:cu[b + 1]] = o[0]", "out[cu[b]:cu[b + 1]] = o[0][::-1]"),
+    ("varlen.py", "np.asarray(seq_lens)[b:b + 1], bias",
+     "np.asarray(seq_lens)[b:b + 1] + 1, bias"),                          # position
 ]
 
 
