@@ -15,7 +15,7 @@ ABI_VERSION = 1
 
 RATTN_OK, RATTN_E_INVALID, RATTN_E_UNSUPPORTED, RATTN_E_HIP, RATTN_E_NOMEM = range(5)
 RATTN_KV_BF16, RATTN_KV_FP8_E4M3 = 0, 1
-RATTN_FLAG_SEQ_LEN_CLAMPED, RATTN_FLAG_PAGE_CLAMPED = 1, 2
+RATTN_FLAG_SEQ_LEN_CLAMPED, RATTN_FLAG_PAGE_CLAMPED, RATTN_FLAG_ROWS_INVALID = 1, 2, 4
 
 
 class Problem(ctypes.Structure):
@@ -68,6 +68,7 @@ def load(path=None):
     lib.rattn_plan_describe.argtypes = [ctypes.POINTER(Problem), i32, ctypes.POINTER(PlanInfo)]
     lib.rattn_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.rattn_decode.argtypes = [vp] * 12
+    lib.rattn_decode_varlen.argtypes = [vp] * 9 + [i32] + [vp] * 4
     lib.rattn_free.argtypes = [vp]
     lib.rattn_debug_flags.argtypes = [vp, i32p, vp]
     lib.rattn_profile_begin.argtypes = [vp, i32, i32]
@@ -78,7 +79,7 @@ def load(path=None):
     lib.rattn_abi_version.argtypes = []
     for fn in ("rattn_plan", "rattn_plan_describe", "rattn_plan_get_info", "rattn_decode",
                "rattn_free", "rattn_debug_flags", "rattn_profile_begin", "rattn_profile_end",
-               "rattn_abi_version", "rattn_append_kv"):
+               "rattn_abi_version", "rattn_append_kv", "rattn_decode_varlen"):
         getattr(lib, fn).restype = ctypes.c_int32
     if lib.rattn_abi_version() != ABI_VERSION:
         raise ImportError("librattn ABI %d, binding expects %d" % (lib.rattn_abi_version(),
@@ -221,6 +222,50 @@ def rattn_decode(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_le
         raise RattnError(st, "rattn_decode")
 
 
+def rattn_decode_varlen(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                        cu_rows, bias, out, lse=None, stream=None, problem=None):
+    """Enqueue an attention call where sequence b brings cu_rows[b+1] - cu_rows[b] query
+    rows, packed in q [rows][Hq][D]; out (and lse) hold as many rows as q."""
+    import torch
+    rows = int(q.shape[0])
+    if problem is not None:
+        p = problem
+        if q.dim() != 3 or tuple(q.shape[1:]) != (p.num_q_heads, p.head_dim):
+            raise ValueError("q must be [rows][%d][%d], got %s" % (p.num_q_heads, p.head_dim,
+                                                                   tuple(q.shape)))
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out has shape %s, q %s" % (tuple(out.shape), tuple(q.shape)))
+        if lse is not None and tuple(lse.shape) != (rows, p.num_q_heads):
+            raise ValueError("lse has shape %s, needs %s" % (tuple(lse.shape),
+                                                            (rows, p.num_q_heads)))
+        if tuple(cu_rows.shape) != (p.batch + 1,):
+            raise ValueError("cu_rows has shape %s, needs (%d,)" % (tuple(cu_rows.shape),
+                                                                   p.batch + 1))
+        check_shapes(p, None, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, bias,
+                     None, None, only=("k_cache", "v_cache", "k_scale", "v_scale",
+                                       "page_table", "seq_lens", "bias"))
+    dev = q.device
+    args = [
+        plan,
+        _ptr(q, "q", (torch.bfloat16,)),
+        _ptr(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev),
+        _ptr(v_cache, "v_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev),
+        _ptr(k_scale, "k_scale", (torch.float32,), dev),
+        _ptr(v_scale, "v_scale", (torch.float32,), dev),
+        _ptr(page_table, "page_table", (torch.int32,), dev),
+        _ptr(seq_lens, "seq_lens", (torch.int32,), dev),
+        _ptr(cu_rows, "cu_rows", (torch.int32,), dev),
+        ctypes.c_int32(rows),
+        _ptr(bias, "bias", (torch.float32,), dev),
+        _ptr(out, "out", (torch.bfloat16,), dev),
+        _ptr(lse, "lse", (torch.float32,), dev),
+        _stream(stream),
+    ]
+    st = load().rattn_decode_varlen(*args)
+    if st != RATTN_OK:
+        raise RattnError(st, "rattn_decode_varlen")
+
+
 def rattn_append_kv(problem, k_new, v_new, page_table, seq_lens, k_cache, v_cache,
                     k_scale=None, v_scale=None, flags=None, stream=None):
     """Enqueue the write of each sequence's n newest tokens into the paged cache."""
@@ -291,6 +336,11 @@ class Plan:
                lse=None, stream=None):
         rattn_decode(self.handle, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
                      bias, out, lse, stream, problem=self.problem)
+
+    def decode_varlen(self, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                      cu_rows, bias, out, lse=None, stream=None):
+        rattn_decode_varlen(self.handle, q, k_cache, v_cache, k_scale, v_scale, page_table,
+                            seq_lens, cu_rows, bias, out, lse, stream, problem=self.problem)
 
     def debug_flags(self, stream=None):
         return rattn_debug_flags(self.handle, stream)

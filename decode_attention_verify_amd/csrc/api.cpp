@@ -136,10 +136,15 @@ rattn_status rattn_plan_get_info(rattn_plan_t plan, rattn_plan_info* info) {
   return RATTN_OK;
 }
 
-rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
-                          const void* v_cache, const float* k_scale, const float* v_scale,
-                          const int32_t* page_table, const int32_t* seq_lens,
-                          const float* bias, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
+                         const void* v_cache, const float* k_scale, const float* v_scale,
+                         const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* cu_rows, int32_t row_cap, const float* bias, void* out,
+                         float* lse, void* stream) {
   if (plan == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr ||
       page_table == nullptr || seq_lens == nullptr || bias == nullptr || out == nullptr)
     return RATTN_E_INVALID;
@@ -162,6 +167,8 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
   a.part_lse = a.part_o + plan->plan.part_o_floats;
   a.unit_info = (int32_t*)(a.part_lse + plan->plan.part_lse_floats);
   a.flags = plan->flags;
+  a.cu_rows = cu_rows;
+  a.row_cap = row_cap;
   a.batch = pr.batch;
   a.n = pr.n_query_rows;
   a.num_q_heads = pr.num_q_heads;
@@ -188,6 +195,29 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
   if (needs_combine(plan->plan) && rattn::launch_combine(a, stream) != 0) return RATTN_E_HIP;
   if (ev && hipEventRecord(ev[2], st) != hipSuccess) return RATTN_E_HIP;
   return RATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
+                          const void* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const float* bias, void* out, float* lse, void* stream) {
+  return decode_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                     nullptr, 0, bias, out, lse, stream);
+}
+
+rattn_status rattn_decode_varlen(rattn_plan_t plan, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* page_table,
+                                 const int32_t* seq_lens, const int32_t* cu_rows,
+                                 int32_t num_rows, const float* bias, void* out, float* lse,
+                                 void* stream) {
+  if (plan == nullptr || cu_rows == nullptr || num_rows < 0) return RATTN_E_INVALID;
+  return decode_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                     cu_rows, num_rows, bias, out, lse, stream);
 }
 
 rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const void* v_new,

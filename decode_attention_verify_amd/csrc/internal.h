@@ -79,6 +79,10 @@ struct KernelArgs {
   float* part_lse;
   int32_t* unit_info;
   int32_t* flags;
+  // rows per sequence: null = n rows each, sequence b at rows b*n ..; else sequence b
+  // owns packed rows cu_rows[b] .. cu_rows[b+1]-1 (at most n) of row_cap rows
+  const int32_t* cu_rows;
+  int32_t row_cap;
   int32_t batch, n, num_q_heads, num_kv_heads, group;   // group = Hq / Hkv
   int32_t page_size, page_shift, num_pages, max_pages;
   int32_t max_seq_len, window, dmax;

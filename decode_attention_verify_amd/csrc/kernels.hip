@@ -123,25 +123,48 @@ __device__ __forceinline__ int vlds_off(int k, int cc) {
 //    w, u or both at every piece boundary. Suits batches of very different lengths.
 // A work-group whose piece is a whole unit writes the final output itself.
 // ---------------------------------------------------------------------------------
-struct SeqGeom {
-  int L;       // length (clamped into [n, max_seq_len])
-  int k_lo;    // first key visible to the earliest query row
-  int base;    // k_lo rounded down to a tile boundary
-  int tiles;   // tiles of [base, L)
+// The query rows of sequence b: n each at rows b*n .., or the packed range that
+// cu_rows gives (at most n rows, within the row buffers; else none, flagged).
+struct SeqRows {
+  int base;    // row index of the sequence's first query row in q, out and lse
+  int n;       // its rows, the last n positions of the sequence
 };
 
-__device__ __forceinline__ SeqGeom seq_geom(const KernelArgs& a, int b, bool flag_bad) {
+__device__ __forceinline__ SeqRows seq_rows(const KernelArgs& a, int b, bool flag_bad) {
+  if (a.cu_rows == nullptr) return SeqRows{b * a.n, a.n};
+  const int lo = a.cu_rows[b], hi = a.cu_rows[b + 1];
+  if (lo < 0 || hi < lo || hi - lo > a.n || hi > a.row_cap) {
+    if (flag_bad) atomicOr(a.flags, RATTN_FLAG_ROWS_INVALID);
+    return SeqRows{0, 0};
+  }
+  return SeqRows{lo, hi - lo};
+}
+
+struct SeqGeom {
+  int nb;      // query rows of the sequence
+  int L;       // length (clamped into [nb, max_seq_len])
+  int k_lo;    // first key visible to the earliest query row
+  int base;    // k_lo rounded down to a tile boundary
+  int tiles;   // tiles of [base, L); none for a sequence without rows
+};
+
+__device__ __forceinline__ SeqGeom seq_geom(const KernelArgs& a, int b, int nb, bool flag_bad) {
   int L = a.seq_lens[b];
-  if (L < a.n || L > a.max_seq_len) {
+  if (L < nb || L > a.max_seq_len) {
     if (flag_bad) atomicOr(a.flags, RATTN_FLAG_SEQ_LEN_CLAMPED);
-    L = min(max(L, a.n), a.max_seq_len);
+    L = min(max(L, nb), a.max_seq_len);
   }
   SeqGeom g;
+  g.nb = nb;
   g.L = L;
-  g.k_lo = a.window > 0 ? max(0, L - a.n + 1 - a.window) : 0;
+  g.k_lo = a.window > 0 ? max(0, L - nb + 1 - a.window) : 0;
   g.base = g.k_lo & ~(kTileKeys - 1);
-  g.tiles = (L - g.base + kTileKeys - 1) / kTileKeys;
+  g.tiles = nb > 0 ? (L - g.base + kTileKeys - 1) / kTileKeys : 0;
   return g;
+}
+
+__device__ __forceinline__ SeqGeom seq_geom(const KernelArgs& a, int b, bool flag_bad) {
+  return seq_geom(a, b, seq_rows(a, b, flag_bad).n, flag_bad);
 }
 
 // Tiles of all units (every lane returns the total; below 2^31 by validation).
@@ -275,8 +298,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       prow0 = wg * R;
       more = false;
       if (tile1 == tile0) {
-        // fewer tiles than splits: an empty piece marks its rows, which the combine skips
-        if (row_ok) a.part_lse[prow0 + rho] = kNegInf;
+        // fewer tiles than splits: an empty piece marks its rows, which the combine
+        // skips (a sequence without rows has no tiles and nothing to mark)
+        if (row_ok && r_of_row < sg.nb) a.part_lse[prow0 + rho] = kNegInf;
         return;
       }
     } else {
@@ -304,17 +328,20 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     }
     const int L = sg.L;
     const int k_lo = sg.k_lo;
+    const int nb = sg.nb;                    // this sequence's rows (<= n)
+    const bool row_live = row_ok && r_of_row < nb;
+    const int row_base = seq_rows(a, b, false).base;
     const int j_begin = sg.base + tile0 * kTileKeys;
     const int j_end = min(sg.base + tile1 * kTileKeys, L);
 
     // tiles at or after `fast_lo` and at or before `fast_hi` need no mask: every key is
     // visible to every row at a distance in [0, W-1]
     const int fast_lo = W > 0 ? max(0, L - W) : 0;
-    const int fast_hi = L - n - (kTileKeys - 1);
+    const int fast_hi = L - nb - (kTileKeys - 1);
     // Bias slice (the sheared access): for a tile starting at key j0, head h of the group
-    // needs distances L-1-j0-pos for pos in [0, 32+n-1): row r reads key j at position
-    // pos = (j - j0) + (n-1-r), so the n rows of a head share one slice, shifted by
-    // their offset. The group loads each head's slice once per tile, with distances
+    // needs distances L-1-j0-pos for pos in [0, 32+nb-1): row r reads key j at position
+    // pos = (j - j0) + (nb-1-r), so the nb rows of a head share one slice, shifted by
+    // their offset (the slice is sized for n >= nb rows). The group loads each head's slice once per tile, with distances
     // clamped to [0, Dmax] (a masked key reads an in-range entry that the mask
     // discards), and every lane then reads its row's entries from LDS.
     const int slice_len = kTileKeys + n - 1;
@@ -323,20 +350,21 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
 
     const int row_h = g * G + hl_of_row;
-    const int row_p = L - n + r_of_row;
+    const int row_p = L - nb + r_of_row;
     bf16x8_t qreg[4];
     {
-      const uint16_t* qrow = a.q + ((int64_t)(b * n + r_of_row) * a.num_q_heads + row_h) * kHeadDim;
+      const uint16_t* qrow =
+          a.q + ((int64_t)(row_base + r_of_row) * a.num_q_heads + row_h) * kHeadDim;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         // the K operand of MFMA s gives lane (lr, lq) the dims 32 s + 8 lq .. + 7
-        const u32x4_t v = row_ok ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
+        const u32x4_t v = row_live ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
         qreg[s] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
     // this lane's position in its head's slice for key 4 lq of subtile 0, and its row's
     // table offset (for the direct gather)
-    const int bias_pos = hl_of_row * slice_len + 4 * lq + (n - 1 - r_of_row);
+    const int bias_pos = hl_of_row * slice_len + 4 * lq + max(nb - 1 - r_of_row, 0);
     const int bias_row = row_h * (a.dmax + 1);
     // this thread's slice elements: element e = tid + 64 WR q of the group's slices is
     // position e % slice_len of head e / slice_len; bs_row is that head's table offset
@@ -522,7 +550,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
           float sc = __builtin_fmaf(sacc[kt][i], scl, bv[kt][i]);
           if (!fast) {
             const int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
-            const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
+            const bool vis = row_live && dist >= 0 && (W == 0 || dist < W);
             sc = vis ? sc : kNegInf;
           }
           sv[kt][i] = sc;
@@ -607,8 +635,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
 
     // ---- epilogue: the final row when the piece is the whole unit, else a partial ----
     const float l = wave_sum_rows(l_run);
-    if (row_ok) {
-      const int64_t row = (int64_t)(b * n + r_of_row) * a.num_q_heads + row_h;
+    if (row_live) {
+      const int64_t row = (int64_t)(row_base + r_of_row) * a.num_q_heads + row_h;
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const float lse = l > 0.f ? m_run + __logf(l) : kNegInf;
       if (whole) {
@@ -664,7 +692,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) 
   const int lane = threadIdx.x;
   const int c4 = lane & 7;
   const int stripe = lane >> 3;
-  const int64_t row = blockIdx.x / kCombineSlices;      // (b * n + r) * Hq + h
+  const int64_t row = blockIdx.x / kCombineSlices;      // slot (b * n + r) * Hq + h
   const int slice = blockIdx.x % kCombineSlices;
   const int Hq = a.num_q_heads;
   const int G = a.group;
@@ -675,6 +703,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) 
   const int h = rem - r * Hq;
   const int g = h / G;
   const int rho = r * G + (h - g * G);
+  const SeqRows sr = seq_rows(a, b, false);
+  if (r >= sr.n) return;                                 // no such row in this sequence
+  const int64_t orow = (int64_t)(sr.base + r) * Hq + h;  // the row's place in out and lse
 
   const int64_t u = (int64_t)b * a.num_kv_heads + g;
   int64_t npieces, prow0;                                // piece k: row prow0 + k * R
@@ -725,9 +756,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) 
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const f32x4_t v = acc * inv;
     const u32x2_t wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    *reinterpret_cast<u32x2_t*>(a.out + row * kHeadDim + 32 * slice + 4 * c4) = wv;
+    *reinterpret_cast<u32x2_t*>(a.out + orow * kHeadDim + 32 * slice + 4 * c4) = wv;
     if (slice == 0 && c4 == 0 && a.lse != nullptr)
-      a.lse[row] = l > 0.f ? m + __logf(l) : kNegInf;
+      a.lse[orow] = l > 0.f ? m + __logf(l) : kNegInf;
   }
 }
 

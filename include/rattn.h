@@ -86,6 +86,7 @@ typedef enum {
 /* Debug flag bits reported by rattn_debug_flags. */
 #define RATTN_FLAG_SEQ_LEN_CLAMPED 1   /* a seq_lens entry was outside [n, max_seq_len] */
 #define RATTN_FLAG_PAGE_CLAMPED 2      /* a page id was outside [0, num_pages)          */
+#define RATTN_FLAG_ROWS_INVALID 4      /* a cu_rows range was not within the row buffers */
 
 typedef struct {
   int32_t batch;             /* sequences, >= 1                                          */
@@ -139,6 +140,28 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
                           const void* v_cache, const float* k_scale, const float* v_scale,
                           const int32_t* page_table, const int32_t* seq_lens,
                           const float* bias, void* out, float* lse, void* stream);
+
+/* As rattn_decode, with a different number of query rows per sequence (page 3, "vLLM
+ * supports Reflection Beam", section on DFlash2 and adaptive verification: the verifier
+ * picks per step which drafts to check; page 2, "vLLM TML Inkling support", model
+ * architecture section: up to 9 tokens per step from chained MTP heads). The plan's
+ * n_query_rows is the largest row count of a sequence.
+ *   cu_rows    device int32 [batch + 1], nondecreasing from cu_rows[0] = 0: sequence b
+ *              owns packed rows cu_rows[b] .. cu_rows[b+1]-1, n_b = cu_rows[b+1] -
+ *              cu_rows[b] in [0, n_query_rows], which are its last n_b positions (row i
+ *              at position L_b - n_b + i; L_b >= n_b)
+ *   num_rows   rows that q, out and lse hold (host int; cu_rows[batch] <= num_rows)
+ *   q, out     bf16 [num_rows][num_q_heads][head_dim]; lse fp32 [num_rows][num_q_heads]
+ * Rows past cu_rows[batch] are not written. A sequence whose range is not within
+ * [0, num_rows] or exceeds n_query_rows rows gets no output and sets
+ * RATTN_FLAG_ROWS_INVALID; lengths and page ids are checked as for rattn_decode, against
+ * n_b. Same plan, workspace and stream rules as rattn_decode. */
+rattn_status rattn_decode_varlen(rattn_plan_t plan, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* page_table,
+                                 const int32_t* seq_lens, const int32_t* cu_rows,
+                                 int32_t num_rows, const float* bias, void* out, float* lse,
+                                 void* stream);
 
 /* Write the n newest tokens of every sequence into the paged cache: the step just
  * before rattn_decode (page 3, "vLLM supports Reflection Beam", section on speeding up
