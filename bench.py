@@ -64,6 +64,13 @@ WORKLOADS = {
                       "log-uniform [32768,262144], bf16 paged KV (page 16)",
     "v1_window_verify": "verify, 9 causal rows, 64q/16kv, d=128, batch 16, W=512, seq_lens "
                         "U[2048,32768], bf16 paged KV (page 16)",
+    "tp4_100k": "one GPU's TP4 share of the full-context layer: 12q/2kv, d=128, batch 1, "
+                "1 row, 100,000 keys, bf16 paged KV (page 16)",
+    "tp8_100k": "one GPU's TP8 share of the full-context layer: 6q/1kv, d=128, batch 1, "
+                "1 row, 100,000 keys, bf16 paged KV (page 16)",
+    "verify_b16_varlen": "speculative verify with 1..8 rows per sequence (seeded), 48q/8kv, "
+                         "d=128, batch 16, full layer, seq_lens log-uniform [32768,262144], "
+                         "bf16 paged KV (page 16)",
 }
 
 
@@ -109,7 +116,7 @@ def copy_probe(mib, reps):
     print(json.dumps({"copy_probe_bytes": n, "reps": reps}), flush=True)
 
 
-def cpu_baseline(case_cpu, tr, budget_s):
+def cpu_baseline(case_cpu, tr, budget_s, rows=None, q_packed=None, cu=None):
     """Time the fp64 oracle on the host cores, (sequence, KV head) unit by unit in
     order, repeating whole passes over the step until ``budget_s`` is spent (a pass cut
     short by the budget is scaled to the whole step by its visible-key work)."""
@@ -135,22 +142,39 @@ def cpu_baseline(case_cpu, tr, budget_s):
     vs = None if a.v_scale is None else a.v_scale.numpy()
     G = sp.num_q_heads // sp.num_kv_heads
     lens = [int(x) for x in sl]
-    unit_work = [accounting.rows_keys(L, sp.n_rows, sp.window) for L in lens]
+    nrows = [sp.n_rows] * sp.batch if rows is None else rows
+    unit_work = [accounting.rows_keys(L, n, sp.window) for L, n in zip(lens, nrows)]
     total_work = sum(unit_work) * sp.num_kv_heads
-    out = np.full((sp.batch, sp.n_rows, sp.num_q_heads, sp.head_dim), np.nan)
-    lse = np.full((sp.batch, sp.n_rows, sp.num_q_heads), np.nan)
+    if rows is None:
+        out = np.full((sp.batch, sp.n_rows, sp.num_q_heads, sp.head_dim), np.nan)
+        lse = np.full((sp.batch, sp.n_rows, sp.num_q_heads), np.nan)
+    else:
+        qp = q_packed.view(torch.uint16).numpy()
+        cun = cu.numpy()
+        out = np.full((qp.shape[0], sp.num_q_heads, sp.head_dim), np.nan)
+        lse = np.full((qp.shape[0], sp.num_q_heads), np.nan)
     done_work = 0
     units = 0
     t0 = time.perf_counter()
     while True:
         for b in range(sp.batch):
             for g in range(sp.num_kv_heads):
-                o, l = oracle.relative_attention(
-                    q, kc, vc, pt, sl, bias, n_query_rows=sp.n_rows, window=sp.window,
-                    dmax=sp.dmax, softmax_scale=a.softmax_scale, k_scale=ks, v_scale=vs,
-                    batches=[b], kv_heads=[g])
-                out[b, :, g * G:(g + 1) * G] = o[b, :, g * G:(g + 1) * G]
-                lse[b, :, g * G:(g + 1) * G] = l[b, :, g * G:(g + 1) * G]
+                hs = slice(g * G, (g + 1) * G)
+                if rows is None:
+                    o, l = oracle.relative_attention(
+                        q, kc, vc, pt, sl, bias, n_query_rows=sp.n_rows, window=sp.window,
+                        dmax=sp.dmax, softmax_scale=a.softmax_scale, k_scale=ks, v_scale=vs,
+                        batches=[b], kv_heads=[g])
+                    out[b, :, hs] = o[b, :, hs]
+                    lse[b, :, hs] = l[b, :, hs]
+                else:
+                    o, l = oracle.relative_attention_varlen(
+                        qp, cun, kc, vc, pt, sl, bias, window=sp.window, dmax=sp.dmax,
+                        softmax_scale=a.softmax_scale, k_scale=ks, v_scale=vs, batches=[b],
+                        kv_heads=[g])
+                    rs = slice(int(cun[b]), int(cun[b + 1]))
+                    out[rs, hs] = o[rs, hs]
+                    lse[rs, hs] = l[rs, hs]
                 done_work += unit_work[b]
                 units += 1
                 if time.perf_counter() - t0 >= budget_s:
@@ -298,12 +322,22 @@ def main():
     torch.cuda.synchronize()
     say("inputs drawn in %.1fs" % (time.perf_counter() - t))
     fp8 = sp.kv_format == synth.KV_FP8
+    rows = None
+    if sp.rows_seed is not None:                 # rows per sequence of their own
+        rows = synth.draw_rows_per_seq(sp.batch, sp.n_rows, seed=sp.rows_seed,
+                                       allow_zero=False)
+        q_packed, cu_rows = synth.varlen_rows(case, rows)
+        case = dataclasses.replace(case, q=q_packed)
+        say("rows per sequence", rows)
     tr = accounting.traffic(case.seq_lens.tolist(), n_rows=sp.n_rows,
                             num_q_heads=sp.num_q_heads, num_kv_heads=sp.num_kv_heads,
                             head_dim=sp.head_dim, window=sp.window, dmax=sp.dmax,
-                            page_size=sp.page_size, kv_bytes_per_elem=1 if fp8 else 2)
+                            page_size=sp.page_size, kv_bytes_per_elem=1 if fp8 else 2,
+                            rows_per_seq=rows)
 
     prob = binding.problem_from_case(case, args.splits)
+    if args.op == "append" and rows is not None:
+        raise SystemExit("--op append takes a workload with the same rows in every sequence")
     if args.op == "append":
         bench_append(args, sp, case, prob)
         return
@@ -327,27 +361,39 @@ def main():
             v_cache=case.v_cache.clone(), bias=case.bias.clone(),
             k_scale=None if case.k_scale is None else case.k_scale.clone(),
             v_scale=None if case.v_scale is None else case.v_scale.clone()))
-    out = torch.empty((sp.batch, sp.n_rows, sp.num_q_heads, sp.head_dim),
-                      dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((sp.batch, sp.n_rows, sp.num_q_heads), dtype=torch.float32,
+    out_rows = (sp.batch, sp.n_rows) if rows is None else (case.q.shape[0],)
+    out = torch.empty(out_rows + (sp.num_q_heads, sp.head_dim), dtype=torch.bfloat16,
                       device="cuda")
-    binding.check_shapes(prob, case.q, case.k_cache, case.v_cache, case.k_scale,
-                         case.v_scale, case.page_table, case.seq_lens, case.bias, out, lse)
+    lse = torch.empty(out_rows + (sp.num_q_heads,), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     vp = ctypes.c_void_p
+    p = lambda t: None if t is None else vp(t.data_ptr())   # noqa: E731
+    if rows is None:
+        binding.check_shapes(prob, case.q, case.k_cache, case.v_cache, case.k_scale,
+                             case.v_scale, case.page_table, case.seq_lens, case.bias, out, lse)
+        decode = lib.rattn_decode
 
-    def argv(c):
-        p = lambda t: None if t is None else vp(t.data_ptr())   # noqa: E731
-        return (plan.handle, p(c.q), p(c.k_cache), p(c.v_cache), p(c.k_scale), p(c.v_scale),
-                p(c.page_table), p(c.seq_lens), p(c.bias), p(out), p(lse),
-                vp(stream.cuda_stream))
+        def argv(c):
+            return (plan.handle, p(c.q), p(c.k_cache), p(c.v_cache), p(c.k_scale),
+                    p(c.v_scale), p(c.page_table), p(c.seq_lens), p(c.bias), p(out), p(lse),
+                    vp(stream.cuda_stream))
+    else:
+        # one checked call through the binding; the timed calls reuse its arguments
+        plan.decode_varlen(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale,
+                           case.page_table, case.seq_lens, cu_rows, case.bias, out, lse)
+        decode = lib.rattn_decode_varlen
+
+        def argv(c):
+            return (plan.handle, p(c.q), p(c.k_cache), p(c.v_cache), p(c.k_scale),
+                    p(c.v_scale), p(c.page_table), p(c.seq_lens), p(cu_rows),
+                    ctypes.c_int32(int(c.q.shape[0])), p(c.bias), p(out), p(lse),
+                    vp(stream.cuda_stream))
     calls = [argv(c) for c in copies]
-    decode = lib.rattn_decode
 
     def step(i):
         st = decode(*calls[i % ncopies])
         if st != binding.RATTN_OK:
-            raise binding.RattnError(st, "rattn_decode")
+            raise binding.RattnError(st, "decode")
 
     for i in range(args.warmup):
         step(i)
@@ -409,7 +455,7 @@ def main():
             "workload": WORKLOADS[args.workload],
             "name": args.workload,
             "batch": sp.batch,
-            "n_query_rows": sp.n_rows,
+            "n_query_rows": sp.n_rows if rows is None else rows,
             "q_heads": sp.num_q_heads,
             "kv_heads": sp.num_kv_heads,
             "head_dim": sp.head_dim,
@@ -453,7 +499,9 @@ def main():
     if not args.no_cpu_baseline:
         say("cpu baseline: oracle on the host cores (budget %.0fs)" % args.cpu_budget)
         case_cpu = case.to("cpu")
-        cb, ref_out, ref_lse = cpu_baseline(case_cpu, tr, args.cpu_budget)
+        cb, ref_out, ref_lse = cpu_baseline(case_cpu, tr, args.cpu_budget, rows,
+                                            None if rows is None else case_cpu.q,
+                                            None if rows is None else cu_rows.cpu())
         result["cpu_baseline"] = cb
         # the last step's output against the oracle on the units it computed
         result["parity_vs_oracle"] = parity_of(out, lse, ref_out, ref_lse)

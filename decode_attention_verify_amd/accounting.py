@@ -48,27 +48,35 @@ def rows_keys(L, n, window):
 
 
 def traffic(seq_lens, *, n_rows, num_q_heads, num_kv_heads, head_dim, window, dmax,
-            page_size, kv_bytes_per_elem, with_lse=True):
+            page_size, kv_bytes_per_elem, with_lse=True, rows_per_seq=None):
+    """``rows_per_seq``: each sequence's own row count (default n_rows for all)."""
     seq_lens = [int(x) for x in seq_lens]
-    B = len(seq_lens)
-    spans = [visible_span(L, n_rows, window) for L in seq_lens]
+    rows = [n_rows] * len(seq_lens) if rows_per_seq is None else [int(x) for x in rows_per_seq]
+    live = [(L, n) for L, n in zip(seq_lens, rows) if n > 0]
+    spans = [visible_span(L, n, window) for L, n in live]
     keys = sum(spans)
     kv = keys * num_kv_heads * head_dim * 2 * kv_bytes_per_elem
     scales = keys * num_kv_heads * 2 * 4 if kv_bytes_per_elem == 1 else 0
-    max_dist = max(((window - 1) if window > 0 else (L - 1)) for L in seq_lens)
-    max_dist = min(max_dist, max(seq_lens) - 1)
-    distinct = min(max_dist, dmax) + 1
+    if live:
+        max_dist = max(((window - 1) if window > 0 else (L - 1)) for L, _ in live)
+        max_dist = min(max_dist, max(L for L, _ in live) - 1)
+        distinct = min(max_dist, dmax) + 1
+    else:
+        distinct = 0
     bias = num_q_heads * 4 * distinct
-    q = B * n_rows * num_q_heads * head_dim * 2
+    total_rows = sum(rows)
+    q = total_rows * num_q_heads * head_dim * 2
     out = q
-    lse = B * n_rows * num_q_heads * 4 if with_lse else 0
+    lse = total_rows * num_q_heads * 4 if with_lse else 0
     pages = 0
-    for L, s in zip(seq_lens, spans):
+    for (L, _), s in zip(live, spans):
         lo = L - s
         pages += (L - 1) // page_size - lo // page_size + 1
-    flops = sum(rows_keys(L, n_rows, window) for L in seq_lens) * num_q_heads * 4 * head_dim
+    flops = sum(rows_keys(L, n, window) for L, n in live) * num_q_heads * 4 * head_dim
+    cu = 4 * (len(seq_lens) + 1) if rows_per_seq is not None else 0
     return Traffic(kv=kv, scales=scales, bias=bias, q=q, out=out, lse=lse,
-                   page_table=pages * 4, seq_lens=B * 4, flops=flops, visible_keys=keys)
+                   page_table=pages * 4 + cu, seq_lens=len(seq_lens) * 4, flops=flops,
+                   visible_keys=keys)
 
 
 def kv_bytes_per_token_per_layer(num_kv_heads, head_dim, kv_bytes_per_elem):

@@ -43,7 +43,10 @@ void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* i
   info->grid_y = 1;
   info->grid_z = 1;
   info->combine_blocks =
-      needs_combine(pl) ? p.batch * p.n_query_rows * p.num_q_heads * rattn::kCombineSlices : 0;
+      needs_combine(pl) ? (int32_t)rattn::combine_blocks(
+                              (int64_t)p.batch * p.n_query_rows * p.num_q_heads,
+                              pl.splits_per_unit)
+                        : 0;
   info->num_cus = pl.num_cus;
   info->blocks_per_cu = pl.blocks_per_cu;
   info->workspace_bytes = pl.workspace_bytes;

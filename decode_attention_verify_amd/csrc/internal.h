@@ -14,7 +14,6 @@ constexpr int kMaxRows = 64;      // packed query rows per (sequence, KV head): 
 constexpr int kMaxSplits = 4096;  // largest forced split count per (sequence, KV head)
 constexpr int kMaxGroups = 1 << 16;   // largest split-kernel grid
 constexpr int kChunkPages = 512;  // page ids staged in LDS per chunk of a piece
-constexpr int kCombineSlices = 4; // combine work-groups per output row (32 dims each)
 
 // Bias slice of one tile: G heads x (32 + n - 1) distances, loaded by the work-group's
 // threads with kBiasPerThread loads each.
@@ -111,6 +110,8 @@ constexpr float kE4M3Max = 448.f;
 // Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value.
 int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream);
 int launch_combine(const KernelArgs& a, void* stream);
+// Work-groups of the combine launch for `rows` output rows (host function).
+int64_t combine_blocks(int64_t rows, int splits_per_unit);
 int launch_append_kv(const AppendArgs& a, void* stream);
 // Resident split-kernel work-groups per CU for this variant (0 if the query fails).
 int split_kv_blocks_per_cu(int waves, bool fp8, bool even);

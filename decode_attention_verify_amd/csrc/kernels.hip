@@ -666,18 +666,19 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
 // w_s = exp(lse_s - max lse), and lse = max + ln sum w_s. Parts with lse = -inf (no
 // visible key) are skipped.
 //
-// One wave per (sequence, row, query head, 32-dim slice). The wave finds the unit's
-// pieces from the same partition as the split kernel; a unit held whole by one
-// work-group was written by it and is left alone. Lane (stripe, c4) merges pieces
-// stripe, stripe + 8, ... for dims 4 c4 .. 4 c4 + 3 with a running maximum, issuing
-// the loads of kCombineUnroll pieces at once, so that a row's partials arrive in one
-// memory round trip for up to 8 * kCombineUnroll pieces; the 8 stripes are then merged
-// with lane shuffles by the same rule.
+// A thread (stripe, c4) of an output row merges pieces stripe, stripe + STRIPES, ...
+// for dims 4 c4 .. 4 c4 + 3 of the row's slice with a running maximum, issuing the
+// loads of UNROLL pieces at once (lse and O together), so that up to STRIPES * UNROLL
+// pieces arrive in one memory round trip; the stripes are
+// then merged by the same rule, with lane shuffles inside a wave and through LDS
+// across the waves of a row. The shape follows the number of pieces:
+//   * few pieces per unit: 32 lanes (1 stripe) or 64 (2 stripes) cover a whole row;
+//   * tens of pieces: 8 stripes x 8 lanes per 32-dim slice of a row, one wave each;
+//   * hundreds of pieces: 128 stripes per 32-dim slice, 16 waves (8 pieces in flight
+//     per thread, which fits the 128 registers of a 1024-thread work-group).
+// A unit held whole by one work-group was written by the split kernel and is left
+// alone; a row that its sequence does not have is skipped.
 // ---------------------------------------------------------------------------------
-constexpr int kCombineThreads = 64;
-constexpr int kCombineStripes = 8;
-constexpr int kCombineUnroll = 16;
-
 __device__ __forceinline__ void merge_part(float& m, float& l, f32x4_t& acc, float m2,
                                            float l2, f32x4_t acc2) {
   const float M = fmaxf(m, m2);
@@ -688,61 +689,79 @@ __device__ __forceinline__ void merge_part(float& m, float& l, f32x4_t& acc, flo
   m = M;
 }
 
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) {
-  const int lane = threadIdx.x;
-  const int c4 = lane & 7;
-  const int stripe = lane >> 3;
-  const int64_t row = blockIdx.x / kCombineSlices;      // slot (b * n + r) * Hq + h
-  const int slice = blockIdx.x % kCombineSlices;
+template <int C4S, int STRIPES, int ROWS, int UNROLL>
+__global__ __launch_bounds__(C4S * STRIPES * ROWS) void combine_kernel(KernelArgs a) {
+  constexpr int SLICES = kHeadDim / (4 * C4S);           // work-group slices of a row
+  constexpr int ROW_THREADS = C4S * STRIPES;
+  constexpr int WAVES_PER_ROW = ROW_THREADS > 64 ? ROW_THREADS / 64 : 1;
+  static_assert(ROWS == 1 || ROW_THREADS <= 64, "rows of a work-group stay within a wave");
+  static_assert(ROW_THREADS % 64 == 0 || 64 % ROW_THREADS == 0, "rows tile the waves");
+  __shared__ float red[WAVES_PER_ROW > 1 ? WAVES_PER_ROW * C4S * 6 : 1];
+
+  const int t = threadIdx.x;
+  const int c4 = t % C4S;
+  const int stripe = (t / C4S) % STRIPES;
+  const int64_t slot = (int64_t)blockIdx.x * ROWS + t / ROW_THREADS;
+  const int64_t row = slot / SLICES;                     // slot (b * n + r) * Hq + h
+  const int slice = (int)(slot - row * SLICES);
   const int Hq = a.num_q_heads;
   const int G = a.group;
   const int R = G * a.n;
-  const int b = (int)(row / ((int64_t)a.n * Hq));
-  const int rem = (int)(row - (int64_t)b * a.n * Hq);
+  const int64_t rows = (int64_t)a.batch * a.n * Hq;
+  const int64_t row_c = row < rows ? row : 0;            // a past-the-end slot reads row 0
+  const int b = (int)(row_c / ((int64_t)a.n * Hq));
+  const int rem = (int)(row_c - (int64_t)b * a.n * Hq);
   const int r = rem / Hq;
   const int h = rem - r * Hq;
   const int g = h / G;
   const int rho = r * G + (h - g * G);
   const SeqRows sr = seq_rows(a, b, false);
-  if (r >= sr.n) return;                                 // no such row in this sequence
   const int64_t orow = (int64_t)(sr.base + r) * Hq + h;  // the row's place in out and lse
 
   const int64_t u = (int64_t)b * a.num_kv_heads + g;
   int64_t npieces, prow0;                                // piece k: row prow0 + k * R
   if (a.splits_per_unit > 0) {
     npieces = a.splits_per_unit;
-    if (npieces == 1) return;                            // written by the split kernel
     prow0 = u * npieces * R + rho;
   } else {
     npieces = a.unit_info[2 * u + 1];                    // recorded by the split kernel
-    if (npieces <= 1) return;                            // a whole unit: already final
     prow0 = (a.unit_info[2 * u] + u) * R + rho;
   }
+  // nothing to merge: past the last row, a row the sequence does not have, or a unit
+  // whose output its one work-group wrote (uniform over a row's threads)
+  const bool live = row < rows && r < sr.n && npieces > 1;
+  if (!live) npieces = 0;
+  if (WAVES_PER_ROW == 1 && !live) return;               // no barrier in this shape
+
   float m = kNegInf, l = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = stripe; k0 < npieces; k0 += kCombineStripes * kCombineUnroll) {
-    float ls[kCombineUnroll];
-    f32x4_t ov[kCombineUnroll];
+  const int dim0 = slice * 4 * C4S + 4 * c4;             // first dim of this thread
+  for (int64_t k0 = stripe; k0 < npieces; k0 += STRIPES * UNROLL) {
+    float ls[UNROLL];
+    f32x4_t ov[UNROLL];
 #pragma unroll
-    for (int v = 0; v < kCombineUnroll; ++v) {
-      const int64_t k = k0 + kCombineStripes * v;
+    for (int v = 0; v < UNROLL; ++v) {
+      const int64_t k = k0 + STRIPES * v;
       ls[v] = k < npieces ? a.part_lse[prow0 + k * R] : kNegInf;
     }
+    // the O loads do not wait for the lse loads: a piece past the last reads piece 0
+    // again, and the O of an empty part (which its work-group never wrote) is dropped
+    // after the load, so that both arrive in one memory round trip
 #pragma unroll
-    for (int v = 0; v < kCombineUnroll; ++v) {
-      const int64_t k = k0 + kCombineStripes * v;
-      ov[v] = ls[v] != kNegInf ? *reinterpret_cast<const f32x4_t*>(
-                                     a.part_o + (prow0 + k * R) * kHeadDim + 32 * slice + 4 * c4)
-                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < UNROLL; ++v) {
+      const int64_t k = k0 + STRIPES * v;
+      const int64_t kk = k < npieces ? k : 0;
+      ov[v] = *reinterpret_cast<const f32x4_t*>(a.part_o + (prow0 + kk * R) * kHeadDim + dim0);
     }
 #pragma unroll
-    for (int v = 0; v < kCombineUnroll; ++v) {
-      if (ls[v] == kNegInf) continue;          // never touch the O of an empty part
+    for (int v = 0; v < UNROLL; ++v) {
+      if (ls[v] == kNegInf) continue;          // an empty part: its O is not used
       merge_part(m, l, acc, ls[v], 1.f, ov[v]);
     }
   }
+  // the stripes of a wave
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int off = C4S; off < (ROW_THREADS < 64 ? ROW_THREADS : 64); off <<= 1) {
     const float m2 = __shfl_xor(m, off);
     const float l2 = __shfl_xor(l, off);
     f32x4_t a2;
@@ -752,13 +771,45 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(KernelArgs a) 
     a2[3] = __shfl_xor(acc[3], off);
     merge_part(m, l, acc, m2, l2, a2);
   }
-  if (stripe == 0) {
+  bool writer = stripe == 0;
+  if constexpr (WAVES_PER_ROW > 1) {
+    // the waves of a row: lanes 0 .. C4S-1 of each wave hold its result; wave 0 merges
+    // them, lane (j, c4) taking waves j, j + 64 / C4S, ... before a last shuffle merge
+    constexpr int J = 64 / C4S;
+    const int wave = t >> 6, lane = t & 63;
+    if (lane < C4S) {
+      float* e = red + (wave * C4S + lane) * 6;
+      e[0] = m; e[1] = l; e[2] = acc[0]; e[3] = acc[1]; e[4] = acc[2]; e[5] = acc[3];
+    }
+    __syncthreads();
+    writer = false;
+    if (wave == 0) {
+      m = kNegInf; l = 0.f; acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int w = lane / C4S; w < WAVES_PER_ROW; w += J) {
+        const float* e = red + (w * C4S + c4) * 6;
+        merge_part(m, l, acc, e[0], e[1], f32x4_t{e[2], e[3], e[4], e[5]});
+      }
+#pragma unroll
+      for (int off = C4S; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m, off);
+        const float l2 = __shfl_xor(l, off);
+        f32x4_t a2;
+        a2[0] = __shfl_xor(acc[0], off);
+        a2[1] = __shfl_xor(acc[1], off);
+        a2[2] = __shfl_xor(acc[2], off);
+        a2[3] = __shfl_xor(acc[3], off);
+        merge_part(m, l, acc, m2, l2, a2);
+      }
+      writer = lane < C4S;
+    }
+    if (!live) return;
+  }
+  if (writer) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const f32x4_t v = acc * inv;
     const u32x2_t wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    *reinterpret_cast<u32x2_t*>(a.out + orow * kHeadDim + 32 * slice + 4 * c4) = wv;
-    if (slice == 0 && c4 == 0 && a.lse != nullptr)
-      a.lse[orow] = l > 0.f ? m + __logf(l) : kNegInf;
+    *reinterpret_cast<u32x2_t*>(a.out + orow * kHeadDim + dim0) = wv;
+    if (dim0 == 0 && a.lse != nullptr) a.lse[orow] = l > 0.f ? m + __logf(l) : kNegInf;
   }
 }
 
@@ -802,10 +853,45 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
   return 0;
 }
 
+// The combine's shape for a partition (see combine_kernel): per-unit splits of up to 16
+// pieces take whole rows, 8 per work-group; even shares (a few to a few tens of pieces
+// per unit) whole rows with 2 stripes, 4 per work-group; per-unit splits of 256 pieces
+// or more 16 waves per 32-dim slice; the rest one wave per 32-dim slice.
+enum CombineShape { kCombineRows, kCombineRows2, kCombineSlices4, kCombineWide };
+
+static CombineShape combine_shape(int splits_per_unit) {
+  if (splits_per_unit == 0) return kCombineRows2;
+  if (splits_per_unit <= 16) return kCombineRows;
+  if (splits_per_unit >= 256) return kCombineWide;
+  return kCombineSlices4;
+}
+
+int64_t combine_blocks(int64_t rows, int splits_per_unit) {
+  switch (combine_shape(splits_per_unit)) {
+    case kCombineRows: return (rows + 7) / 8;
+    case kCombineRows2: return (rows + 3) / 4;
+    default: return rows * 4;
+  }
+}
+
 int launch_combine(const KernelArgs& a, void* stream) {
   const int64_t rows = (int64_t)a.batch * a.n * a.num_q_heads;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(rows * kCombineSlices)),
-                     dim3(kCombineThreads), 0, (hipStream_t)stream, a);
+  const dim3 grid((unsigned)combine_blocks(rows, a.splits_per_unit));
+  const hipStream_t st = (hipStream_t)stream;
+  switch (combine_shape(a.splits_per_unit)) {
+    case kCombineRows:
+      hipLaunchKernelGGL((combine_kernel<32, 1, 8, 16>), grid, dim3(256), 0, st, a);
+      break;
+    case kCombineRows2:
+      hipLaunchKernelGGL((combine_kernel<32, 2, 4, 16>), grid, dim3(256), 0, st, a);
+      break;
+    case kCombineWide:
+      hipLaunchKernelGGL((combine_kernel<8, 128, 1, 8>), grid, dim3(1024), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL((combine_kernel<8, 8, 1, 16>), grid, dim3(64), 0, st, a);
+      break;
+  }
   return (int)hipGetLastError();
 }
 

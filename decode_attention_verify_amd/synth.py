@@ -56,6 +56,7 @@ class Spec:
     bias_decay: float = 0.0
     permute_pages: bool = True
     max_seq_len: Optional[int] = None   # planning bound; defaults to the spec's upper bound
+    rows_seed: Optional[int] = None     # if set: rows per sequence drawn in [1, n_rows]
 
     def seq_len_bound(self):
         if self.max_seq_len is not None:
@@ -97,6 +98,17 @@ def _named_specs():
                                ("loguniform", 32768, 262144), bias_decay=1e-5),
         "v1_window_verify": Spec("v1_window_verify", 16, 9, 64, 16, 128, 512, 520, 16,
                                  KV_BF16, ("uniform", 2048, 32768)),
+        # one GPU's share of the headline layer under tensor parallelism over KV heads:
+        # TP4 keeps 2 KV heads and their 12 query heads, TP8 one and its 6
+        "tp4_100k": Spec("tp4_100k", 1, 1, 12, 2, 128, 0, 131071, 16, KV_BF16, 100000,
+                         bias_decay=1e-5),
+        "tp8_100k": Spec("tp8_100k", 1, 1, 6, 1, 128, 0, 131071, 16, KV_BF16, 100000,
+                         bias_decay=1e-5),
+        # verify where each sequence checks its own number of drafts, 1..8 (page 3,
+        # adaptive verification)
+        "verify_b16_varlen": Spec("verify_b16_varlen", 16, 8, 48, 8, 128, 0, 262143, 16,
+                                  KV_BF16, ("loguniform", 32768, 262144), bias_decay=1e-5,
+                                  rows_seed=11),
     }
 
 

@@ -67,6 +67,13 @@ def test_v1_window_verify():
     check_case(synth.spec("v1_window_verify"), seed=0, gen_device="cuda")
 
 
+# ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
+
+@pytest.mark.parametrize("name", ["tp4_100k", "tp8_100k"])
+def test_tensor_parallel_shares(name):
+    check_case(synth.spec(name), seed=0, gen_device="cuda")
+
+
 # ---------------------------------------------------------------- sweeps at small sizes
 
 @pytest.mark.parametrize("n", range(1, 9))
