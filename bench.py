@@ -13,9 +13,9 @@ section on vLLM's optimisations: batch-1 decode at 100K context).
 
 Cache hygiene: the inputs are cloned into enough copies that the steps rotate over at
 least 1 GiB, four times the 256 MiB Infinity Cache, so every step streams its K/V from
-HBM. The K timed steps run back to back, bracketed by device synchronisations; HIP
-events recorded by the library around each kernel give the per-kernel durations used
-for the roofline figure.
+HBM. The K timed steps run back to back, bracketed by device synchronisations; on every
+8th step the library launches its kernels with HIP events that the runtime stamps with
+each kernel's start and end, which give the per-kernel durations of the roofline.
 
 Output: one JSON line (rank 0, N = 1) with the step time, the achieved HBM bandwidth
 over the algorithmic bytes, the roofline of the dominant kernel and the CPU oracle's
@@ -40,7 +40,8 @@ METRIC = "decode-attn µs/step + achieved HBM GB/s; 48q/8kv GQA, d=128, 100K ctx
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 CACHE_EVICT_BYTES = 1 << 30     # rotate over at least this many input bytes
 PLAN_REPS = 20                  # host planning calls timed (rattn_plan + rattn_free)
-KERNEL_SOURCES = ("csrc/kernels.hip", "csrc/internal.h", "csrc/planner.cpp")
+KERNEL_SOURCES = ("csrc/device_common.h", "csrc/split_kv.h", "csrc/internal.h",
+                  "csrc/planner.cpp")   # what decides the split kernel and its launch
 
 WORKLOADS = {
     "full_100k": "full-context layer decode, 48q/8kv, d=128, batch 1, 1 row, 100,000 keys, "
@@ -294,6 +295,9 @@ def main():
     ap.add_argument("--op", default="decode", choices=("decode", "append"),
                     help="decode: the attention call (default); append: the KV-cache write "
                          "of each sequence's new tokens, on the same workload's shapes")
+    ap.add_argument("--hot-cache", action="store_true",
+                    help="after the timed steps, time as many on one input copy (a warm-cache "
+                         "figure, reported beside the main one)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -416,13 +420,15 @@ def main():
         split_ms, comb_ms = [float("nan")], [float("nan")]
     else:
         split_ms, comb_ms = binding.rattn_profile_end(plan.handle, nrec)
-    # secondary: the same steps on one input copy, whose K/V partly stay in the caches
-    torch.cuda.synchronize()
-    th = time.perf_counter()
-    for i in range(K):
-        step(0)
-    torch.cuda.synchronize()
-    hot_us = (time.perf_counter() - th) * 1e6 / K
+    hot_us = None
+    if args.hot_cache:
+        # secondary: the same steps on one input copy, whose K/V partly stay in the caches
+        torch.cuda.synchronize()
+        th = time.perf_counter()
+        for i in range(K):
+            step(0)
+        torch.cuda.synchronize()
+        hot_us = round((time.perf_counter() - th) * 1e6 / K, 3)
     flags = plan.debug_flags()
     if flags:
         raise RuntimeError("device flags %d on valid input" % flags)
@@ -481,7 +487,7 @@ def main():
             "combine_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 3),
         },
         "plan_host_us": round(plan_us, 1),
-        "hot_cache_us_per_step": round(hot_us, 3),
+        "hot_cache_us_per_step": hot_us,
         "roofline": {
             "bound": "hbm",
             "kernel": "split_kv_kernel",

@@ -19,7 +19,7 @@ struct rattn_plan_s {
   int32_t prof_count;
   int32_t prof_stride;      // record every prof_stride-th call
   int64_t prof_calls;       // calls since rattn_profile_begin
-  std::vector<hipEvent_t> prof_events;   // 3 per call: before split, after split, after combine
+  std::vector<hipEvent_t> prof_events;   // 4 per call: split start/end, combine start/end
 };
 
 namespace {
@@ -190,13 +190,13 @@ rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
 
   hipEvent_t* ev = nullptr;
   if (plan->prof_count < plan->prof_max && plan->prof_calls++ % plan->prof_stride == 0)
-    ev = &plan->prof_events[3 * plan->prof_count++];
-  hipStream_t st = (hipStream_t)stream;
-  if (ev && hipEventRecord(ev[0], st) != hipSuccess) return RATTN_E_HIP;
-  if (rattn::launch_split_kv(a, plan->plan.waves, fp8, stream) != 0) return RATTN_E_HIP;
-  if (ev && hipEventRecord(ev[1], st) != hipSuccess) return RATTN_E_HIP;
-  if (needs_combine(plan->plan) && rattn::launch_combine(a, stream) != 0) return RATTN_E_HIP;
-  if (ev && hipEventRecord(ev[2], st) != hipSuccess) return RATTN_E_HIP;
+    ev = &plan->prof_events[4 * plan->prof_count++];
+  if (rattn::launch_split_kv(a, plan->plan.waves, fp8, stream, ev ? ev[0] : nullptr,
+                             ev ? ev[1] : nullptr) != 0)
+    return RATTN_E_HIP;
+  if (needs_combine(plan->plan) &&
+      rattn::launch_combine(a, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != 0)
+    return RATTN_E_HIP;
   return RATTN_OK;
 }
 
@@ -281,10 +281,9 @@ rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls, int32_t s
   if (plan == nullptr || max_calls < 1 || max_calls > (1 << 20) || stride < 1)
     return RATTN_E_INVALID;
   destroy_events(plan);
-  plan->prof_events.resize((size_t)3 * max_calls);
+  plan->prof_events.resize((size_t)4 * max_calls);
   for (size_t i = 0; i < plan->prof_events.size(); ++i) {
-    // timing-only events: without the system-scope fence a record costs a few hundred
-    // nanoseconds of stream time instead of a cache writeback and invalidation
+    // timing-only events, stamped by the kernel launches (no system-scope fence)
     if (hipEventCreateWithFlags(&plan->prof_events[i], hipEventDisableSystemFence) != hipSuccess) {
       plan->prof_events.resize(i);
       destroy_events(plan);
@@ -305,10 +304,14 @@ rattn_status rattn_profile_end(rattn_plan_t plan, float* split_ms, float* combin
   const int32_t n = plan->prof_count;
   rattn_status st = RATTN_OK;
   for (int32_t i = 0; i < n && st == RATTN_OK; ++i) {
-    hipEvent_t* ev = &plan->prof_events[3 * i];
-    if (hipEventSynchronize(ev[2]) != hipSuccess ||
-        hipEventElapsedTime(&split_ms[i], ev[0], ev[1]) != hipSuccess ||
-        hipEventElapsedTime(&combine_ms[i], ev[1], ev[2]) != hipSuccess)
+    hipEvent_t* ev = &plan->prof_events[4 * i];
+    combine_ms[i] = 0.f;
+    if (hipEventSynchronize(ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&split_ms[i], ev[0], ev[1]) != hipSuccess)
+      st = RATTN_E_HIP;
+    else if (needs_combine(plan->plan) &&
+             (hipEventSynchronize(ev[3]) != hipSuccess ||
+              hipEventElapsedTime(&combine_ms[i], ev[2], ev[3]) != hipSuccess))
       st = RATTN_E_HIP;
   }
   *ncalls = n;

@@ -107,9 +107,12 @@ struct AppendArgs {
 
 constexpr float kE4M3Max = 448.f;
 
-// Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value.
-int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream);
-int launch_combine(const KernelArgs& a, void* stream);
+// Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value. With a
+// pair of events (hipEvent_t), the launch stamps them with the kernel's start and end.
+int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream,
+                    void* ev_start = nullptr, void* ev_stop = nullptr);
+int launch_combine(const KernelArgs& a, void* stream, void* ev_start = nullptr,
+                   void* ev_stop = nullptr);
 // Work-groups of the combine launch for `rows` output rows (host function).
 int64_t combine_blocks(int64_t rows, int splits_per_unit);
 int launch_append_kv(const AppendArgs& a, void* stream);

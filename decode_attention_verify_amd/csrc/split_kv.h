@@ -1,0 +1,492 @@
+// The split kernel: the attention of one decode/verify call over a piece of the keys.
+//
+// Method (page 2 "vLLM TML Inkling support", model architecture section): logits
+// s_j = scale * q.k_j + B[h][min(p - j, Dmax)], softmax over the visible keys. Page 1
+// ("vLLM supports Inkling 2 Small", section on vLLM's optimisations) packs the query
+// heads of a GQA group into one tile so that each K/V page is read once per group;
+// page 2 (technical optimisations, FA4 kernel) splits the KV range, with a "sheared"
+// bias access, and merges the splits.
+//
+// Design on gfx950:
+//  * one work-group of 1, 2 or 4 waves per piece of a (sequence, KV head) unit; the G*n
+//    packed query rows (G = Hq/Hkv) go to 16-row MFMA tiles, one per wave (6 rows pad to
+//    16 here, not to 64 as in the pages' Blackwell tile);
+//  * K and V tiles of 32 keys are read with non-temporal 16-byte loads in row order (a
+//    16-lane pass reads 256 contiguous bytes), two tiles in flight, and stored to LDS
+//    with XOR-swizzled 16-byte chunks; page ids are staged in LDS per chunk of pages;
+//  * S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 with K (read back from LDS) as the A
+//    operand; the S^T accumulator layout (lane = query row, 4 keys per lane) is exactly
+//    the B operand layout that O^T = V^T * P^T needs, so P never moves between lanes;
+//  * V is read back transposed with ds_read_b64_tr_b16, the gfx950 LDS transpose read;
+//  * the bias is sheared: per tile, each head of the group needs one contiguous slice of
+//    32 + n - 1 distances, which row r reads shifted by n - 1 - r; multi-wave groups load
+//    the slices once (coalesced) into LDS, a single wave gathers its row's entries;
+//  * online softmax in fp32, one row per lane, row max across the 4 lanes of a row, the
+//    reference point moved only when a tile's maximum passes it by 8 ln 2;
+//  * FP8 (OCP E4M3) K/V are decoded exactly to bf16 with v_cvt_scalef32_pk_bf16_fp8; the
+//    K scale multiplies the logit column, the V scale multiplies P before its bf16
+//    rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "device_common.h"
+
+namespace rattn {
+
+// ---------------------------------------------------------------------------------
+// Split kernel: WR waves per work-group, each owning one 16-row MFMA tile of the G*n
+// packed query rows of a (sequence, KV head) unit (rows per wave: ceil(G*n / WR)).
+// The waves load equal shares of every 32-key K/V tile into registers, store them to
+// a double-buffered LDS tile and meet at one barrier per tile; each wave then attends
+// its rows over the whole tile. Each K/V byte is read from HBM once per unit.
+// ---------------------------------------------------------------------------------
+// Multi-wave work-groups ask for two waves per SIMD (at most 256 VGPRs each): on the
+// 8-row verify workload that beat one wave per SIMD by 1.4x despite a few spilled
+// registers, since every tile's barrier waits on the slowest of the group's waves.
+template <int WR, bool FP8, bool EVEN>
+__global__ __launch_bounds__(64 * WR)
+__attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
+  constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
+  __shared__ __attribute__((aligned(16))) unsigned char klds[TILE_BUFS][kTileKeys * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[TILE_BUFS][kTileKeys * 256];
+  __shared__ int pages_lds[kChunkPages + 1];
+  // Several waves load the bias slice of a tile together and share it through LDS; a
+  // single wave gathers its row's entries one tile ahead in registers, which keeps the
+  // read off each tile's critical path. Both the buffer count and every index into the
+  // buffers derive from STAGE_BIAS (two buffers exactly when several waves share one).
+  constexpr bool STAGE_BIAS = WR > 1;
+  constexpr int BIAS_BUFS = STAGE_BIAS ? 2 : 1;
+  __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? kMaxBiasSlice : 1];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lr = lane & 15;        // key (A operand) / query row (B operand) within a tile
+  const int lq = lane >> 4;        // k-group of the MFMA operands
+  const int n = a.n;
+  const int G = a.group;
+  const int R = G * n;
+  const int S = a.page_size;
+  const int W = a.window;
+  const int64_t Hkv = a.num_kv_heads;
+  const int rpw = (R + WR - 1) / WR;
+
+  const int64_t wg = blockIdx.x;
+  const int k_split = a.splits_per_unit;     // used when !EVEN
+  int T = 0;
+  int64_t P = 0, t_begin = 0, t_end = 0;
+  if (EVEN) {                                // even shares of the whole tile space
+    T = total_tiles(a, lane);
+    P = min((int64_t)gridDim.x, (int64_t)T);
+    if (wg >= P) return;                     // uniform over the work-group
+    t_begin = wg * T / P;
+    t_end = (wg + 1) * T / P;
+  }
+
+  // ---- this wave's query row (row rho of the unit's packed rows) ----
+  const int rho = wave * rpw + lr;
+  const bool row_ok = lr < rpw && rho < R;
+  const int r_of_row = row_ok ? rho / G : 0;
+  const int hl_of_row = row_ok ? rho - r_of_row * G : 0;
+
+  // ---- per-tile registers: this wave's share of the tile's 16-byte loads ----
+  constexpr int SLOTS = FP8 ? 8 : 16;        // 16-byte loads per lane for one whole tile
+  constexpr int NSLOT = SLOTS / WR;
+  struct Tile {
+    u32x4_t x[NSLOT];
+    f32x4_t ks[2], vs[2];
+    // multi-wave groups: this thread's elements of the tile's bias slice; one wave:
+    // the bias of its row for keys 4 lq + i of each subtile, gathered directly
+    float bs[STAGE_BIAS ? kBiasPerThread : 8];
+  };
+  constexpr int ROW_BYTES = FP8 ? kHeadDim : 2 * kHeadDim;
+  // lane offset within a 16-key subtile block: each 16-lane pass of a load reads 256
+  // contiguous bytes (one bf16 row, two E4M3 rows); a pass spread over 16 rows caps the
+  // read rate near 5.2 TB/s on MI355X, against 6.4 TB/s for contiguous passes
+  const unsigned kv_off = FP8 ? (lane >> 3) * 128 + 16 * (lane & 7) : lq * 256 + 16 * lr;
+  const unsigned sc_off = 16 * lq;
+  const unsigned char* kc = (const unsigned char*)a.k_cache;
+  const unsigned char* vc = (const unsigned char*)a.v_cache;
+
+  for (bool more = true; more;) {
+    // ---- the next piece: tiles [tile0, tile1) of unit (b, g) ----
+    int b, g, tile0, tile1;
+    SeqGeom sg;
+    bool whole;
+    int64_t prow0;                           // partial row of packed row 0 of the unit
+    if (!EVEN) {
+      const int64_t u = wg / k_split;
+      const int sidx = (int)(wg - u * k_split);
+      b = (int)(u / Hkv);
+      g = (int)(u - (int64_t)b * Hkv);
+      sg = seq_geom(a, b, true);
+      tile0 = (int)((int64_t)sidx * sg.tiles / k_split);
+      tile1 = (int)((int64_t)(sidx + 1) * sg.tiles / k_split);
+      whole = k_split == 1;
+      prow0 = wg * R;
+      more = false;
+      if (tile1 == tile0) {
+        // fewer tiles than splits: an empty piece marks its rows, which the combine
+        // skips (a sequence without rows has no tiles and nothing to mark)
+        if (row_ok && r_of_row < sg.nb) a.part_lse[prow0 + rho] = kNegInf;
+        return;
+      }
+    } else {
+      int before;
+      locate_tile(a, lane, (int)t_begin, b, before);
+      sg = seq_geom(a, b, false);
+      g = (t_begin - before) / sg.tiles;
+      const int64_t ustart = before + (int64_t)g * sg.tiles;
+      const int64_t uend = ustart + sg.tiles;
+      const int64_t piece_end = min(t_end, uend);
+      tile0 = (int)(t_begin - ustart);
+      tile1 = (int)(piece_end - ustart);
+      whole = t_begin == ustart && piece_end == uend;
+      const int64_t u = (int64_t)b * Hkv + g;
+      prow0 = (wg + u) * R;
+      if (t_begin == ustart && lane == 0 && wave == 0) {
+        // the unit's first work-group records where its pieces are, for the combine
+        // (one piece: the unit is whole and its output final)
+        const int64_t w_last = (uend * P - 1) / T;
+        a.unit_info[2 * u] = (int)wg;
+        a.unit_info[2 * u + 1] = (int)(w_last - wg + 1);
+      }
+      t_begin = piece_end;
+      more = t_begin < t_end;
+    }
+    const int L = sg.L;
+    const int k_lo = sg.k_lo;
+    const int nb = sg.nb;                    // this sequence's rows (<= n)
+    const bool row_live = row_ok && r_of_row < nb;
+    const int row_base = seq_rows(a, b, false).base;
+    const int j_begin = sg.base + tile0 * kTileKeys;
+    const int j_end = min(sg.base + tile1 * kTileKeys, L);
+
+    // tiles at or after `fast_lo` and at or before `fast_hi` need no mask: every key is
+    // visible to every row at a distance in [0, W-1]
+    const int fast_lo = W > 0 ? max(0, L - W) : 0;
+    const int fast_hi = L - nb - (kTileKeys - 1);
+    // Bias slice (the sheared access): for a tile starting at key j0, head h of the group
+    // needs distances L-1-j0-pos for pos in [0, 32+nb-1): row r reads key j at position
+    // pos = (j - j0) + (nb-1-r), so the nb rows of a head share one slice, shifted by
+    // their offset (the slice is sized for n >= nb rows). The group loads each head's slice once per tile, with distances
+    // clamped to [0, Dmax] (a masked key reads an in-range entry that the mask
+    // discards), and every lane then reads its row's entries from LDS.
+    const int slice_len = kTileKeys + n - 1;
+    const int slice_elems = G * slice_len;     // <= kMaxBiasSlice (validated)
+    const int sub_lo = k_lo & ~15;           // first 16-key subtile holding a visible key
+    const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
+
+    const int row_h = g * G + hl_of_row;
+    const int row_p = L - nb + r_of_row;
+    bf16x8_t qreg[4];
+    {
+      const uint16_t* qrow =
+          a.q + ((int64_t)(row_base + r_of_row) * a.num_q_heads + row_h) * kHeadDim;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // the K operand of MFMA s gives lane (lr, lq) the dims 32 s + 8 lq .. + 7
+        const u32x4_t v = row_live ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
+        qreg[s] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    // this lane's position in its head's slice for key 4 lq of subtile 0, and its row's
+    // table offset (for the direct gather)
+    const int bias_pos = hl_of_row * slice_len + 4 * lq + max(nb - 1 - r_of_row, 0);
+    const int bias_row = row_h * (a.dmax + 1);
+    // this thread's slice elements: element e = tid + 64 WR q of the group's slices is
+    // position e % slice_len of head e / slice_len; bs_row is that head's table offset
+    // (-1: no element), bs_pos the position
+    int bs_row[kBiasPerThread], bs_pos[kBiasPerThread];
+    {
+      const int tid = wave * 64 + lane;
+#pragma unroll
+      for (int q = 0; q < kBiasPerThread; ++q) {
+        const int e = tid + 64 * WR * q;
+        const int hl = e / slice_len;
+        bs_pos[q] = e - hl * slice_len;
+        bs_row[q] = e < slice_elems ? (g * G + hl) * (a.dmax + 1) : -1;
+      }
+    }
+
+    // ---- page ids ----
+    // The ids of the pages a chunk of the piece touches are staged in LDS before its
+    // tile loop, so that the loop looks them up with an LDS read: a page-table load in
+    // the loop would make every tile wait for all of its predecessors' K/V loads.
+    const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
+    int chunk_p0 = 0;
+    auto stage_pages = [&](int c0, int c1) {
+      if (WR > 1) __syncthreads();           // the previous chunk's ids and tiles are done
+      chunk_p0 = c0 >> a.page_shift;
+      const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
+      for (int i = (int)threadIdx.x; i < np; i += 64 * WR) {
+        int ph = pt_row[chunk_p0 + i];
+        if (ph < 0 || ph >= a.num_pages) {
+          atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
+          ph = min(max(ph, 0), a.num_pages - 1);
+        }
+        pages_lds[i] = ph;
+      }
+      if (WR > 1) __syncthreads();
+    };
+    auto phys_at = [&](int jt) -> int {     // physical page of key jt of the current chunk
+      const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
+      return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
+    };
+
+    // Every load of a tile is issued unconditionally, so that the compiler can count the
+    // loads in flight and wait for exactly one tile at a time. A subtile with no key in
+    // [k_lo, L) (at the two ends of the visible range) reads the nearest subtile that
+    // has one instead; the masks of process_tile discard its keys.
+    auto load_tile = [&](Tile& X, int j0) {
+      int64_t tok0[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int js = min(max(j0 + 16 * kt, sub_lo), sub_hi);
+        tok0[kt] = ((int64_t)phys_at(js) * Hkv + g) * S + (js & (S - 1));
+      }
+#pragma unroll
+      for (int m = 0; m < NSLOT; ++m) {
+        // slot = (K|V, subtile, 1 KiB block of the subtile)
+        const int slot = wave + WR * m;
+        const int kv = FP8 ? slot >> 2 : slot >> 3;
+        const int kt = FP8 ? (slot >> 1) & 1 : (slot >> 2) & 1;
+        const int u = FP8 ? slot & 1 : slot & 3;
+        const unsigned char* base = (kv ? vc : kc) + tok0[kt] * ROW_BYTES;
+        X.x[m] = ld16_stream(base + kv_off + 1024 * u);
+      }
+      if (FP8) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          X.ks[kt] = __builtin_nontemporal_load(
+              (const f32x4_t*)((const unsigned char*)(a.k_scale + tok0[kt]) + sc_off));
+          X.vs[kt] = __builtin_nontemporal_load(
+              (const f32x4_t*)((const unsigned char*)(a.v_scale + tok0[kt]) + sc_off));
+        }
+      }
+      if constexpr (STAGE_BIAS) {
+        // the bias slice elements of this thread (a thread without one re-reads entry 0)
+#pragma unroll
+        for (int q = 0; q < kBiasPerThread; ++q) {
+          const int d = min(max(L - 1 - j0 - bs_pos[q], 0), a.dmax);
+          X.bs[q] = ldf_stream(a.bias + (bs_row[q] >= 0 ? (unsigned)(bs_row[q] + d) : 0u));
+        }
+      } else {
+        // row r of head h reads B[h][p_r - j] for its keys, distances clamped to [0, Dmax]
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = min(max(row_p - (j0 + 16 * kt + 4 * lq + i), 0), a.dmax);
+            X.bs[4 * kt + i] = ldf_stream(a.bias + (unsigned)(bias_row + d));
+          }
+      }
+    };
+
+    // ---- running state of this lane's row ----
+    f32x4_t o[8];
+    float m_run = kNegInf, l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0, 0, 0, 0};
+
+    auto process_tile = [&](const Tile& X, int j0, int buf) {
+      const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
+      // a single wave reuses one LDS buffer (its LDS accesses execute in order); several
+      // waves alternate two, so that one barrier per tile separates writes from reads
+      unsigned char* kl = klds[TILE_BUFS == 2 ? buf : 0];
+      unsigned char* vl = vlds[TILE_BUFS == 2 ? buf : 0];
+      float* bl = bias_lds[BIAS_BUFS == 2 ? buf : 0];
+      if constexpr (STAGE_BIAS) {
+        const int tid = wave * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < kBiasPerThread; ++q)
+          if (bs_row[q] >= 0) bl[tid + 64 * WR * q] = X.bs[q];
+      }
+      // this wave's share -> LDS as bf16 (swizzled). V of keys outside [k_lo, L) becomes
+      // zero, so that P = 0 times a stale or NaN value cannot reach the accumulator.
+#pragma unroll
+      for (int m = 0; m < NSLOT; ++m) {
+        const int slot = wave + WR * m;
+        const int kv = FP8 ? slot >> 2 : slot >> 3;
+        const int kt = FP8 ? (slot >> 1) & 1 : (slot >> 2) & 1;
+        const int u = FP8 ? slot & 1 : slot & 3;
+        if (!FP8) {
+          const int kk = 16 * kt + 4 * u + lq;
+          u32x4_t v = X.x[m];
+          if (kv == 0) {
+            *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, lr)) = v;
+          } else {
+            const int j = j0 + kk;
+            if (!fast && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
+            *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, lr)) = v;
+          }
+        } else {
+          const int kk = 16 * kt + 8 * u + (lane >> 3);
+          const int c8 = lane & 7;
+          u32x4_t raw = X.x[m];
+          if (kv == 1) {
+            const int j = j0 + kk;
+            if (!fast && (j < k_lo || j >= L)) raw = u32x4_t{0, 0, 0, 0};
+          }
+          const u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
+          const u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
+          const u32x4_t lo = {c0.x, c0.y, c1.x, c1.y}, hi = {c2.x, c2.y, c3.x, c3.y};
+          if (kv == 0) {
+            *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, 2 * c8)) = lo;
+            *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, 2 * c8 + 1)) = hi;
+          } else {
+            *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, 2 * c8)) = lo;
+            *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, 2 * c8 + 1)) = hi;
+          }
+        }
+      }
+      if (WR > 1) __syncthreads();            // the whole tile is in LDS buffer `buf`
+
+      // S^T = K Q^T : lane (lr, lq) of MFMA s reads key 16 kt + lr, dims 32 s + 8 lq ..;
+      // the result gives lane (lr, lq) row lr and keys 4 lq + i of each 16-key subtile
+      f32x4_t sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t kop = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[s], acc, 0, 0, 0);
+        }
+        sacc[kt] = acc;
+      }
+
+      // the bias of this lane's row for its keys 4 lq + i of each subtile
+      float bv[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (STAGE_BIAS) bv[kt][i] = bl[bias_pos + 16 * kt + i];
+          else bv[kt][i] = X.bs[4 * kt + i];
+        }
+
+      // logits, mask, online softmax; P packed as the B operand of O^T += V^T P^T
+      float sv[2][4];
+      float mt = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float scl = FP8 ? a.softmax_scale * X.ks[kt][i] : a.softmax_scale;
+          float sc = __builtin_fmaf(sacc[kt][i], scl, bv[kt][i]);
+          if (!fast) {
+            const int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
+            const bool vis = row_live && dist >= 0 && (W == 0 || dist < W);
+            sc = vis ? sc : kNegInf;
+          }
+          sv[kt][i] = sc;
+          mt = fmaxf(mt, sc);
+        }
+      }
+      mt = wave_max_rows(mt);
+      // The reference point m of a row moves only when the tile's maximum exceeds it by
+      // more than kRescaleSlack, so that the accumulators are rescaled on few tiles;
+      // p = exp(s - m) then stays below exp(kRescaleSlack). O and l share m, so the
+      // quotient O / l and lse = m + ln l are unchanged by the choice of m.
+      const bool grow = mt > m_run + kRescaleSlack;      // false while mt = -inf
+      if (__ballot(grow) != 0) {                         // wave-uniform
+        const float m_new = grow ? mt : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float mb = -(m_run == kNegInf ? 0.f : m_run) * kLog2e;
+      float psum = 0.f;
+      float pv[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][i], kLog2e, mb));
+          psum += p;
+          pv[kt][i] = FP8 ? (p > 0.f ? p * X.vs[kt][i] : 0.f) : p;
+        }
+      }
+      l_run += psum;
+      const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                          pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pk);
+
+      // O^T += V^T P^T : V^T operand by transpose reads of the LDS tile. Lane (lr, lq)
+      // supplies the address of 4 dims of key 16 e + 4 lq + lr/4; the read returns to
+      // lane lr the dim 16 dt + lr of keys 16 e + 4 lq + 0..3.
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int cc = 2 * dt + ((lr & 3) >> 1);
+        const int k0 = 4 * lq + (lr >> 2);
+        const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
+        const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(vl + off0));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(vl + off1));
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, o[dt], 0, 0, 0);
+      }
+    };
+
+    // ---- tile loop: two tiles in flight, chunks of at most kChunkPages pages ----
+    const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
+    Tile A, B;
+    for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+      const int c1 = min(c0 + chunk_keys, j_end);
+      stage_pages(c0, c1);
+      const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+      load_tile(A, c0);
+      int i = 0;
+      for (; i + 3 <= nt; i += 2) {
+        const int j0 = c0 + i * kTileKeys;
+        load_tile(B, j0 + kTileKeys);
+        process_tile(A, j0, 0);
+        load_tile(A, j0 + 2 * kTileKeys);
+        process_tile(B, j0 + kTileKeys, 1);
+      }
+      if (i + 2 == nt) {              // the last one or two tiles of the chunk
+        const int j0 = c0 + i * kTileKeys;
+        load_tile(B, j0 + kTileKeys);
+        process_tile(A, j0, 0);
+        process_tile(B, j0 + kTileKeys, 1);
+      } else {
+        process_tile(A, c0 + i * kTileKeys, 0);
+      }
+    }
+
+    // ---- epilogue: the final row when the piece is the whole unit, else a partial ----
+    const float l = wave_sum_rows(l_run);
+    if (row_live) {
+      const int64_t row = (int64_t)(row_base + r_of_row) * a.num_q_heads + row_h;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float lse = l > 0.f ? m_run + __logf(l) : kNegInf;
+      if (whole) {
+        uint16_t* op = a.out + row * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const f32x4_t v = o[dt] * inv;
+          const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2_t*>(op + 16 * dt + 4 * lq) = w;
+        }
+        if (lq == 0 && a.lse != nullptr) a.lse[row] = lse;
+      } else {
+        const int64_t prow = prow0 + rho;
+        float* pp = a.part_o + prow * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * lq) = o[dt] * inv;
+        if (lq == 0) a.part_lse[prow] = lse;
+      }
+    }
+  }
+}
+
+}  // namespace rattn

@@ -192,11 +192,12 @@ rattn_status rattn_free(rattn_plan_t plan);
 /* Read and clear the plan's device flag word (RATTN_FLAG_*). Synchronises `stream`. */
 rattn_status rattn_debug_flags(rattn_plan_t plan, int32_t* flags, void* stream);
 
-/* Instrumentation: record HIP events around the kernels of every `stride`-th
- * rattn_decode call of this plan (the first call after this one, then every stride-th),
- * on the call's stream, for at most `max_calls` calls. The events are timing-only
- * (no system-scope fence); each record still adds a little stream time, which a stride
- * above 1 spreads over the calls in between. */
+/* Instrumentation: time the kernels of every `stride`-th rattn_decode (or
+ * rattn_decode_varlen) call of this plan (the first call after this one, then every
+ * stride-th), for at most `max_calls` calls. Those calls launch their kernels with a
+ * pair of HIP events each, which the runtime stamps with the kernel's own start and end
+ * (hipExtLaunchKernel), so the durations leave out launch gaps; the other calls are
+ * launched as usual. */
 rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls, int32_t stride);
 
 /* Stop recording; waits for the recorded events and writes, per call, the split
