@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn µs/step + achieved HBM GB/s; 48q/8kv GQA, d=128, 100K ctx, b=1"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
 CACHE_EVICT_BYTES = 1 << 30     # rotate over at least this many input bytes
 PLAN_REPS = 20                  # host planning calls timed (rattn_plan + rattn_free)
 KERNEL_SOURCES = ("csrc/device_common.h", "csrc/split_kv.h", "csrc/internal.h",
@@ -69,6 +70,9 @@ WORKLOADS = {
                 "1 row, 100,000 keys, bf16 paged KV (page 16)",
     "tp8_100k": "one GPU's TP8 share of the full-context layer: 6q/1kv, d=128, batch 1, "
                 "1 row, 100,000 keys, bf16 paged KV (page 16)",
+    "prefill_8x2k": "chunked prefill: 8 sequences, a chunk of 2048 query tokens each at "
+                    "100,000 keys (the chunk included), 48q/8kv, d=128, causal, bf16 paged "
+                    "KV (page 16)",
     "verify_b16_varlen": "speculative verify with 1..8 rows per sequence (seeded), 48q/8kv, "
                          "d=128, batch 16, full layer, seq_lens log-uniform [32768,262144], "
                          "bf16 paged KV (page 16)",
@@ -196,6 +200,63 @@ def cpu_baseline(case_cpu, tr, budget_s, rows=None, q_packed=None, cu=None):
                   "pass) in %.1f s; fp64 numpy, BLAS threads=%d, elementwise work "
                   "single-threaded" % (steps, units, sp.batch * sp.num_kv_heads, secs, cores),
         "GBps": tr.total / (us_step * 1e-6) / 1e9,
+    }, out, lse
+
+
+def cpu_baseline_rows(case_cpu, tr, budget_s, block=32):
+    """The oracle on the host cores for a chunk of many rows: blocks of `block` rows of
+    one (sequence, KV head), each attended as the last rows of the sequence cut after
+    them (the same rows of a shorter sequence), in a seeded random order until
+    ``budget_s`` is spent; scaled to the whole step by visible-key work."""
+    import numpy as np
+    import torch
+    import oracle
+    from decode_attention_verify_amd import accounting
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads", 1) for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:
+        cores = 1
+    a = case_cpu
+    sp = a.spec
+    n, G = sp.n_rows, sp.num_q_heads // sp.num_kv_heads
+    kc, vc = a.k_cache.view(torch.uint16).numpy(), a.v_cache.view(torch.uint16).numpy()
+    q = a.q.view(torch.uint16).numpy()
+    lens = [int(x) for x in a.seq_lens]
+    total_work = sum(accounting.rows_keys(L, n, sp.window) for L in lens) * sp.num_kv_heads
+    out = np.full((sp.batch, n, sp.num_q_heads, sp.head_dim), np.nan)
+    lse = np.full((sp.batch, n, sp.num_q_heads), np.nan)
+    rng = np.random.default_rng(0)
+    done, blocks = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = int(rng.integers(0, sp.batch))
+        g = int(rng.integers(0, sp.num_kv_heads))
+        r0 = int(rng.integers(0, n // block)) * block
+        r1 = min(r0 + block, n)
+        L_cut = lens[b] - (n - r1)
+        o, l = oracle.relative_attention(
+            q[b:b + 1, r0:r1], kc, vc, a.page_table[b:b + 1].numpy(), np.array([L_cut]),
+            a.bias.numpy(), n_query_rows=r1 - r0, window=sp.window, dmax=sp.dmax,
+            softmax_scale=a.softmax_scale, kv_heads=[g])
+        hs = slice(g * G, (g + 1) * G)
+        out[b, r0:r1, hs] = o[0, :, hs]
+        lse[b, r0:r1, hs] = l[0, :, hs]
+        done += accounting.rows_keys(L_cut, r1 - r0, sp.window)
+        blocks += 1
+    secs = time.perf_counter() - t0
+    us_step = secs * total_work / done * 1e6
+    return {
+        "value": us_step,
+        "unit": "us/step",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d blocks of %d rows of one (sequence, KV head), %.4f of the step's "
+                  "visible-key work, in %.1f s, scaled to the whole step; fp64 numpy, BLAS "
+                  "threads=%d" % (blocks, block, done / total_work, secs, cores),
+        "TFLOPs": tr.flops / (us_step * 1e-6) / 1e12,
     }, out, lse
 
 
@@ -442,6 +503,7 @@ def main():
     if info["num_splits"] == 1:
         split_bytes += tr.out + tr.lse
     achieved = split_bytes / split_mean_s / 1e9
+    prefill = info["kernel"] == binding.RATTN_KERNEL_PREFILL
     digest = kernel_digest()
     traffic = read_traffic(args.workload, digest)
     result = {
@@ -478,6 +540,7 @@ def main():
         },
         "algorithmic_bytes": tr.total,
         "hbm_GBps": round(tr.total / (us * 1e-6) / 1e9, 1),
+        "TFLOPs": round(tr.flops / (us * 1e-6) / 1e12, 2),
         "hbm_frac_of_peak": round(tr.total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernels_us": {
             "split_kv_mean": round(split_mean_s * 1e6, 3),
@@ -488,7 +551,7 @@ def main():
         },
         "plan_host_us": round(plan_us, 1),
         "hot_cache_us_per_step": hot_us,
-        "roofline": {
+        "roofline": ({
             "bound": "hbm",
             "kernel": "split_kv_kernel",
             "achieved": round(achieved, 1),
@@ -498,16 +561,30 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": split_bytes,
             "kernel_digest": digest,
-        },
+        } if not prefill else {
+            # a chunk of thousands of rows is a dense contraction: priced against the
+            # bf16 matrix peak, 4 D flops per (row, query head, visible key)
+            "bound": "mfma",
+            "kernel": "prefill_kernel",
+            "achieved": round(tr.flops / split_mean_s / 1e12, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tr.flops / split_mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": tr.flops,
+        }),
         "input_copies": ncopies,
     }
 
     if not args.no_cpu_baseline:
         say("cpu baseline: oracle on the host cores (budget %.0fs)" % args.cpu_budget)
         case_cpu = case.to("cpu")
-        cb, ref_out, ref_lse = cpu_baseline(case_cpu, tr, args.cpu_budget, rows,
-                                            None if rows is None else case_cpu.q,
-                                            None if rows is None else cu_rows.cpu())
+        if prefill:
+            cb, ref_out, ref_lse = cpu_baseline_rows(case_cpu, tr, args.cpu_budget)
+        else:
+            cb, ref_out, ref_lse = cpu_baseline(case_cpu, tr, args.cpu_budget, rows,
+                                                None if rows is None else case_cpu.q,
+                                                None if rows is None else cu_rows.cpu())
         result["cpu_baseline"] = cb
         # the last step's output against the oracle on the units it computed
         result["parity_vs_oracle"] = parity_of(out, lse, ref_out, ref_lse)

@@ -11,11 +11,12 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librattn.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 RATTN_OK, RATTN_E_INVALID, RATTN_E_UNSUPPORTED, RATTN_E_HIP, RATTN_E_NOMEM = range(5)
 RATTN_KV_BF16, RATTN_KV_FP8_E4M3 = 0, 1
 RATTN_FLAG_SEQ_LEN_CLAMPED, RATTN_FLAG_PAGE_CLAMPED, RATTN_FLAG_ROWS_INVALID = 1, 2, 4
+RATTN_KERNEL_SPLIT_KV, RATTN_KERNEL_PREFILL = 0, 1
 
 
 class Problem(ctypes.Structure):
@@ -29,7 +30,7 @@ class Problem(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_splits", "keys_per_split", "tile_keys", "row_tiles", "grid_x", "grid_y",
-        "grid_z", "combine_blocks", "num_cus", "blocks_per_cu")] + [
+        "grid_z", "combine_blocks", "num_cus", "blocks_per_cu", "kernel", "reserved")] + [
         ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):

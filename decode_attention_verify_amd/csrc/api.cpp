@@ -49,6 +49,8 @@ void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* i
                         : 0;
   info->num_cus = pl.num_cus;
   info->blocks_per_cu = pl.blocks_per_cu;
+  info->kernel = pl.prefill ? RATTN_KERNEL_PREFILL : RATTN_KERNEL_SPLIT_KV;
+  info->reserved = 0;
   info->workspace_bytes = pl.workspace_bytes;
 }
 
@@ -100,10 +102,12 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   rattn_plan_s* p = new (std::nothrow) rattn_plan_s();
   if (p == nullptr) return RATTN_E_NOMEM;
   p->prob = *prob;
-  int bpc = rattn::split_kv_blocks_per_cu(
-      rattn::waves_for(prob->num_q_heads / prob->num_kv_heads, prob->n_query_rows),
-                                          prob->kv_dtype == RATTN_KV_FP8_E4M3,
-                                          rattn::uses_even_shares(*prob));
+  const int G = prob->num_q_heads / prob->num_kv_heads;
+  int bpc = (int64_t)G * prob->n_query_rows > rattn::kMaxRows
+                ? 1
+                : rattn::split_kv_blocks_per_cu(rattn::waves_for(G, prob->n_query_rows),
+                                                prob->kv_dtype == RATTN_KV_FP8_E4M3,
+                                                rattn::uses_even_shares(*prob));
   if (bpc < 1) bpc = rattn::kDefaultBlocksPerCU;
   p->plan = rattn::make_plan(*prob, cus, bpc);
   p->device = dev;
@@ -191,6 +195,11 @@ rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
   hipEvent_t* ev = nullptr;
   if (plan->prof_count < plan->prof_max && plan->prof_calls++ % plan->prof_stride == 0)
     ev = &plan->prof_events[4 * plan->prof_count++];
+  if (plan->plan.prefill)
+    return rattn::launch_prefill(a, plan->plan.prefill_hw, a.group, stream, ev ? ev[0] : nullptr,
+                                 ev ? ev[1] : nullptr) == 0
+               ? RATTN_OK
+               : RATTN_E_HIP;
   if (rattn::launch_split_kv(a, plan->plan.waves, fp8, stream, ev ? ev[0] : nullptr,
                              ev ? ev[1] : nullptr) != 0)
     return RATTN_E_HIP;
@@ -219,6 +228,7 @@ rattn_status rattn_decode_varlen(rattn_plan_t plan, const void* q, const void* k
                                  int32_t num_rows, const float* bias, void* out, float* lse,
                                  void* stream) {
   if (plan == nullptr || cu_rows == nullptr || num_rows < 0) return RATTN_E_INVALID;
+  if (plan->plan.prefill) return RATTN_E_UNSUPPORTED;   // rows per sequence: decode/verify
   return decode_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
                      cu_rows, num_rows, bias, out, lse, stream);
 }

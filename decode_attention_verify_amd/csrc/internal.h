@@ -33,6 +33,17 @@ inline int waves_for(int G, int n) {
   return slice <= 64 * w * kBiasPerThread ? w : 0;
 }
 
+// Chunked prefill (G n > kMaxRows): heads per wave of the prefill kernel for G query
+// heads per KV head, 0 if not built. A wave holds all 4 heads of a 4-head group, or
+// half of a 6- or 8-head group: its O accumulators (32 registers per head) and queries
+// must fit one wave's registers without spilling.
+inline int prefill_heads_per_wave(int G) {
+  return G == 4 ? 4 : (G == 6 ? 3 : (G == 8 ? 4 : 0));
+}
+// Query tokens per prefill work-group: 4 waves of 16 tokens, halved when two waves
+// share a token block's heads.
+inline int prefill_tokens(int G) { return G == prefill_heads_per_wave(G) ? 64 : 32; }
+
 // Planner output: how one rattn_decode call is launched.
 struct Plan {
   int32_t split_groups;     // split-kernel work-groups (the grid)
@@ -46,6 +57,8 @@ struct Plan {
   int64_t part_o_floats;    // [pieces][rows per unit][D]
   int64_t part_lse_floats;  // [pieces][rows per unit]
   int64_t unit_info_ints;   // even shares: [units][2] (first work-group, pieces)
+  int32_t prefill;          // 1: the prefill kernel (many rows per sequence), no combine
+  int32_t prefill_hw;       // heads per wave of the prefill kernel
 };
 
 // Host-side validation of a problem; no HIP call.
@@ -116,6 +129,8 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start = nullptr,
 // Work-groups of the combine launch for `rows` output rows (host function).
 int64_t combine_blocks(int64_t rows, int splits_per_unit);
 int launch_append_kv(const AppendArgs& a, void* stream);
+int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
+                   void* ev_start = nullptr, void* ev_stop = nullptr);
 // Resident split-kernel work-groups per CU for this variant (0 if the query fails).
 int split_kv_blocks_per_cu(int waves, bool fp8, bool even);
 

@@ -6,6 +6,8 @@
 //    shared;
 //  * append.h: the KV-cache write of each sequence's newest tokens, with E4M3
 //    quantisation for an FP8 cache;
+//  * prefill.h: the same attention for chunks of many query rows per sequence (chunked
+//    prefill), on the MFMA units;
 //  * device_common.h: device helpers and the work partition.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -13,6 +15,7 @@
 #include "internal.h"
 #include "append.h"
 #include "combine.h"
+#include "prefill.h"
 #include "split_kv.h"
 
 namespace rattn {
@@ -106,6 +109,18 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_s
     default:
       return launch(combine_kernel<8, 8, 1, 16>, grid, dim3(64), stream, a, ev_start, ev_stop);
   }
+}
+
+int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
+                   void* ev_start, void* ev_stop) {
+  const dim3 grid((unsigned)a.split_groups);
+  if (heads_per_wave == 3 && group == 6)
+    return launch(prefill_kernel<3, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
+  if (heads_per_wave == 4 && group == 4)
+    return launch(prefill_kernel<4, 1>, grid, dim3(256), stream, a, ev_start, ev_stop);
+  if (heads_per_wave == 4 && group == 8)
+    return launch(prefill_kernel<4, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_append_kv(const AppendArgs& a, void* stream) {

@@ -42,11 +42,21 @@ rattn_status validate_problem(const rattn_problem* p) {
   if (p->num_splits < 0) return RATTN_E_INVALID;
   // valid, but outside what the kernels implement
   if (p->head_dim != kHeadDim) return RATTN_E_UNSUPPORTED;
-  const int64_t rows = (int64_t)(p->num_q_heads / p->num_kv_heads) * p->n_query_rows;
-  if (rows > kMaxRows) return RATTN_E_UNSUPPORTED;
-  // a tile's bias slice (G heads x (32 + n - 1) distances) must fit the work-group's loads
-  if (waves_for(p->num_q_heads / p->num_kv_heads, p->n_query_rows) == 0)
+  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  const int64_t rows = (int64_t)G * p->n_query_rows;
+  if (rows > kMaxRows) {
+    // many rows per sequence: the prefill kernel, for the group sizes it is built for,
+    // over a bf16 cache, without forced splits
+    if (prefill_heads_per_wave(G) == 0) return RATTN_E_UNSUPPORTED;
+    if (p->kv_dtype != RATTN_KV_BF16 || p->num_splits != 0) return RATTN_E_UNSUPPORTED;
+    const int64_t blocks = (p->n_query_rows + prefill_tokens(G) - 1) / prefill_tokens(G);
+    if ((int64_t)p->batch * p->num_kv_heads * blocks > ((int64_t)1 << 31) - 8)
+      return RATTN_E_UNSUPPORTED;
+  } else if (waves_for(G, p->n_query_rows) == 0) {
+    // a tile's bias slice (G heads x (32 + n - 1) distances) must fit the work-group's
+    // loads
     return RATTN_E_UNSUPPORTED;
+  }
   if (!is_pow2(p->page_size) || p->page_size < 16) return RATTN_E_UNSUPPORTED;
   if (p->max_seq_len > (1 << 30)) return RATTN_E_UNSUPPORTED;
   if (p->num_splits > kMaxSplits) return RATTN_E_UNSUPPORTED;
@@ -54,6 +64,7 @@ rattn_status validate_problem(const rattn_problem* p) {
   if ((int64_t)p->num_q_heads * ((int64_t)p->dmax + 1) > INT32_MAX) return RATTN_E_UNSUPPORTED;
   // the work partition multiplies tile counts by the grid size in 64-bit arithmetic
   const int64_t total = (int64_t)p->batch * p->num_kv_heads * unit_tiles_bound(*p);
+  // (the prefill kernel's row and query offsets are 64-bit as well)
   if (total > ((int64_t)1 << 62) / kMaxGroups) return RATTN_E_UNSUPPORTED;
   return RATTN_OK;
 }
@@ -63,9 +74,31 @@ bool uses_even_shares(const rattn_problem& p) {
   return p.num_splits == 0 && p.window == 0 && p.batch > 1;
 }
 
+// Chunked prefill: one work-group per (sequence, KV head, block of query tokens), each
+// over all the keys its rows see; the grid is rounded up to a multiple of the 8 XCDs
+// (the kernel numbers its work-groups per XCD). No partials, no combine.
+static Plan make_prefill_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
+  const int32_t G = p.num_q_heads / p.num_kv_heads;
+  Plan pl{};
+  pl.prefill = 1;
+  pl.prefill_hw = prefill_heads_per_wave(G);
+  pl.waves = 4;
+  pl.num_cus = num_cus;
+  pl.blocks_per_cu = blocks_per_cu;
+  const int64_t blocks = (p.n_query_rows + prefill_tokens(G) - 1) / prefill_tokens(G);
+  const int64_t groups = (int64_t)p.batch * p.num_kv_heads * blocks;
+  pl.split_groups = (int32_t)((groups + 7) / 8 * 8);
+  pl.splits_per_unit = 1;
+  pl.num_splits = 1;
+  pl.keys_per_split = p.max_seq_len;
+  pl.workspace_bytes = 256;                  // the flag word only
+  return pl;
+}
+
 Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int32_t G = p.num_q_heads / p.num_kv_heads;
   const int32_t rows = G * p.n_query_rows;
+  if (rows > kMaxRows) return make_prefill_plan(p, num_cus, blocks_per_cu);
   Plan pl{};
   pl.waves = waves_for(G, p.n_query_rows);
   pl.num_cus = num_cus;

@@ -1,0 +1,334 @@
+// Chunked prefill: attention of a chunk of many query rows per sequence (its last n
+// positions, causal among themselves) over the paged cache, with the relative-position
+// bias. Page 3 ("vLLM supports Reflection Beam", section on coding agents speeding up
+// the implementation) times a prefill of 8 chunks of 2048 tokens at about 100K
+// context; the arithmetic is the decode/verify arithmetic with n in the thousands
+// (page 2, "vLLM TML Inkling support", model architecture section: a learned relative
+// term added to the logits before the softmax).
+//
+// With thousands of rows per (sequence, KV head) the work is a dense contraction, so
+// this kernel is built around the MFMA units rather than around streaming:
+//  * one work-group of 4 waves per (sequence, KV head, block of M query tokens); a wave
+//    takes 16 consecutive tokens for HW query heads of the group, one 16-row MFMA tile
+//    per head (M = 64 tokens when one wave holds all G heads, 32 when two waves share
+//    them: 6 or 8 heads' O accumulators and queries do not fit one wave's registers);
+//  * 32-key K/V tiles are loaded by all 256 threads (16-byte non-temporal loads, a wave
+//    reading 1 KiB of contiguous key rows), double-buffered in LDS with one barrier per
+//    tile; every K or V fragment read from LDS feeds the MFMAs of all HW heads;
+//  * the bias is sheared: for a tile at key j0, head h needs distances p0 - j0 - 31 ..
+//    p0 + M - 1 - j0 (p0 the position of the block's first token), one contiguous slice
+//    of M + 31 entries which the work-group stages in LDS next to the tile; row t reads
+//    key j at slice position (t - t0) - (j - j0) + 31;
+//  * logits, masks (causal and window, only on tiles that cross the diagonal or the
+//    window edge), lazy online softmax and P V follow the decode kernel's layouts: S^T
+//    = K Q^T leaves lane (lr, lq) row lr with keys 4 lq + i, which is the B operand of
+//    O^T += V^T P^T, and V^T is read back with ds_read_b64_tr_b16;
+//  * work-groups are numbered so that the token blocks of one (sequence, KV head) run
+//    back to back on one XCD (work-group w runs on XCD w mod 8): they stream the same
+//    K/V at about the same time and share that XCD's L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "device_common.h"
+
+namespace rattn {
+
+template <int HW, int HG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(KernelArgs a) {
+  constexpr int TB = 4 / HG;                 // 16-token blocks per work-group
+  constexpr int M = 16 * TB;                 // query tokens per work-group
+  constexpr int G = HW * HG;                 // query heads per KV head
+  constexpr int SL = M + kTileKeys - 1;      // bias slice per head and tile
+  constexpr int BIAS_ELEMS = G * SL;
+  constexpr int BIAS_PER_THREAD = (BIAS_ELEMS + 255) / 256;
+  static_assert(TB * HG == 4, "four waves per work-group");
+  __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
+  __shared__ float bias_lds[2][BIAS_ELEMS];
+  __shared__ int pages_lds[kChunkPages + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = wave % TB;                  // this wave's 16-token block
+  const int hg = wave / TB;                  // this wave's share of the group's heads
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int n = a.n;
+  const int64_t Hkv = a.num_kv_heads;
+  const int S = a.page_size;
+  const int W = a.window;
+
+  // ---- which (sequence, KV head, token block): consecutive logical ids on one XCD ----
+  const int NB = (n + M - 1) / M;
+  const int64_t total = (int64_t)a.batch * Hkv * NB;
+  const int64_t per_xcd = (int64_t)gridDim.x / 8;          // the grid is a multiple of 8
+  const int64_t li = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (li >= total) return;                                 // uniform over the group
+  const int64_t u = li / NB;
+  const int blk = (int)(li - u * NB);
+  const int b = (int)(u / Hkv);
+  const int g = (int)(u - (int64_t)b * Hkv);
+
+  const SeqGeom sg = seq_geom(a, b, n, true);              // length clamped into [n, max]
+  const int L = sg.L;
+  const int t0 = blk * M;                                  // tokens [t0, t1) of the chunk
+  const int t1 = min(t0 + M, n);
+  const int p0 = L - n + t0;                               // position of token t0
+  const int p_last = L - n + t1 - 1;
+  const int k_lo = W > 0 ? max(0, p0 - W + 1) : 0;         // first key any row sees
+  const int j_begin = k_lo & ~(kTileKeys - 1);
+  const int j_end = p_last + 1;
+  const int sub_lo = k_lo & ~15;
+  const int sub_hi = p_last & ~15;
+
+  // ---- this lane's row: token t_row, its position, its HW heads' queries ----
+  const int t_row = t0 + 16 * tb + lr;
+  const bool row_ok = t_row < t1;
+  const int row_p = p0 + 16 * tb + lr;
+  const int wave_last_p = p0 + min(16 * tb + 15, t1 - t0 - 1);   // last row of the wave
+  const bool wave_live = 16 * tb < t1 - t0;
+  bf16x8_t qreg[HW][4];
+#pragma unroll
+  for (int i = 0; i < HW; ++i) {
+    const int h = g * G + hg * HW + i;
+    const int64_t qr = (int64_t)b * n + (row_ok ? t_row : t0);
+    const uint16_t* qrow = a.q + (qr * a.num_q_heads + h) * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4_t v = row_ok ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
+      qreg[i][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // ---- page ids of a chunk of keys, staged in LDS ----
+  const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
+  int chunk_p0 = 0;
+  auto stage_pages = [&](int c0, int c1) {
+    __syncthreads();                         // the previous chunk's ids and tiles are done
+    chunk_p0 = c0 >> a.page_shift;
+    const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
+    for (int i = tid; i < np; i += 256) {
+      int ph = pt_row[chunk_p0 + i];
+      if (ph < 0 || ph >= a.num_pages) {
+        atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
+        ph = min(max(ph, 0), a.num_pages - 1);
+      }
+      pages_lds[i] = ph;
+    }
+    __syncthreads();
+  };
+  auto phys_at = [&](int jt) -> int {
+    const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
+    return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
+  };
+
+  // ---- a tile's loads: slot m = (K|V, 16-key subtile); thread tid reads 16 bytes of key
+  // tid / 16 of the subtile (a wave reads 4 whole key rows, 1 KiB contiguous) ----
+  struct Tile {
+    u32x4_t x[4];
+    float bs[BIAS_PER_THREAD];
+  };
+  const unsigned char* kc = (const unsigned char*)a.k_cache;
+  const unsigned char* vc = (const unsigned char*)a.v_cache;
+  const int ld_key = tid >> 4;               // key within a subtile
+  const int ld_ch = tid & 15;                // 16-byte chunk of the key row
+  auto load_tile = [&](Tile& X, int j0) {
+    int64_t tok0[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // a subtile with no key in [k_lo, p_last] reads the nearest one that has
+      const int js = min(max(j0 + 16 * kt, sub_lo), sub_hi);
+      tok0[kt] = ((int64_t)phys_at(js) * Hkv + g) * S + (js & (S - 1));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int kt = m & 1;
+      const unsigned char* base = (m >> 1 ? vc : kc) + (tok0[kt] + ld_key) * 256;
+      X.x[m] = ld16_stream(base + 16 * ld_ch);
+    }
+#pragma unroll
+    for (int q = 0; q < BIAS_PER_THREAD; ++q) {
+      // slice element e: head e / SL of the group, distance p0 - j0 - 31 + e % SL,
+      // clamped to [0, Dmax] (a masked key reads an in-range entry)
+      const int e = tid + 256 * q;
+      const int hi = e / SL;
+      const int d = min(max(p0 - j0 - (kTileKeys - 1) + (e - hi * SL), 0), a.dmax);
+      const unsigned idx = e < BIAS_ELEMS ? (unsigned)((g * G + hi) * (a.dmax + 1) + d) : 0u;
+      X.bs[q] = ldf_stream(a.bias + idx);
+    }
+  };
+
+  // ---- running state: per head, the lane's row ----
+  f32x4_t o[HW][8];
+  float m_run[HW], l_run[HW];
+#pragma unroll
+  for (int i = 0; i < HW; ++i) {
+    m_run[i] = kNegInf;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4_t{0, 0, 0, 0};
+  }
+  // this lane's bias slice position for key 4 lq of subtile 0, at head 0 of the wave
+  const int bias_pos0 = (hg * HW) * SL + 16 * tb + lr - 4 * lq + (kTileKeys - 1);
+
+  auto process_tile = [&](const Tile& X, int j0, int buf) {
+    unsigned char* kl = klds[buf];
+    unsigned char* vl = vlds[buf];
+    float* bl = bias_lds[buf];
+    // every key of the tile visible to every row of the work-group: no mask
+    const bool fast = j0 + kTileKeys - 1 <= p0 && (W == 0 || p_last - j0 <= W - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int kk = 16 * (m & 1) + ld_key;
+      u32x4_t v = X.x[m];
+      if (m >> 1) {
+        // V of a key outside [k_lo, L) becomes zero, so that P = 0 times a stale or
+        // NaN value cannot reach the accumulator
+        const int j = j0 + kk;
+        if (!fast && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, ld_ch)) = v;
+      } else {
+        *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, ld_ch)) = v;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < BIAS_PER_THREAD; ++q) {
+      const int e = tid + 256 * q;
+      if (e < BIAS_ELEMS) bl[e] = X.bs[q];
+    }
+    __syncthreads();                         // the tile and its bias slices are in LDS
+    if (!wave_live || j0 > wave_last_p) return;   // every key after every row: no work
+
+    // S^T = K Q^T for the HW heads; each K fragment feeds all of them
+    f32x4_t sacc[HW][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < HW; ++i) sacc[i][kt] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
+#pragma unroll
+        for (int i = 0; i < HW; ++i)
+          sacc[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[i][s], sacc[i][kt], 0, 0, 0);
+      }
+    }
+
+    // logits, mask, online softmax per head; P packed as the B operand of the PV MFMA
+    bf16x8_t pop[HW];
+#pragma unroll
+    for (int i = 0; i < HW; ++i) {
+      float sv[2][4];
+      float mt = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float sc = __builtin_fmaf(sacc[i][kt][c], a.softmax_scale,
+                                    bl[bias_pos0 + i * SL - 16 * kt - c]);
+          if (!fast) {
+            const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
+            const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
+            sc = vis ? sc : kNegInf;
+          }
+          sv[kt][c] = sc;
+          mt = fmaxf(mt, sc);
+        }
+      mt = wave_max_rows(mt);
+      // the reference point moves only when the tile's maximum passes it by 8 ln 2
+      const bool grow = mt > m_run[i] + kRescaleSlack;
+      if (__ballot(grow) != 0) {
+        const float m_new = grow ? mt : m_run[i];
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[i] - m_new) * kLog2e) : 1.f;
+        l_run[i] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+        m_run[i] = m_new;
+      }
+      const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]) * kLog2e;
+      float pv[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][c], kLog2e, mb));
+          psum += p;
+          pv[kt][c] = p;
+        }
+      l_run[i] += psum;
+      const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                          pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+      pop[i] = __builtin_bit_cast(bf16x8_t, pk);
+    }
+
+    // O^T += V^T P^T; each V^T fragment feeds all HW heads
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int cc = 2 * dt + ((lr & 3) >> 1);
+      const int k0 = 4 * lq + (lr >> 2);
+      const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
+      const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
+      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (i16x4_t __attribute__((address_space(3)))*)(vl + off0));
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (i16x4_t __attribute__((address_space(3)))*)(vl + off1));
+      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
+#pragma unroll
+      for (int i = 0; i < HW; ++i)
+        o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i], o[i][dt], 0, 0, 0);
+    }
+  };
+
+  // ---- tile loop: two tiles in flight, chunks of at most kChunkPages pages ----
+  const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
+  Tile A, B;
+  for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+    const int c1 = min(c0 + chunk_keys, j_end);
+    stage_pages(c0, c1);
+    const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+    load_tile(A, c0);
+    int i = 0;
+    for (; i + 3 <= nt; i += 2) {
+      const int j0 = c0 + i * kTileKeys;
+      load_tile(B, j0 + kTileKeys);
+      process_tile(A, j0, 0);
+      load_tile(A, j0 + 2 * kTileKeys);
+      process_tile(B, j0 + kTileKeys, 1);
+    }
+    if (i + 2 == nt) {
+      const int j0 = c0 + i * kTileKeys;
+      load_tile(B, j0 + kTileKeys);
+      process_tile(A, j0, 0);
+      process_tile(B, j0 + kTileKeys, 1);
+    } else {
+      process_tile(A, c0 + i * kTileKeys, 0);
+    }
+  }
+
+  // ---- epilogue: every row's output and log-sum-exp, per head ----
+#pragma unroll
+  for (int i = 0; i < HW; ++i) {
+    const float l = wave_sum_rows(l_run[i]);
+    if (!row_ok) continue;
+    const int h = g * G + hg * HW + i;
+    const int64_t row = ((int64_t)b * n + t_row) * a.num_q_heads + h;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = a.out + row * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4_t v = o[i][dt] * inv;
+      const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2_t*>(op + 16 * dt + 4 * lq) = w;
+    }
+    if (lq == 0 && a.lse != nullptr) a.lse[row] = l > 0.f ? m_run[i] + __logf(l) : kNegInf;
+  }
+}
+
+}  // namespace rattn

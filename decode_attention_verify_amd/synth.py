@@ -104,6 +104,10 @@ def _named_specs():
                          bias_decay=1e-5),
         "tp8_100k": Spec("tp8_100k", 1, 1, 6, 1, 128, 0, 131071, 16, KV_BF16, 100000,
                          bias_decay=1e-5),
+        # chunked prefill: 8 chunks of 2048 tokens at about 100K context (page 3, section
+        # on coding agents speeding up the implementation)
+        "prefill_8x2k": Spec("prefill_8x2k", 8, 2048, 48, 8, 128, 0, 131071, 16, KV_BF16,
+                             100000, bias_decay=1e-5),
         # verify where each sequence checks its own number of drafts, 1..8 (page 3,
         # adaptive verification)
         "verify_b16_varlen": Spec("verify_b16_varlen", 16, 8, 48, 8, 128, 0, 262143, 16,

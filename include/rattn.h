@@ -25,7 +25,10 @@
  *   - page 2, technical-optimisation section (FA4 kernel): a "sheared-bias" access
  *     pattern for the relative term, and a split count chosen from batch size and KV
  *     length; roadmap: FP8 global attention. Page 3 ("vLLM supports Reflection Beam"),
- *     support section: an FP8 KV cache.
+ *     support section: an FP8 KV cache; section on coding agents speeding up the
+ *     implementation: a chunked prefill (8 x 2048 tokens at about 100K context) and a
+ *     fused KV-cache update; section on DFlash2 and adaptive verification: a different
+ *     number of verified drafts per sequence.
  * The pages do not fix how the relative term is parameterised; here it is a per-head
  * float32 table indexed by the query-key distance, clamped at dmax.
  *
@@ -66,7 +69,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 1
+#define RATTN_ABI_VERSION 2
 
 typedef struct rattn_plan_s* rattn_plan_t;
 
@@ -93,8 +96,9 @@ typedef struct {
   int32_t num_q_heads;       /* query heads (48 in the Inkling 2 Small layers)            */
   int32_t num_kv_heads;      /* KV heads (8); num_q_heads % num_kv_heads == 0             */
   int32_t head_dim;          /* 128 (the only supported value)                            */
-  int32_t n_query_rows;      /* rows per sequence: 1 for decode, 1 + drafts for verify;   */
-                             /* (num_q_heads/num_kv_heads) * n_query_rows <= 64            */
+  int32_t n_query_rows;      /* rows per sequence: 1 for decode, 1 + drafts for verify,   */
+                             /* the chunk length for a chunked prefill (see              */
+                             /* RATTN_KERNEL_PREFILL)                                    */
   int32_t page_size;         /* slots per page: a power of two >= 16                      */
   int32_t num_pages;         /* physical pages in the cache                               */
   int32_t max_pages_per_seq; /* page_table row length                                     */
@@ -116,8 +120,18 @@ typedef struct {
   int32_t combine_blocks;    /* combine work-groups; 0 when the grid is one work-group    */
   int32_t num_cus;           /* compute units the plan was sized for                      */
   int32_t blocks_per_cu;     /* resident split-kernel work-groups per CU assumed          */
+  int32_t kernel;            /* RATTN_KERNEL_*: which kernel the plan launches            */
+  int32_t reserved;          /* 0                                                         */
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps, and a flag word         */
 } rattn_plan_info;
+
+/* rattn_plan_info.kernel. Up to 64 packed rows per (sequence, KV head) (G * n, G =
+ * num_q_heads / num_kv_heads): the split-KV kernel and, when a unit is split, the
+ * log-sum-exp combine. More rows (chunked prefill): one MFMA kernel per block of query
+ * tokens over all the keys they see, no split; built for G = 4, 6 and 8 over a bf16
+ * cache, without forced splits (else RATTN_E_UNSUPPORTED). */
+#define RATTN_KERNEL_SPLIT_KV 0
+#define RATTN_KERNEL_PREFILL 1
 
 /* Validate `prob`, size the launch for the current HIP device and allocate the
  * workspace. On success *plan_out owns the workspace until rattn_free. */

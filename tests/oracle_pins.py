@@ -562,6 +562,15 @@ def pin_varlen_uniform_rows_are_fixed(orc):
     _close(lse, ref_lse.reshape(12, 6), 1e-13, "uniform varlen lse")
 
 
+def pin_many_rows_brute_force(orc):
+    """A chunk of many query rows (prefill) at its last positions, causal among
+    themselves, with and without a window: brute force."""
+    for n, L, W in ((40, 50, 0), (33, 33, 0), (48, 70, 9)):
+        sp = synth.spec("tiny", batch=1, n_rows=n, num_q_heads=3, num_kv_heads=1,
+                        seq_len=L, dmax=60, head_dim=8, window=W, permute_pages=True)
+        _brute_vs_oracle(orc, synth.make_case(sp, seed=600 + n))
+
+
 ALL_PINS = [
     pin_encode_round_trips_every_code,
     pin_encode_ties_go_to_even_codes,
@@ -589,4 +598,5 @@ ALL_PINS = [
     pin_fp8_cache,
     pin_varlen_brute_force,
     pin_varlen_uniform_rows_are_fixed,
+    pin_many_rows_brute_force,
 ]

@@ -44,7 +44,11 @@ INVALID = [
     dict(num_splits=-1),
 ]
 UNSUPPORTED = [
-    dict(head_dim=64), dict(n_query_rows=11), dict(page_size=24, max_pages_per_seq=6250),
+    dict(head_dim=64), dict(page_size=24, max_pages_per_seq=6250),
+    # more than 64 packed rows go to the prefill kernel, built for G = 4, 6, 8 over a
+    # bf16 cache without forced splits
+    dict(n_query_rows=11, kv_dtype=binding.RATTN_KV_FP8_E4M3),
+    dict(n_query_rows=100, num_q_heads=24), dict(n_query_rows=100, num_splits=4),
     dict(page_size=8, max_pages_per_seq=12500), dict(num_splits=4097),
     # 64 query heads per KV head: a tile's bias slice (64 x 32 distances) exceeds what
     # a work-group stages
@@ -139,3 +143,17 @@ def test_combine_shape_follows_the_pieces():
         headline(batch=16, n_query_rows=8, max_seq_len=262144, max_pages_per_seq=16384,
                  dmax=262143), 256)
     assert verify.combine_blocks == 16 * 8 * 48 // 4
+
+
+@pytest.mark.parametrize("hq,n,tokens", [(48, 11, 32), (48, 2048, 32), (32, 17, 64),
+                                         (64, 9, 32), (64, 1000, 32)])
+def test_planner_prefill(hq, n, tokens):
+    # more than 64 packed rows: one prefill work-group per (sequence, KV head, block of
+    # query tokens), a grid rounded up to a multiple of 8 (one share per XCD), no combine
+    p = headline(batch=3, num_q_heads=hq, n_query_rows=n)
+    info = binding.rattn_plan_describe(p, 256)
+    assert info.kernel == binding.RATTN_KERNEL_PREFILL
+    blocks = 3 * 8 * -(-n // tokens)
+    assert info.grid_x % 8 == 0 and blocks <= info.grid_x < blocks + 8
+    assert info.combine_blocks == 0 and info.row_tiles == 4
+    assert binding.rattn_plan_describe(headline(), 256).kernel == binding.RATTN_KERNEL_SPLIT_KV

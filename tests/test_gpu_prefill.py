@@ -1,0 +1,79 @@
+"""Chunked prefill (many query rows per sequence) on the GPU against the oracle.
+
+Same floating-point bar as the decode parity tests. Small shapes compare every row;
+the page's prefill workload (8 chunks of 2048 tokens at 100K context) compares sampled
+rows, each computed by the oracle as a one-row decode of the first L - (n - 1 - r) keys
+(a row of a chunk attends exactly as the last row of that shorter sequence).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_verify_amd import binding, synth
+from tests.parity import check_case, compare, run_hip, say
+
+pytestmark = pytest.mark.gpu
+
+
+def small(base, **kw):
+    return dataclasses.replace(synth.spec(base), **kw)
+
+
+@pytest.mark.parametrize("n,lens,W", [(11, (11, 40), 0), (65, (65, 700), 0),
+                                      (100, (100, 1500), 0), (257, (300, 2100), 0),
+                                      (96, (96, 900), 1), (130, (200, 3000), 64),
+                                      (128, (128, 2000), 1024)])
+def test_prefill_rows_windows(n, lens, W):
+    sp = small("full_100k", batch=2, n_rows=n, seq_len=("uniform",) + lens, window=W,
+               dmax=3500, name="prefill")
+    _, _, info = check_case(sp, seed=n + W)
+    assert info["kernel"] == binding.RATTN_KERNEL_PREFILL
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 16), (64, 8), (48, 8)])
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+def test_prefill_groups_and_pages(hq, hkv, page_size):
+    sp = small("full_100k", batch=2, n_rows=80, num_q_heads=hq, num_kv_heads=hkv,
+               page_size=page_size, seq_len=("uniform", 80, 1200), dmax=1300,
+               name="prefill_g")
+    check_case(sp, seed=hq + hkv + page_size)
+
+
+def test_prefill_whole_sequence_is_the_chunk():
+    # the first chunk of a prompt: L = n, every row causal over the chunk alone
+    sp = small("full_100k", batch=3, n_rows=200, seq_len=200, dmax=250, bias_decay=0.0,
+               name="prefill_first")
+    check_case(sp, seed=4)
+
+
+def test_prefill_full_size_sampled():
+    sp = synth.spec("prefill_8x2k")
+    say("prefill full size: B=%d n=%d L=%s" % (sp.batch, sp.n_rows, sp.seq_len))
+    case = synth.make_case(sp, seed=0, device="cuda")
+    out, lse, info, flags = run_hip(case)
+    assert flags == 0 and info["kernel"] == binding.RATTN_KERNEL_PREFILL
+    cpu = case.to("cpu")
+    del case
+    view = torch.uint16
+    kc, vc = cpu.k_cache.view(view).numpy(), cpu.v_cache.view(view).numpy()
+    G = sp.num_q_heads // sp.num_kv_heads
+    rng = np.random.default_rng(0)
+    picks = [(b, r, g) for b, r, g in zip(rng.integers(0, sp.batch, 12),
+                                          rng.integers(0, sp.n_rows, 12),
+                                          rng.integers(0, sp.num_kv_heads, 12))]
+    picks += [(0, 0, 0), (7, sp.n_rows - 1, 7), (3, 1023, 2)]
+    for b, r, g in picks:
+        L = int(cpu.seq_lens[b])
+        q1 = cpu.q[b:b + 1, r:r + 1].contiguous().view(view).numpy()
+        o1, l1 = oracle.relative_attention(
+            q1, kc, vc, cpu.page_table[b:b + 1].numpy(),
+            np.array([L - (sp.n_rows - 1 - r)]), cpu.bias.numpy(), n_query_rows=1,
+            window=sp.window, dmax=sp.dmax, softmax_scale=cpu.softmax_scale,
+            kv_heads=[int(g)])
+        hs = slice(g * G, (g + 1) * G)
+        compare(out[b, r, hs].unsqueeze(0), lse[b, r, hs].unsqueeze(0), o1[0, 0, hs][None],
+                l1[0, 0, hs][None], "prefill b=%d r=%d g=%d" % (b, r, g))
