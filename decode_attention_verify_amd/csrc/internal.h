@@ -34,15 +34,18 @@ inline int waves_for(int G, int n) {
 }
 
 // Chunked prefill (G n > kMaxRows): heads per wave of the prefill kernel for G query
-// heads per KV head, 0 if not built. A wave holds all 4 heads of a 4-head group, or
-// half of a 6- or 8-head group: its O accumulators (32 registers per head) and queries
-// must fit one wave's registers without spilling.
+// heads per KV head, 0 if not built. Each head costs a wave 48 registers (its 16 rows'
+// O accumulators and queries): 3 heads fit one wave's registers without spilling, so a
+// 6-head group takes two waves per 16-token block, and 4- and 8-head groups 2 and 4.
 inline int prefill_heads_per_wave(int G) {
-  return G == 4 ? 4 : (G == 6 ? 3 : (G == 8 ? 4 : 0));
+  return G == 6 ? 3 : ((G == 4 || G == 8) ? 2 : 0);
 }
-// Query tokens per prefill work-group: 4 waves of 16 tokens, halved when two waves
-// share a token block's heads.
-inline int prefill_tokens(int G) { return G == prefill_heads_per_wave(G) ? 64 : 32; }
+// Query tokens per prefill work-group: its 4 waves cover 4 / (G / heads per wave)
+// blocks of 16 tokens.
+inline int prefill_tokens(int G) {
+  const int hw = prefill_heads_per_wave(G);
+  return hw ? 16 * (4 / (G / hw)) : 0;
+}
 
 // Planner output: how one rattn_decode call is launched.
 struct Plan {

@@ -116,10 +116,10 @@ int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* str
   const dim3 grid((unsigned)a.split_groups);
   if (heads_per_wave == 3 && group == 6)
     return launch(prefill_kernel<3, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
-  if (heads_per_wave == 4 && group == 4)
-    return launch(prefill_kernel<4, 1>, grid, dim3(256), stream, a, ev_start, ev_stop);
-  if (heads_per_wave == 4 && group == 8)
-    return launch(prefill_kernel<4, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
+  if (heads_per_wave == 2 && group == 4)
+    return launch(prefill_kernel<2, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
+  if (heads_per_wave == 2 && group == 8)
+    return launch(prefill_kernel<2, 4>, grid, dim3(256), stream, a, ev_start, ev_stop);
   return (int)hipErrorInvalidValue;
 }
 

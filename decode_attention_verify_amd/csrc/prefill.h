@@ -10,17 +10,20 @@
 // this kernel is built around the MFMA units rather than around streaming:
 //  * one work-group of 4 waves per (sequence, KV head, block of M query tokens); a wave
 //    takes 16 consecutive tokens for HW query heads of the group, one 16-row MFMA tile
-//    per head (M = 64 tokens when one wave holds all G heads, 32 when two waves share
-//    them: 6 or 8 heads' O accumulators and queries do not fit one wave's registers);
-//  * 32-key K/V tiles are loaded by all 256 threads (16-byte non-temporal loads, a wave
-//    reading 1 KiB of contiguous key rows), double-buffered in LDS with one barrier per
-//    tile; every K or V fragment read from LDS feeds the MFMAs of all HW heads;
+//    per head (3 heads for a 6-head group, 2 for 4- and 8-head groups: a head's O
+//    accumulators and queries take 48 of a wave's registers), so M = 16 * 4 / (G / HW);
+//  * 32-key K/V tiles are loaded by all 256 threads (16-byte loads through the caches,
+//    which the unit's other blocks hit; a wave reads 1 KiB of contiguous key rows); the
+//    next tile's loads are in flight while a tile is attended; tiles are double-buffered
+//    in LDS with one barrier per tile; every K or V fragment read from LDS feeds the
+//    MFMAs of all HW heads;
 //  * the bias is sheared: for a tile at key j0, head h needs distances p0 - j0 - 31 ..
 //    p0 + M - 1 - j0 (p0 the position of the block's first token), one contiguous slice
 //    of M + 31 entries which the work-group stages in LDS next to the tile; row t reads
 //    key j at slice position (t - t0) - (j - j0) + 31;
-//  * logits, masks (causal and window, only on tiles that cross the diagonal or the
-//    window edge), lazy online softmax and P V follow the decode kernel's layouts: S^T
+//  * logits, masks (causal and window, compiled only into the instance for tiles that
+//    cross the diagonal or the window edge), lazy online softmax and P V follow the
+//    decode kernel's layouts: S^T
 //    = K Q^T leaves lane (lr, lq) row lr with keys 4 lq + i, which is the B operand of
 //    O^T += V^T P^T, and V^T is read back with ds_read_b64_tr_b16;
 //  * work-groups are numbered so that the token blocks of one (sequence, KV head) run
@@ -29,6 +32,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.h"
 #include "device_common.h"
@@ -44,7 +49,7 @@ void prefill_kernel(KernelArgs a) {
   constexpr int SL = M + kTileKeys - 1;      // bias slice per head and tile
   constexpr int BIAS_ELEMS = G * SL;
   constexpr int BIAS_PER_THREAD = (BIAS_ELEMS + 255) / 256;
-  static_assert(TB * HG == 4, "four waves per work-group");
+  static_assert(TB * HG == 4 && TB >= 1, "four waves per work-group");
   __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
   __shared__ float bias_lds[2][BIAS_ELEMS];
@@ -148,7 +153,7 @@ void prefill_kernel(KernelArgs a) {
     for (int m = 0; m < 4; ++m) {
       const int kt = m & 1;
       const unsigned char* base = (m >> 1 ? vc : kc) + (tok0[kt] + ld_key) * 256;
-      X.x[m] = ld16_stream(base + 16 * ld_ch);
+      X.x[m] = ld16(base + 16 * ld_ch);   // cached: the unit's other blocks read it too
     }
 #pragma unroll
     for (int q = 0; q < BIAS_PER_THREAD; ++q) {
@@ -158,7 +163,7 @@ void prefill_kernel(KernelArgs a) {
       const int hi = e / SL;
       const int d = min(max(p0 - j0 - (kTileKeys - 1) + (e - hi * SL), 0), a.dmax);
       const unsigned idx = e < BIAS_ELEMS ? (unsigned)((g * G + hi) * (a.dmax + 1) + d) : 0u;
-      X.bs[q] = ldf_stream(a.bias + idx);
+      X.bs[q] = a.bias[idx];
     }
   };
 
@@ -175,21 +180,20 @@ void prefill_kernel(KernelArgs a) {
   // this lane's bias slice position for key 4 lq of subtile 0, at head 0 of the wave
   const int bias_pos0 = (hg * HW) * SL + 16 * tb + lr - 4 * lq + (kTileKeys - 1);
 
-  auto process_tile = [&](const Tile& X, int j0, int buf) {
+  // the tile in registers -> LDS buffer `buf` (V of keys outside [k_lo, L) as zero, so
+  // that P = 0 times a stale or NaN value cannot reach the accumulator)
+  auto store_tile = [&](const Tile& X, int j0, int buf) {
     unsigned char* kl = klds[buf];
     unsigned char* vl = vlds[buf];
     float* bl = bias_lds[buf];
-    // every key of the tile visible to every row of the work-group: no mask
-    const bool fast = j0 + kTileKeys - 1 <= p0 && (W == 0 || p_last - j0 <= W - 1);
+    const bool edge = j0 < k_lo || j0 + kTileKeys > L;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int kk = 16 * (m & 1) + ld_key;
       u32x4_t v = X.x[m];
       if (m >> 1) {
-        // V of a key outside [k_lo, L) becomes zero, so that P = 0 times a stale or
-        // NaN value cannot reach the accumulator
         const int j = j0 + kk;
-        if (!fast && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
+        if (edge && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
         *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, ld_ch)) = v;
       } else {
         *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, ld_ch)) = v;
@@ -200,8 +204,18 @@ void prefill_kernel(KernelArgs a) {
       const int e = tid + 256 * q;
       if (e < BIAS_ELEMS) bl[e] = X.bs[q];
     }
-    __syncthreads();                         // the tile and its bias slices are in LDS
-    if (!wave_live || j0 > wave_last_p) return;   // every key after every row: no work
+  };
+  // every key of the tile at j0 visible to every row of the work-group: no mask
+  auto tile_is_fast = [&](int j0) {
+    return j0 + kTileKeys - 1 <= p0 && (W == 0 || p_last - j0 <= W - 1);
+  };
+  // attention of this wave's rows over the tile in LDS buffer `buf`
+  auto compute_tile = [&](int j0, int buf, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const unsigned char* kl = klds[buf];
+    const unsigned char* vl = vlds[buf];
+    const float* bl = bias_lds[buf];
+    if (!FAST && (!wave_live || j0 > wave_last_p)) return;   // every key after every row
 
     // S^T = K Q^T for the HW heads; each K fragment feeds all of them
     f32x4_t sacc[HW][2];
@@ -231,7 +245,7 @@ void prefill_kernel(KernelArgs a) {
         for (int c = 0; c < 4; ++c) {
           float sc = __builtin_fmaf(sacc[i][kt][c], a.softmax_scale,
                                     bl[bias_pos0 + i * SL - 16 * kt - c]);
-          if (!fast) {
+          if (!FAST) {
             const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
             const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
             sc = vis ? sc : kNegInf;
@@ -275,9 +289,9 @@ void prefill_kernel(KernelArgs a) {
       const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
       const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
       const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(vl + off0));
+          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off0));
       const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(vl + off1));
+          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off1));
       const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
       const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
 #pragma unroll
@@ -286,29 +300,22 @@ void prefill_kernel(KernelArgs a) {
     }
   };
 
-  // ---- tile loop: two tiles in flight, chunks of at most kChunkPages pages ----
+  // ---- tile loop: the next tile's loads in flight while a tile is attended ----
   const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-  Tile A, B;
+  Tile R;
   for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
     const int c1 = min(c0 + chunk_keys, j_end);
     stage_pages(c0, c1);
     const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
-    load_tile(A, c0);
-    int i = 0;
-    for (; i + 3 <= nt; i += 2) {
+    load_tile(R, c0);
+    for (int i = 0; i < nt; ++i) {
       const int j0 = c0 + i * kTileKeys;
-      load_tile(B, j0 + kTileKeys);
-      process_tile(A, j0, 0);
-      load_tile(A, j0 + 2 * kTileKeys);
-      process_tile(B, j0 + kTileKeys, 1);
-    }
-    if (i + 2 == nt) {
-      const int j0 = c0 + i * kTileKeys;
-      load_tile(B, j0 + kTileKeys);
-      process_tile(A, j0, 0);
-      process_tile(B, j0 + kTileKeys, 1);
-    } else {
-      process_tile(A, c0 + i * kTileKeys, 0);
+      const int buf = i & 1;
+      store_tile(R, j0, buf);
+      if (i + 1 < nt) load_tile(R, j0 + kTileKeys);
+      __syncthreads();                       // tile i and its bias slices are in LDS
+      if (tile_is_fast(j0)) compute_tile(j0, buf, std::true_type{});
+      else compute_tile(j0, buf, std::false_type{});
     }
   }
 
