@@ -233,37 +233,46 @@ void prefill_kernel(KernelArgs a) {
       }
     }
 
-    // logits, mask, online softmax per head; P packed as the B operand of the PV MFMA
-    bf16x8_t pop[HW];
+    // logits (with masks on the tiles that need them) of head i, key (kt, c)
+    auto logit = [&](int i, int kt, int c) {
+      float sc = __builtin_fmaf(sacc[i][kt][c], a.softmax_scale,
+                                bl[bias_pos0 + i * SL - 16 * kt - c]);
+      if (!FAST) {
+        const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
+        const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
+        sc = vis ? sc : kNegInf;
+      }
+      return sc;
+    };
+    // each head's tile maximum; one test for all heads, the rare rescale in one branch
+    float mt[HW];
+    bool grow_any = false;
 #pragma unroll
     for (int i = 0; i < HW; ++i) {
-      float sv[2][4];
-      float mt = kNegInf;
+      float x = kNegInf;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float sc = __builtin_fmaf(sacc[i][kt][c], a.softmax_scale,
-                                    bl[bias_pos0 + i * SL - 16 * kt - c]);
-          if (!FAST) {
-            const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
-            const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
-            sc = vis ? sc : kNegInf;
-          }
-          sv[kt][c] = sc;
-          mt = fmaxf(mt, sc);
-        }
-      mt = wave_max_rows(mt);
-      // the reference point moves only when the tile's maximum passes it by 8 ln 2
-      const bool grow = mt > m_run[i] + kRescaleSlack;
-      if (__ballot(grow) != 0) {
-        const float m_new = grow ? mt : m_run[i];
+        for (int c = 0; c < 4; ++c) x = fmaxf(x, logit(i, kt, c));
+      mt[i] = wave_max_rows(x);
+      grow_any |= mt[i] > m_run[i] + kRescaleSlack;
+    }
+    if (__ballot(grow_any) != 0) {
+#pragma unroll
+      for (int i = 0; i < HW; ++i) {
+        const bool grow = mt[i] > m_run[i] + kRescaleSlack;
+        const float m_new = grow ? mt[i] : m_run[i];
         const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[i] - m_new) * kLog2e) : 1.f;
         l_run[i] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
         m_run[i] = m_new;
       }
+    }
+    // P = exp(s - m) from the logits again, packed as the B operand of the PV MFMA
+    bf16x8_t pop[HW];
+#pragma unroll
+    for (int i = 0; i < HW; ++i) {
       const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]) * kLog2e;
       float pv[2][4];
       float psum = 0.f;
@@ -271,7 +280,7 @@ void prefill_kernel(KernelArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][c], kLog2e, mb));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(logit(i, kt, c), kLog2e, mb));
           psum += p;
           pv[kt][c] = p;
         }
