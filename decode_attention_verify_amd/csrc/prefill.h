@@ -11,7 +11,9 @@
 //  * one work-group of 4 waves per (sequence, KV head, block of M query tokens); a wave
 //    takes 16 consecutive tokens for HW query heads of the group, one 16-row MFMA tile
 //    per head (3 heads for a 6-head group, 2 for 4- and 8-head groups: a head's O
-//    accumulators and queries take 48 of a wave's registers), so M = 16 * 4 / (G / HW);
+//    accumulators take 32 of a wave's registers), so M = 16 * 4 / (G / HW);
+//  * each wave's queries sit in LDS in MFMA operand order (one 16-byte read per lane and
+//    head per k-step), which leaves the registers to the O accumulators;
 //  * 32-key K/V tiles are loaded by all 256 threads (16-byte loads through the caches,
 //    which the unit's other blocks hit; a wave reads 1 KiB of contiguous key rows); the
 //    next tile's loads are in flight while a tile is attended; tiles are double-buffered
@@ -22,10 +24,12 @@
 //    of M + 31 entries which the work-group stages in LDS next to the tile; row t reads
 //    key j at slice position (t - t0) - (j - j0) + 31;
 //  * logits, masks (causal and window, compiled only into the instance for tiles that
-//    cross the diagonal or the window edge), lazy online softmax and P V follow the
-//    decode kernel's layouts: S^T
-//    = K Q^T leaves lane (lr, lq) row lr with keys 4 lq + i, which is the B operand of
-//    O^T += V^T P^T, and V^T is read back with ds_read_b64_tr_b16;
+//    cross the diagonal or the window edge), lazy online softmax (one rescale test per
+//    tile for all heads) and P V follow the decode kernel's layouts; the V^T fragments are
+//    read once per tile and each head's P V MFMAs follow its exponentials, so that the
+//    next head's VALU work overlaps them. S^T = K Q^T leaves lane (lr, lq) row lr with
+//    keys 4 lq + i, which is the B operand of O^T += V^T P^T, and V^T is read back with
+//    ds_read_b64_tr_b16;
 //  * work-groups are numbered so that the token blocks of one (sequence, KV head) run
 //    back to back on one XCD (work-group w runs on XCD w mod 8): they stream the same
 //    K/V at about the same time and share that XCD's L2.
@@ -54,6 +58,9 @@ void prefill_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
   __shared__ float bias_lds[2][BIAS_ELEMS];
   __shared__ int pages_lds[kChunkPages + 1];
+  // each wave's queries in MFMA operand order: block (head i, k-step s) holds lane l's
+  // 16 bytes at l * 16, read back with one 16-byte LDS read per lane
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[4][HW][4][1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,7 +103,6 @@ void prefill_kernel(KernelArgs a) {
   const int row_p = p0 + 16 * tb + lr;
   const int wave_last_p = p0 + min(16 * tb + 15, t1 - t0 - 1);   // last row of the wave
   const bool wave_live = 16 * tb < t1 - t0;
-  bf16x8_t qreg[HW][4];
 #pragma unroll
   for (int i = 0; i < HW; ++i) {
     const int h = g * G + hg * HW + i;
@@ -105,9 +111,10 @@ void prefill_kernel(KernelArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4_t v = row_ok ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
-      qreg[i][s] = __builtin_bit_cast(bf16x8_t, v);
+      *reinterpret_cast<u32x4_t*>(&q_lds[wave][i][s][16 * lane]) = v;
     }
   }
+  // (each wave reads only its own queries, after its own writes: no barrier needed)
 
   // ---- page ids of a chunk of keys, staged in LDS ----
   const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
@@ -228,8 +235,11 @@ void prefill_kernel(KernelArgs a) {
         const bf16x8_t kop = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
 #pragma unroll
-        for (int i = 0; i < HW; ++i)
-          sacc[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[i][s], sacc[i][kt], 0, 0, 0);
+        for (int i = 0; i < HW; ++i) {
+          const bf16x8_t qop = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(&q_lds[wave][i][s][16 * lane]));
+          sacc[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop, sacc[i][kt], 0, 0, 0);
+        }
       }
     }
 
@@ -269,8 +279,23 @@ void prefill_kernel(KernelArgs a) {
         m_run[i] = m_new;
       }
     }
-    // P = exp(s - m) from the logits again, packed as the B operand of the PV MFMA
-    bf16x8_t pop[HW];
+    // V^T fragments of the tile (each feeds all HW heads)
+    bf16x8_t vop[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int cc = 2 * dt + ((lr & 3) >> 1);
+      const int k0 = 4 * lq + (lr >> 2);
+      const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
+      const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
+      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off0));
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off1));
+      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
+      vop[dt] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
+    }
+    // per head: P = exp(s - m) from the logits again, packed as the B operand, then
+    // O^T += V^T P^T (the next head's exponentials overlap these MFMAs)
 #pragma unroll
     for (int i = 0; i < HW; ++i) {
       const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]) * kLog2e;
@@ -287,25 +312,10 @@ void prefill_kernel(KernelArgs a) {
       l_run[i] += psum;
       const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
                           pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
-      pop[i] = __builtin_bit_cast(bf16x8_t, pk);
-    }
-
-    // O^T += V^T P^T; each V^T fragment feeds all HW heads
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int cc = 2 * dt + ((lr & 3) >> 1);
-      const int k0 = 4 * lq + (lr >> 2);
-      const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
-      const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
-      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off0));
-      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off1));
-      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
-      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
-#pragma unroll
-      for (int i = 0; i < HW; ++i)
-        o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i], o[i][dt], 0, 0, 0);
+      for (int dt = 0; dt < 8; ++dt)
+        o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, o[i][dt], 0, 0, 0);
     }
   };
 
