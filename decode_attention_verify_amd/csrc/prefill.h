@@ -212,10 +212,6 @@ void prefill_kernel(KernelArgs a) {
       if (e < BIAS_ELEMS) bl[e] = X.bs[q];
     }
   };
-  // every key of the tile at j0 visible to every row of the work-group: no mask
-  auto tile_is_fast = [&](int j0) {
-    return j0 + kTileKeys - 1 <= p0 && (W == 0 || p_last - j0 <= W - 1);
-  };
   // attention of this wave's rows over the tile in LDS buffer `buf`
   auto compute_tile = [&](int j0, int buf, auto fast_tag) {
     constexpr bool FAST = decltype(fast_tag)::value;
@@ -319,23 +315,36 @@ void prefill_kernel(KernelArgs a) {
     }
   };
 
-  // ---- tile loop: the next tile's loads in flight while a tile is attended ----
+  // ---- tile loop: the next tile's loads in flight while a tile is attended. Tiles
+  // that need no mask form one contiguous run; the masked tiles before and after it run
+  // in loops of their own, so that each loop body holds one instance of the attention.
   const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
   Tile R;
   for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
     const int c1 = min(c0 + chunk_keys, j_end);
     stage_pages(c0, c1);
     const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+    // fast tiles i: c0 + 32 i + 31 <= p0, and with a window p_last - (c0 + 32 i) <= W - 1
+    int i_lo = 0;
+    if (W > 0) {
+      const int first = p_last - W + 1 - c0;             // smallest fast j0 - c0
+      i_lo = first <= 0 ? 0 : min((first + kTileKeys - 1) / kTileKeys, nt);
+    }
+    const int last = p0 - (kTileKeys - 1) - c0;           // largest fast j0 - c0
+    const int i_hi = last < 0 ? i_lo : max(i_lo, min(last / kTileKeys + 1, nt));
     load_tile(R, c0);
-    for (int i = 0; i < nt; ++i) {
+    auto step = [&](int i, auto fast_tag) {
       const int j0 = c0 + i * kTileKeys;
       const int buf = i & 1;
       store_tile(R, j0, buf);
       if (i + 1 < nt) load_tile(R, j0 + kTileKeys);
       __syncthreads();                       // tile i and its bias slices are in LDS
-      if (tile_is_fast(j0)) compute_tile(j0, buf, std::true_type{});
-      else compute_tile(j0, buf, std::false_type{});
-    }
+      compute_tile(j0, buf, fast_tag);
+    };
+    int i = 0;
+    for (; i < i_lo; ++i) step(i, std::false_type{});
+    for (; i < i_hi; ++i) step(i, std::true_type{});
+    for (; i < nt; ++i) step(i, std::false_type{});
   }
 
   // ---- epilogue: every row's output and log-sum-exp, per head ----
