@@ -260,6 +260,51 @@ def cpu_baseline_rows(case_cpu, tr, budget_s, block=32):
     }, out, lse
 
 
+def read_probe(lib, case, sp, fp8, num_cus, reps=8, seed=0):
+    """The read rate the split kernel's access pattern reaches on this device: buffers of
+    the size of the K and V caches together, streamed in one launch by rattn_read_probe
+    (whole (page, KV head) blocks in a random order, non-temporal 16-byte loads, 1 KiB
+    per 64-lane pass), rotated over enough copies that no pass hits in the caches."""
+    import torch
+    from decode_attention_verify_amd import binding
+    elem = 1 if fp8 else 2
+    block = sp.page_size * sp.head_dim * elem
+    nblocks = 2 * case.k_cache.numel() * elem // block
+    byts = nblocks * block
+    ncopies = max(2, min(4, math.ceil(CACHE_EVICT_BYTES / byts) + 1))
+    bufs = [torch.ones(byts, dtype=torch.uint8, device="cuda") for _ in range(ncopies)]
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    order = torch.randperm(nblocks, generator=g, device="cuda").to(torch.int32)
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    waves = 8 * num_cus                          # 64 KiB in flight per CU at 4 KiB blocks
+    stream = torch.cuda.current_stream()
+    vp = ctypes.c_void_p
+
+    def one(i):
+        st = lib.rattn_read_probe(vp(bufs[i % ncopies].data_ptr()), nblocks, block,
+                                  vp(order.data_ptr()), waves, vp(sink.data_ptr()),
+                                  vp(stream.cuda_stream))
+        if st != binding.RATTN_OK:
+            raise binding.RattnError(st, "rattn_read_probe")
+    for i in range(2):
+        one(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        one(i)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    del bufs
+    return {"GBps": round(byts / secs / 1e9, 1),
+            "frac_of_peak": round(byts / secs / 1e9 / HBM_PEAK_GBPS, 4),
+            "bytes_per_pass": byts,
+            "pattern": "%d blocks of %d B (the K and V caches' size) in a random order, "
+                       "non-temporal 16-byte loads, 1 KiB per 64-lane pass, %d single-wave "
+                       "work-groups, one launch (rattn_read_probe)" % (nblocks, block, waves)}
+
+
 def parity_of(out_gpu, lse_gpu, ref_out, ref_lse):
     import numpy as np
     sel = ~np.isnan(ref_lse)
@@ -356,6 +401,8 @@ def main():
     ap.add_argument("--op", default="decode", choices=("decode", "append"),
                     help="decode: the attention call (default); append: the KV-cache write "
                          "of each sequence's new tokens, on the same workload's shapes")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the streaming-read probe over the same K/V caches")
     ap.add_argument("--hot-cache", action="store_true",
                     help="after the timed steps, time as many on one input copy (a warm-cache "
                          "figure, reported beside the main one)")
@@ -466,6 +513,7 @@ def main():
     say("warmup done (%d steps, %d input copies, %.0f MB each)" % (
         args.warmup, ncopies, per_copy / 1e6))
 
+    prefill_plan = info["kernel"] == binding.RATTN_KERNEL_PREFILL
     K = args.steps
     stride = max(1, args.event_stride)
     nrec = (K + stride - 1) // stride
@@ -490,6 +538,10 @@ def main():
             step(0)
         torch.cuda.synchronize()
         hot_us = round((time.perf_counter() - th) * 1e6 / K, 3)
+    probe = None
+    if not args.no_read_probe and not prefill_plan:
+        probe = read_probe(lib, case, sp, fp8, info["num_cus"])
+        say("read probe: %.0f GB/s" % probe["GBps"])
     flags = plan.debug_flags()
     if flags:
         raise RuntimeError("device flags %d on valid input" % flags)
@@ -574,6 +626,7 @@ def main():
             "algorithmic_flops_per_launch": tr.flops,
         }),
         "input_copies": ncopies,
+        "read_probe": probe,
     }
 
     if not args.no_cpu_baseline:

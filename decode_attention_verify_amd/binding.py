@@ -75,12 +75,14 @@ def load(path=None):
     lib.rattn_profile_begin.argtypes = [vp, i32, i32]
     lib.rattn_profile_end.argtypes = [vp, f32p, f32p, i32p]
     lib.rattn_append_kv.argtypes = [ctypes.POINTER(Problem)] + [vp] * 10
+    lib.rattn_read_probe.argtypes = [vp, ctypes.c_int64, i32, vp, i32, vp, vp]
     lib.rattn_status_string.argtypes = [ctypes.c_int]
     lib.rattn_status_string.restype = ctypes.c_char_p
     lib.rattn_abi_version.argtypes = []
     for fn in ("rattn_plan", "rattn_plan_describe", "rattn_plan_get_info", "rattn_decode",
                "rattn_free", "rattn_debug_flags", "rattn_profile_begin", "rattn_profile_end",
-               "rattn_abi_version", "rattn_append_kv", "rattn_decode_varlen"):
+               "rattn_abi_version", "rattn_append_kv", "rattn_decode_varlen",
+               "rattn_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int32
     if lib.rattn_abi_version() != ABI_VERSION:
         raise ImportError("librattn ABI %d, binding expects %d" % (lib.rattn_abi_version(),

@@ -266,6 +266,16 @@ rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const
   return rattn::launch_append_kv(a, stream) == 0 ? RATTN_OK : RATTN_E_HIP;
 }
 
+rattn_status rattn_read_probe(const void* buf, int64_t nblocks, int32_t block_bytes,
+                              const int32_t* order, int32_t waves, void* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr || nblocks < 1 || block_bytes < 1024 ||
+      block_bytes % 1024 != 0 || waves < 1 || waves > (1 << 20))
+    return RATTN_E_INVALID;
+  return rattn::launch_read_probe(buf, nblocks, block_bytes, order, waves, sink, stream) == 0
+             ? RATTN_OK
+             : RATTN_E_HIP;
+}
+
 rattn_status rattn_free(rattn_plan_t plan) {
   if (plan == nullptr) return RATTN_OK;
   destroy_events(plan);

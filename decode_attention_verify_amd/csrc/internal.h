@@ -134,6 +134,8 @@ int64_t combine_blocks(int64_t rows, int splits_per_unit);
 int launch_append_kv(const AppendArgs& a, void* stream);
 int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
+int launch_read_probe(const void* buf, int64_t nblocks, int block_bytes, const int32_t* order,
+                      int waves, void* sink, void* stream);
 // Resident split-kernel work-groups per CU for this variant (0 if the query fails).
 int split_kv_blocks_per_cu(int waves, bool fp8, bool even);
 

@@ -8,6 +8,7 @@
 //    quantisation for an FP8 cache;
 //  * prefill.h: the same attention for chunks of many query rows per sequence (chunked
 //    prefill), on the MFMA units;
+//  * probe.h: a streaming-read probe with the split kernel's load pattern (measurement);
 //  * device_common.h: device helpers and the work partition.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -16,6 +17,7 @@
 #include "append.h"
 #include "combine.h"
 #include "prefill.h"
+#include "probe.h"
 #include "split_kv.h"
 
 namespace rattn {
@@ -121,6 +123,13 @@ int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* str
   if (heads_per_wave == 2 && group == 8)
     return launch(prefill_kernel<2, 4>, grid, dim3(256), stream, a, ev_start, ev_stop);
   return (int)hipErrorInvalidValue;
+}
+
+int launch_read_probe(const void* buf, int64_t nblocks, int block_bytes, const int32_t* order,
+                      int waves, void* sink, void* stream) {
+  return launch(read_probe_kernel, dim3((unsigned)waves), dim3(64), stream,
+                ProbeArgs{(const unsigned char*)buf, nblocks, block_bytes, order, (u32x4_t*)sink},
+                nullptr, nullptr);
 }
 
 int launch_append_kv(const AppendArgs& a, void* stream) {

@@ -221,6 +221,17 @@ rattn_status rattn_profile_begin(rattn_plan_t plan, int32_t max_calls, int32_t s
 rattn_status rattn_profile_end(rattn_plan_t plan, float* split_ms, float* combine_ms,
                                int32_t* ncalls);
 
+/* Measurement aid (not part of the attention): read `nblocks` blocks of `block_bytes`
+ * bytes (a multiple of 1024) of the device buffer `buf`, block order[i] i-th (device int32
+ * [nblocks], a permutation of 0..nblocks-1; NULL = in place order; entries outside
+ * [0, nblocks) read a clamped block), with the split kernel's load pattern: non-temporal
+ * 16-byte loads, each 64-lane pass reading 1 KiB of contiguous bytes, two blocks in flight
+ * per wave, `waves` single-wave work-groups sharing the blocks evenly. `sink` is device
+ * memory of 1024 bytes that the kernel may write. Asynchronous on `stream`; a benchmark
+ * times it to report the read rate this access pattern reaches on the device. */
+rattn_status rattn_read_probe(const void* buf, int64_t nblocks, int32_t block_bytes,
+                              const int32_t* order, int32_t waves, void* sink, void* stream);
+
 const char* rattn_status_string(rattn_status status);
 int32_t rattn_abi_version(void);
 

@@ -157,3 +157,13 @@ def test_planner_prefill(hq, n, tokens):
     assert info.grid_x % 8 == 0 and blocks <= info.grid_x < blocks + 8
     assert info.combine_blocks == 0 and info.row_tiles == 4
     assert binding.rattn_plan_describe(headline(), 256).kernel == binding.RATTN_KERNEL_SPLIT_KV
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = binding.load()
+    vp = ctypes.c_void_p
+    one = vp(16)                               # never dereferenced: rejected on the host
+    for args in ((None, 4, 4096, None, 8, one, None), (one, 0, 4096, None, 8, one, None),
+                 (one, 4, 1000, None, 8, one, None), (one, 4, 4096, None, 0, one, None),
+                 (one, 4, 4096, None, 8, None, None)):
+        assert lib.rattn_read_probe(*args) == binding.RATTN_E_INVALID
