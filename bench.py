@@ -53,6 +53,8 @@ WORKLOADS = {
                   "seq_lens U[2048,32768], bf16 paged KV (page 16)",
     "window_b64": "sliding-window (W=1024) layer decode, 48q/8kv, d=128, batch 64, 1 row, "
                   "seq_lens U[2048,32768], bf16 paged KV (page 16)",
+    "window_verify_b16": "speculative verify, 8 causal rows, sliding-window (W=1024) layer, 48q/8kv, "
+                         "d=128, batch 16, seq_lens U[2048,32768], bf16 paged KV (page 16)",
     "verify_b16": "speculative verify, 8 causal rows, 48q/8kv, d=128, batch 16, full layer, "
                   "seq_lens log-uniform [32768,262144], bf16 paged KV (page 16)",
     "fp8_1m": "full-context layer decode, 48q/8kv, d=128, batch 1, 1 row, 1,048,576 keys, "

@@ -115,7 +115,11 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   // quarters) and the E4M3 cache, which decodes every element (the 1M-key decode:
   // 529 us against 542 us).
   // No work-group gets fewer than 4 tiles (128 keys): every piece of a shared unit costs
-  // a partial and a merge.
+  // a partial and a merge. Units of multi-wave groups stay whole when they alone give
+  // every CU four waves: then splitting buys little and the merge of their many rows
+  // costs more (9-row verify over W = 512 on 64q/16kv, 256 units: 26.6 us whole against
+  // 30.7 us in two pieces, 7 us of it the merge; the 8-row verify over W = 1024 on
+  // 48q/8kv has 128 units and is fastest in four pieces, 30.2 us against 32.3 in two).
   const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
   const bool latency_bound = pl.waves > 1 || p.kv_dtype == RATTN_KV_FP8_E4M3;
   const int64_t target = std::max<int64_t>(1, latency_bound ? slots : slots * 3 / 4);
@@ -128,6 +132,7 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
     // every unit spans about the same keys (a window, or a single sequence): an equal
     // number of pieces per unit is balanced and needs no search for a work-group's unit
     k = std::max<int64_t>(1, std::min<int64_t>(target / units, tiles / 4));
+    if (pl.waves > 1 && units * pl.waves >= 4 * (int64_t)std::max(num_cus, 1)) k = 1;
     k = std::min<int64_t>(k, std::max<int64_t>(1, kMaxGroups / units));
     groups = k * units;
   } else {

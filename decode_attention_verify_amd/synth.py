@@ -79,6 +79,9 @@ def _named_specs():
                            ("uniform", 2048, 32768)),
         "window_b64": Spec("window_b64", 64, 1, 48, 8, 128, 1024, 1024, 16, KV_BF16,
                            ("uniform", 2048, 32768)),
+        # the sliding-window layers during an 8-row verify step
+        "window_verify_b16": Spec("window_verify_b16", 16, 8, 48, 8, 128, 1024, 1031, 16,
+                                  KV_BF16, ("uniform", 2048, 32768)),
         # full-context layer, batch 1, 100,000 keys
         "full_100k": Spec("full_100k", 1, 1, 48, 8, 128, 0, 131071, 16, KV_BF16, 100000,
                           bias_decay=1e-5),

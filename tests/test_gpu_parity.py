@@ -32,6 +32,10 @@ def test_sliding_window(name):
     check_case(synth.spec(name), seed=0, gen_device="cuda")
 
 
+def test_window_verify_b16():
+    check_case(synth.spec("window_verify_b16"), seed=0, gen_device="cuda")
+
+
 def test_full_context_100k():
     check_case(synth.spec("full_100k"), seed=0, gen_device="cuda")
 
