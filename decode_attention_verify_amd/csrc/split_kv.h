@@ -301,7 +301,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         const int tid = wave * 64 + lane;
 #pragma unroll
         for (int q = 0; q < kBiasPerThread; ++q)
-          if (bs_row[q] >= 0) bl[tid + 64 * WR * q] = X.bs[q];
+          bl[tid + 64 * WR * q] = X.bs[q];   // < kMaxBiasSlice; past the slice: unread
       }
       // this wave's share -> LDS as bf16 (swizzled). V of keys outside [k_lo, L) becomes
       // zero, so that P = 0 times a stale or NaN value cannot reach the accumulator.
@@ -318,7 +318,10 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
             *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, lr)) = v;
           } else {
             const int j = j0 + kk;
-            if (!fast && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
+            if (!fast) {                                // uniform; inside, a mask
+              const unsigned keep = (j < k_lo || j >= L) ? 0u : ~0u;
+              v &= u32x4_t{keep, keep, keep, keep};
+            }
             *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, lr)) = v;
           }
         } else {
@@ -327,7 +330,10 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
           u32x4_t raw = X.x[m];
           if (kv == 1) {
             const int j = j0 + kk;
-            if (!fast && (j < k_lo || j >= L)) raw = u32x4_t{0, 0, 0, 0};
+            if (!fast) {
+              const unsigned keep = (j < k_lo || j >= L) ? 0u : ~0u;
+              raw &= u32x4_t{keep, keep, keep, keep};
+            }
           }
           const u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
           const u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
