@@ -40,11 +40,11 @@ __device__ __forceinline__ float ldf_stream(const float* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Four E4M3 codes (one dword) -> four bf16 values (two dwords), in code order. Exact:
@@ -58,19 +58,34 @@ __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(unsigned int w) {
   return r;
 }
 
-// The 4 lanes lr, lr+16, lr+32, lr+48 hold the same query row. (The gfx950 permlane
-// swaps would keep this in the VALU, but this compiler folds the two results of a swap
-// whose operands are the same value into one, so the reductions use lane shuffles.)
+// The 4 lanes lr, lr+16, lr+32, lr+48 hold the same query row. The gfx950 permlane
+// swaps exchange their values inside the VALU, without an LDS round trip: a 16-lane
+// swap of a value with itself leaves lane l holding its own value and that of lane
+// l ^ 16 (one in each result, in an order that depends on l), a 32-lane swap that of
+// lane l ^ 32.
+template <int SPAN>
+__device__ __forceinline__ void lane_pair(float x, float& p, float& q) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = SPAN == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  p = __uint_as_float(r[0]);
+  q = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  float p, q;
+  lane_pair<16>(x, p, q);
+  x = fmaxf(p, q);
+  lane_pair<32>(x, p, q);
+  return fmaxf(p, q);
 }
 
 __device__ __forceinline__ float wave_sum_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  float p, q;
+  lane_pair<16>(x, p, q);
+  x = p + q;
+  lane_pair<32>(x, p, q);
+  return p + q;
 }
 
 // Byte offset in the LDS V tile of 16-byte chunk `cc` (0..15) of key row `k` (0..31).
