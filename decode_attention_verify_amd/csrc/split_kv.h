@@ -77,7 +77,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   int T = 0;
   int64_t P = 0, t_begin = 0, t_end = 0;
   if (EVEN) {                                // even shares of the whole tile space
-    T = total_tiles(a, lane);
+    T = __builtin_amdgcn_readfirstlane(total_tiles(a, lane));   // the same in every lane
     P = min((int64_t)gridDim.x, (int64_t)T);
     if (wg >= P) return;                     // uniform over the work-group
     t_begin = wg * T / P;
@@ -135,6 +135,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     } else {
       int before;
       locate_tile(a, lane, (int)t_begin, b, before);
+      b = __builtin_amdgcn_readfirstlane(b);           // the same in every lane
+      before = __builtin_amdgcn_readfirstlane(before);
       sg = seq_geom(a, b, false);
       g = (t_begin - before) / sg.tiles;
       const int64_t ustart = before + (int64_t)g * sg.tiles;
@@ -175,6 +177,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     // discards), and every lane then reads its row's entries from LDS.
     const int slice_len = kTileKeys + n - 1;
     const int slice_elems = G * slice_len;     // <= kMaxBiasSlice (validated)
+    const int nbias = (slice_elems + 64 * WR - 1) / (64 * WR);   // slice loads per thread
     const int sub_lo = k_lo & ~15;           // first 16-key subtile holding a visible key
     const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
 
@@ -240,6 +243,15 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     // [k_lo, L) (at the two ends of the visible range) reads the nearest subtile that
     // has one instead; the masks of process_tile discard its keys.
     auto load_tile = [&](Tile& X, int j0) {
+      if constexpr (STAGE_BIAS) {
+        // the bias slice elements of this thread (a thread without one re-reads entry 0)
+#pragma unroll
+        for (int q = 0; q < kBiasPerThread; ++q) {
+          if (q > 0 && q >= nbias) break;   // uniform
+          const int d = min(max(L - 1 - j0 - bs_pos[q], 0), a.dmax);
+          X.bs[q] = ldf_stream(a.bias + (bs_row[q] >= 0 ? (unsigned)(bs_row[q] + d) : 0u));
+        }
+      }
       int64_t tok0[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -265,14 +277,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
               (const f32x4_t*)((const unsigned char*)(a.v_scale + tok0[kt]) + sc_off));
         }
       }
-      if constexpr (STAGE_BIAS) {
-        // the bias slice elements of this thread (a thread without one re-reads entry 0)
-#pragma unroll
-        for (int q = 0; q < kBiasPerThread; ++q) {
-          const int d = min(max(L - 1 - j0 - bs_pos[q], 0), a.dmax);
-          X.bs[q] = ldf_stream(a.bias + (bs_row[q] >= 0 ? (unsigned)(bs_row[q] + d) : 0u));
-        }
-      } else {
+      if constexpr (!STAGE_BIAS) {
         // row r of head h reads B[h][p_r - j] for its keys, distances clamped to [0, Dmax]
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -300,8 +305,10 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       if constexpr (STAGE_BIAS) {
         const int tid = wave * 64 + lane;
 #pragma unroll
-        for (int q = 0; q < kBiasPerThread; ++q)
+        for (int q = 0; q < kBiasPerThread; ++q) {
+          if (q > 0 && q >= nbias) break;   // uniform
           bl[tid + 64 * WR * q] = X.bs[q];   // < kMaxBiasSlice; past the slice: unread
+        }
       }
       // this wave's share -> LDS as bf16 (swizzled). V of keys outside [k_lo, L) becomes
       // zero, so that P = 0 times a stale or NaN value cannot reach the accumulator.
