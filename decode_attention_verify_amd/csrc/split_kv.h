@@ -25,7 +25,9 @@
 //    reference point moved only when a tile's maximum passes it by 8 ln 2;
 //  * FP8 (OCP E4M3) K/V are decoded exactly to bf16 with v_cvt_scalef32_pk_bf16_fp8; the
 //    K scale multiplies the logit column, the V scale multiplies P before its bf16
-//    rounding.
+//    rounding. A tile's 64 scales arrive with one 4-byte load per lane and are staged in
+//    LDS beside the tile (per-lane 16-byte scale loads cost 32 registers and 6 % of the
+//    1M-key decode).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,6 +54,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   __shared__ __attribute__((aligned(16))) unsigned char klds[TILE_BUFS][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[TILE_BUFS][kTileKeys * 256];
   __shared__ int pages_lds[kChunkPages + 1];
+  // E4M3: a tile's 32 K and 32 V scales, staged beside the tile
+  __shared__ __attribute__((aligned(16))) float scale_lds[FP8 ? TILE_BUFS : 1][FP8 ? 64 : 1];
   // Several waves load the bias slice of a tile together and share it through LDS; a
   // single wave gathers its row's entries one tile ahead in registers, which keeps the
   // read off each tile's critical path. Both the buffer count and every index into the
@@ -95,7 +99,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   constexpr int NSLOT = SLOTS / WR;
   struct Tile {
     u32x4_t x[NSLOT];
-    f32x4_t ks[2], vs[2];
+    float sc;    // E4M3: lane l's scale, of key l (K) or key l - 32 (V) of the tile
     // multi-wave groups: this thread's elements of the tile's bias slice; one wave:
     // the bias of its row for keys 4 lq + i of each subtile, gathered directly
     float bs[STAGE_BIAS ? kBiasPerThread : 8];
@@ -105,7 +109,6 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   // contiguous bytes (one bf16 row, two E4M3 rows); a pass spread over 16 rows caps the
   // read rate near 5.2 TB/s on MI355X, against 6.4 TB/s for contiguous passes
   const unsigned kv_off = FP8 ? (lane >> 3) * 128 + 16 * (lane & 7) : lq * 256 + 16 * lr;
-  const unsigned sc_off = 16 * lq;
   const unsigned char* kc = (const unsigned char*)a.k_cache;
   const unsigned char* vc = (const unsigned char*)a.v_cache;
 
@@ -269,13 +272,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         X.x[m] = ld16_stream(base + kv_off + 1024 * u);
       }
       if (FP8) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          X.ks[kt] = __builtin_nontemporal_load(
-              (const f32x4_t*)((const unsigned char*)(a.k_scale + tok0[kt]) + sc_off));
-          X.vs[kt] = __builtin_nontemporal_load(
-              (const f32x4_t*)((const unsigned char*)(a.v_scale + tok0[kt]) + sc_off));
-        }
+        // one 4-byte load per lane: the tile's 32 K scales, then its 32 V scales
+        const int64_t tok = ((lane & 16) ? tok0[1] : tok0[0]) + (lane & 15);
+        X.sc = __builtin_nontemporal_load((lane & 32 ? a.v_scale : a.k_scale) + tok);
       }
       if constexpr (!STAGE_BIAS) {
         // row r of head h reads B[h][p_r - j] for its keys, distances clamped to [0, Dmax]
@@ -354,6 +353,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
           }
         }
       }
+      float* sl = scale_lds[FP8 && TILE_BUFS == 2 ? buf : 0];
+      if (FP8 && wave == 0) sl[lane] = X.sc;
       if (WR > 1) __syncthreads();            // the whole tile is in LDS buffer `buf`
 
       // S^T = K Q^T : lane (lr, lq) of MFMA s reads key 16 kt + lr, dims 32 s + 8 lq ..;
@@ -381,6 +382,16 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
           else bv[kt][i] = X.bs[4 * kt + i];
         }
 
+      // E4M3: the scales of this lane's keys 4 lq + i of each subtile
+      f32x4_t ks[2], vs[2];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          ks[kt] = *reinterpret_cast<const f32x4_t*>(sl + 16 * kt + 4 * lq);
+          vs[kt] = *reinterpret_cast<const f32x4_t*>(sl + 32 + 16 * kt + 4 * lq);
+        }
+      }
+
       // logits, mask, online softmax; P packed as the B operand of O^T += V^T P^T
       float sv[2][4];
       float mt = kNegInf;
@@ -388,7 +399,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float scl = FP8 ? a.softmax_scale * X.ks[kt][i] : a.softmax_scale;
+          const float scl = FP8 ? a.softmax_scale * ks[kt][i] : a.softmax_scale;
           float sc = __builtin_fmaf(sacc[kt][i], scl, bv[kt][i]);
           if (!fast) {
             const int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
@@ -422,7 +433,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         for (int i = 0; i < 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][i], kLog2e, mb));
           psum += p;
-          pv[kt][i] = FP8 ? (p > 0.f ? p * X.vs[kt][i] : 0.f) : p;
+          pv[kt][i] = FP8 ? (p > 0.f ? p * vs[kt][i] : 0.f) : p;
         }
       }
       l_run += psum;
