@@ -25,7 +25,9 @@
 //    key j at slice position (t - t0) - (j - j0) + 31;
 //  * logits, masks (causal and window, compiled only into the instance for tiles that
 //    cross the diagonal or the window edge), lazy online softmax (one rescale test per
-//    tile for all heads) and P V follow the decode kernel's layouts; the V^T fragments are
+//    tile for all heads) and P V follow the decode kernel's layouts; the logits are kept
+//    in base 2 (scale and staged bias multiplied by log2 e) and held in registers from
+//    the tile maximum to the exponentials; the V^T fragments are
 //    read once per tile and each head's P V MFMAs follow its exponentials, so that the
 //    next head's VALU work overlaps them. S^T = K Q^T leaves lane (lr, lq) row lr with
 //    keys 4 lq + i, which is the B operand of O^T += V^T P^T, and V^T is read back with
@@ -73,6 +75,9 @@ void prefill_kernel(KernelArgs a) {
   const int64_t Hkv = a.num_kv_heads;
   const int S = a.page_size;
   const int W = a.window;
+  const float scale2 = a.softmax_scale * kLog2e;
+  constexpr float kRescaleSlack2 = 8.f;      // kRescaleSlack in base 2
+  constexpr float kLn2 = 0.6931471805599453f;
 
   // ---- which (sequence, KV head, token block): consecutive logical ids on one XCD ----
   const int NB = (n + M - 1) / M;
@@ -209,7 +214,7 @@ void prefill_kernel(KernelArgs a) {
 #pragma unroll
     for (int q = 0; q < BIAS_PER_THREAD; ++q) {
       const int e = tid + 256 * q;
-      if (e < BIAS_ELEMS) bl[e] = X.bs[q];
+      if (e < BIAS_ELEMS) bl[e] = X.bs[q] * kLog2e;   // base-2 logits
     }
   };
   // attention of this wave's rows over the tile in LDS buffer `buf`
@@ -240,8 +245,9 @@ void prefill_kernel(KernelArgs a) {
     }
 
     // logits (with masks on the tiles that need them) of head i, key (kt, c)
+    // logits in base 2 (scaled by log2 e): the exponentials need no multiply
     auto logit = [&](int i, int kt, int c) {
-      float sc = __builtin_fmaf(sacc[i][kt][c], a.softmax_scale,
+      float sc = __builtin_fmaf(sacc[i][kt][c], scale2,
                                 bl[bias_pos0 + i * SL - 16 * kt - c]);
       if (!FAST) {
         const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
@@ -252,6 +258,7 @@ void prefill_kernel(KernelArgs a) {
     };
     // each head's tile maximum; one test for all heads, the rare rescale in one branch
     float mt[HW];
+    float sv[HW][2][4];
     bool grow_any = false;
 #pragma unroll
     for (int i = 0; i < HW; ++i) {
@@ -259,16 +266,19 @@ void prefill_kernel(KernelArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x = fmaxf(x, logit(i, kt, c));
+        for (int c = 0; c < 4; ++c) {
+          sv[i][kt][c] = logit(i, kt, c);
+          x = fmaxf(x, sv[i][kt][c]);
+        }
       mt[i] = wave_max_rows(x);
-      grow_any |= mt[i] > m_run[i] + kRescaleSlack;
+      grow_any |= mt[i] > m_run[i] + kRescaleSlack2;
     }
     if (__ballot(grow_any) != 0) {
 #pragma unroll
       for (int i = 0; i < HW; ++i) {
-        const bool grow = mt[i] > m_run[i] + kRescaleSlack;
+        const bool grow = mt[i] > m_run[i] + kRescaleSlack2;
         const float m_new = grow ? mt[i] : m_run[i];
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[i] - m_new) * kLog2e) : 1.f;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[i] - m_new) : 1.f;
         l_run[i] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
@@ -294,14 +304,14 @@ void prefill_kernel(KernelArgs a) {
     // O^T += V^T P^T (the next head's exponentials overlap these MFMAs)
 #pragma unroll
     for (int i = 0; i < HW; ++i) {
-      const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]) * kLog2e;
+      const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]);
       float pv[2][4];
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(logit(i, kt, c), kLog2e, mb));
+          const float p = __builtin_amdgcn_exp2f(sv[i][kt][c] + mb);
           psum += p;
           pv[kt][c] = p;
         }
@@ -362,7 +372,9 @@ void prefill_kernel(KernelArgs a) {
       const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       *reinterpret_cast<u32x2_t*>(op + 16 * dt + 4 * lq) = w;
     }
-    if (lq == 0 && a.lse != nullptr) a.lse[row] = l > 0.f ? m_run[i] + __logf(l) : kNegInf;
+    // m_run is in base 2
+    if (lq == 0 && a.lse != nullptr)
+      a.lse[row] = l > 0.f ? m_run[i] * kLn2 + __logf(l) : kNegInf;
   }
 }
 
