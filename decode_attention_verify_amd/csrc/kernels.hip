@@ -115,13 +115,13 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_s
 
 int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
                    void* ev_start, void* ev_stop) {
-  const dim3 grid((unsigned)a.split_groups);
+  const dim3 grid((unsigned)a.split_groups), block(64 * kPrefillWaves);
   if (heads_per_wave == 3 && group == 6)
-    return launch(prefill_kernel<3, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
+    return launch(prefill_kernel<3, 2, kPrefillWaves>, grid, block, stream, a, ev_start, ev_stop);
   if (heads_per_wave == 2 && group == 4)
-    return launch(prefill_kernel<2, 2>, grid, dim3(256), stream, a, ev_start, ev_stop);
+    return launch(prefill_kernel<2, 2, kPrefillWaves>, grid, block, stream, a, ev_start, ev_stop);
   if (heads_per_wave == 2 && group == 8)
-    return launch(prefill_kernel<2, 4>, grid, dim3(256), stream, a, ev_start, ev_stop);
+    return launch(prefill_kernel<2, 4, kPrefillWaves>, grid, block, stream, a, ev_start, ev_stop);
   return (int)hipErrorInvalidValue;
 }
 

@@ -82,7 +82,7 @@ static Plan make_prefill_plan(const rattn_problem& p, int32_t num_cus, int32_t b
   Plan pl{};
   pl.prefill = 1;
   pl.prefill_hw = prefill_heads_per_wave(G);
-  pl.waves = 4;
+  pl.waves = kPrefillWaves;
   pl.num_cus = num_cus;
   pl.blocks_per_cu = blocks_per_cu;
   const int64_t blocks = (p.n_query_rows + prefill_tokens(G) - 1) / prefill_tokens(G);

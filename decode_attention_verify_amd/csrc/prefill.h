@@ -8,14 +8,16 @@
 //
 // With thousands of rows per (sequence, KV head) the work is a dense contraction, so
 // this kernel is built around the MFMA units rather than around streaming:
-//  * one work-group of 4 waves per (sequence, KV head, block of M query tokens); a wave
-//    takes 16 consecutive tokens for HW query heads of the group, one 16-row MFMA tile
-//    per head (3 heads for a 6-head group, 2 for 4- and 8-head groups: a head's O
-//    accumulators take 32 of a wave's registers), so M = 16 * 4 / (G / HW);
+//  * one work-group of NW = 8 waves (two per SIMD, so that one wave's exponentials and
+//    logits overlap the other's matrix instructions) per (sequence, KV head, block of M
+//    query tokens); a wave takes 16 consecutive tokens for HW query heads of the group,
+//    one 16-row MFMA tile per head (3 heads for a 6-head group, 2 for 4- and 8-head
+//    groups: a head's O accumulators take 32 of a wave's 256 registers), so
+//    M = 16 * NW / (G / HW);
 //  * each wave's queries sit in LDS in MFMA operand order (one 16-byte read per lane and
 //    head per k-step), which leaves the registers to the O accumulators;
-//  * 32-key K/V tiles are loaded by all 256 threads (16-byte loads through the caches,
-//    which the unit's other blocks hit; a wave reads 1 KiB of contiguous key rows); the
+//  * 32-key K/V tiles are loaded by all the group's threads (16-byte loads through the
+//    caches, which the unit's other blocks hit; 16 lanes read a 256-byte key row); the
 //    next tile's loads are in flight while a tile is attended; tiles are double-buffered
 //    in LDS with one barrier per tile; every K or V fragment read from LDS feeds the
 //    MFMAs of all HW heads;
@@ -46,23 +48,26 @@
 
 namespace rattn {
 
-template <int HW, int HG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int HW, int HG, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(KernelArgs a) {
-  constexpr int TB = 4 / HG;                 // 16-token blocks per work-group
+  constexpr int NT = 64 * NW;                // threads
+  constexpr int TB = NW / HG;                // 16-token blocks per work-group
   constexpr int M = 16 * TB;                 // query tokens per work-group
   constexpr int G = HW * HG;                 // query heads per KV head
   constexpr int SL = M + kTileKeys - 1;      // bias slice per head and tile
   constexpr int BIAS_ELEMS = G * SL;
-  constexpr int BIAS_PER_THREAD = (BIAS_ELEMS + 255) / 256;
-  static_assert(TB * HG == 4 && TB >= 1, "four waves per work-group");
+  constexpr int BIAS_PER_THREAD = (BIAS_ELEMS + NT - 1) / NT;
+  constexpr int KPP = NT / 16;               // keys one load pass of the group covers
+  constexpr int SPK = kTileKeys / KPP;       // passes per K (or V) tile
+  static_assert(TB * HG == NW && TB >= 1 && SPK >= 1 && SPK * KPP == kTileKeys, "shape");
   __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
   __shared__ float bias_lds[2][BIAS_ELEMS];
   __shared__ int pages_lds[kChunkPages + 1];
   // each wave's queries in MFMA operand order: block (head i, k-step s) holds lane l's
   // 16 bytes at l * 16, read back with one 16-byte LDS read per lane
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[4][HW][4][1024];
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[NW][HW][4][1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,7 +133,7 @@ void prefill_kernel(KernelArgs a) {
     __syncthreads();                         // the previous chunk's ids and tiles are done
     chunk_p0 = c0 >> a.page_shift;
     const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
-    for (int i = tid; i < np; i += 256) {
+    for (int i = tid; i < np; i += NT) {
       int ph = pt_row[chunk_p0 + i];
       if (ph < 0 || ph >= a.num_pages) {
         atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
@@ -146,7 +151,7 @@ void prefill_kernel(KernelArgs a) {
   // ---- a tile's loads: slot m = (K|V, 16-key subtile); thread tid reads 16 bytes of key
   // tid / 16 of the subtile (a wave reads 4 whole key rows, 1 KiB contiguous) ----
   struct Tile {
-    u32x4_t x[4];
+    u32x4_t x[2 * SPK];
     float bs[BIAS_PER_THREAD];
   };
   const unsigned char* kc = (const unsigned char*)a.k_cache;
@@ -162,16 +167,17 @@ void prefill_kernel(KernelArgs a) {
       tok0[kt] = ((int64_t)phys_at(js) * Hkv + g) * S + (js & (S - 1));
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int kt = m & 1;
-      const unsigned char* base = (m >> 1 ? vc : kc) + (tok0[kt] + ld_key) * 256;
+    for (int m = 0; m < 2 * SPK; ++m) {
+      const int kk = (m % SPK) * KPP + ld_key;    // key of the tile
+      const int64_t tok = (kk >> 4 ? tok0[1] : tok0[0]) + (kk & 15);
+      const unsigned char* base = (m / SPK ? vc : kc) + tok * 256;
       X.x[m] = ld16(base + 16 * ld_ch);   // cached: the unit's other blocks read it too
     }
 #pragma unroll
     for (int q = 0; q < BIAS_PER_THREAD; ++q) {
       // slice element e: head e / SL of the group, distance p0 - j0 - 31 + e % SL,
       // clamped to [0, Dmax] (a masked key reads an in-range entry)
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       const int hi = e / SL;
       const int d = min(max(p0 - j0 - (kTileKeys - 1) + (e - hi * SL), 0), a.dmax);
       const unsigned idx = e < BIAS_ELEMS ? (unsigned)((g * G + hi) * (a.dmax + 1) + d) : 0u;
@@ -200,10 +206,10 @@ void prefill_kernel(KernelArgs a) {
     float* bl = bias_lds[buf];
     const bool edge = j0 < k_lo || j0 + kTileKeys > L;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int kk = 16 * (m & 1) + ld_key;
+    for (int m = 0; m < 2 * SPK; ++m) {
+      const int kk = (m % SPK) * KPP + ld_key;
       u32x4_t v = X.x[m];
-      if (m >> 1) {
+      if (m / SPK) {
         const int j = j0 + kk;
         if (edge && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
         *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, ld_ch)) = v;
@@ -213,7 +219,7 @@ void prefill_kernel(KernelArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < BIAS_PER_THREAD; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + NT * q;
       if (e < BIAS_ELEMS) bl[e] = X.bs[q] * kLog2e;   // base-2 logits
     }
   };

@@ -115,7 +115,8 @@ typedef struct {
   int32_t num_splits;        /* split work-groups per (sequence, KV head), nominal        */
   int32_t keys_per_split;    /* keys per split work-group at max_seq_len, nominal         */
   int32_t tile_keys;         /* keys per inner-loop step                                  */
-  int32_t row_tiles;         /* waves per split work-group, one 16-row MFMA tile each     */
+  int32_t row_tiles;         /* waves per work-group (split: one 16-row MFMA tile each;   */
+                             /* prefill: 8)                                               */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (work-groups, 1, 1)             */
   int32_t combine_blocks;    /* combine work-groups; 0 when the grid is one work-group    */
   int32_t num_cus;           /* compute units the plan was sized for                      */

@@ -145,17 +145,18 @@ def test_combine_shape_follows_the_pieces():
     assert verify.combine_blocks == 16 * 8 * 48 // 4
 
 
-@pytest.mark.parametrize("hq,n,tokens", [(48, 11, 32), (48, 2048, 32), (32, 17, 32),
-                                         (64, 9, 16), (64, 1000, 16)])
+@pytest.mark.parametrize("hq,n,tokens", [(48, 11, 64), (48, 2048, 64), (32, 17, 64),
+                                         (64, 9, 32), (64, 1000, 32)])
 def test_planner_prefill(hq, n, tokens):
-    # more than 64 packed rows: one prefill work-group per (sequence, KV head, block of
-    # query tokens), a grid rounded up to a multiple of 8 (one share per XCD), no combine
+    # more than 64 packed rows: one 8-wave prefill work-group per (sequence, KV head, block
+    # of query tokens: 4 blocks of 16 for 6- and 4-head groups, 2 for 8-head groups), a
+    # grid rounded up to a multiple of 8 (one share per XCD), no combine
     p = headline(batch=3, num_q_heads=hq, n_query_rows=n)
     info = binding.rattn_plan_describe(p, 256)
     assert info.kernel == binding.RATTN_KERNEL_PREFILL
     blocks = 3 * 8 * -(-n // tokens)
     assert info.grid_x % 8 == 0 and blocks <= info.grid_x < blocks + 8
-    assert info.combine_blocks == 0 and info.row_tiles == 4
+    assert info.combine_blocks == 0 and info.row_tiles == 8
     assert binding.rattn_plan_describe(headline(), 256).kernel == binding.RATTN_KERNEL_SPLIT_KV
 
 
