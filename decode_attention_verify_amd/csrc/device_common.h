@@ -40,6 +40,15 @@ __device__ __forceinline__ float ldf_stream(const float* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// Four adjacent floats at any 4-byte aligned address. The type's 4-byte alignment keeps
+// the access defined: the compiler emits one 16-byte load where the target allows
+// unaligned dword-multiple accesses, else four 4-byte loads.
+typedef float f32x4u_t __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ f32x4_t ldf4u_stream(const float* p) {
+  const f32x4u_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4u_t*>(p));
+  return f32x4_t{v[0], v[1], v[2], v[3]};
+}
+
 // Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));

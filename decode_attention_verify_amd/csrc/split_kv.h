@@ -20,7 +20,8 @@
 //  * V is read back transposed with ds_read_b64_tr_b16, the gfx950 LDS transpose read;
 //  * the bias is sheared: per tile, each head of the group needs one contiguous slice of
 //    32 + n - 1 distances, which row r reads shifted by n - 1 - r; multi-wave groups load
-//    the slices once (coalesced) into LDS, a single wave gathers its row's entries;
+//    the slices once (coalesced) into LDS, a single wave reads its row's entries four
+//    adjacent distances per 16-byte load;
 //  * online softmax in fp32, one row per lane, row max across the 4 lanes of a row, the
 //    reference point moved only when a tile's maximum passes it by 8 ln 2;
 //  * FP8 (OCP E4M3) K/V are decoded exactly to bf16 with v_cvt_scalef32_pk_bf16_fp8; the
@@ -57,7 +58,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   // E4M3: a tile's 32 K and 32 V scales, staged beside the tile
   __shared__ __attribute__((aligned(16))) float scale_lds[FP8 ? TILE_BUFS : 1][FP8 ? 64 : 1];
   // Several waves load the bias slice of a tile together and share it through LDS; a
-  // single wave gathers its row's entries one tile ahead in registers, which keeps the
+  // single wave reads its row's entries one tile ahead in registers, which keeps the
   // read off each tile's critical path. Both the buffer count and every index into the
   // buffers derive from STAGE_BIAS (two buffers exactly when several waves share one).
   constexpr bool STAGE_BIAS = WR > 1;
@@ -280,14 +281,25 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         X.sc = __builtin_nontemporal_load((lane & 32 ? a.v_scale : a.k_scale) + tok);
       }
       if constexpr (!STAGE_BIAS) {
-        // row r of head h reads B[h][p_r - j] for its keys, distances clamped to [0, Dmax]
+        // row r of head h reads B[h][p_r - j] for its keys j = j0 + 16 kt + 4 lq + i: the
+        // four distances d0 - i (d0 = p_r - j0 - 16 kt - 4 lq) are adjacent table entries,
+        // read with one 16-byte load when all four lie in [0, Dmax] (four times fewer
+        // vector-memory instructions), else one by one with the distances clamped
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) {
+          const int d0 = row_p - (j0 + 16 * kt + 4 * lq);
+          if (d0 >= 3 && d0 <= a.dmax) {
+            const f32x4_t v = ldf4u_stream(a.bias + (unsigned)(bias_row + d0 - 3));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = min(max(row_p - (j0 + 16 * kt + 4 * lq + i), 0), a.dmax);
-            X.bs[4 * kt + i] = ldf_stream(a.bias + (unsigned)(bias_row + d));
+            for (int i = 0; i < 4; ++i) X.bs[4 * kt + i] = v[3 - i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int d = min(max(d0 - i, 0), a.dmax);
+              X.bs[4 * kt + i] = ldf_stream(a.bias + (unsigned)(bias_row + d));
+            }
           }
+        }
       }
     };
 

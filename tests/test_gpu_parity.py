@@ -135,6 +135,30 @@ def test_dmax_clamp_on_gpu():
     check_case(sp, seed=3, poison=False)
 
 
+@pytest.mark.parametrize("dmax", [0, 1, 2, 3, 4, 37])
+@pytest.mark.parametrize("n", [1, 2])
+def test_dmax_clamp_single_wave(dmax, n):
+    # 6 n <= 16 rows: one wave per piece, which reads its bias as four adjacent table
+    # entries per 16-byte load; tables of fewer than four entries per head, and tiles
+    # whose distances pass Dmax or run below zero, take the entries one by one
+    sp = small("full_100k", batch=3, n_rows=n, seq_len=("uniform", 300, 900), dmax=dmax,
+               name="dmax1")
+    check_case(sp, seed=40 + dmax, poison=False)
+
+
+@pytest.mark.parametrize("dmax", [2, 45])
+def test_dmax_clamp_fp8_single_wave(dmax):
+    sp = small("fp8_1m", batch=2, seq_len=("uniform", 200, 1500), dmax=dmax, name="dmax_fp8")
+    check_case(sp, seed=50 + dmax, poison=False)
+
+
+@pytest.mark.parametrize("L", [100001, 100002, 100003])
+def test_full_context_unaligned_lengths(L):
+    # every length modulo 4: the bias entries of a 16-byte load start at any 4-byte
+    # boundary of the table
+    check_case(small("full_100k", seq_len=L), seed=0, gen_device="cuda", kv_heads=[2, 5])
+
+
 def test_window_fp8():
     sp = small("window_b16", batch=4, n_rows=8, kv_format=synth.KV_FP8, page_size=64,
                name="window_fp8")
