@@ -11,7 +11,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librattn.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 RATTN_OK, RATTN_E_INVALID, RATTN_E_UNSUPPORTED, RATTN_E_HIP, RATTN_E_NOMEM = range(5)
 RATTN_KV_BF16, RATTN_KV_FP8_E4M3 = 0, 1
@@ -30,7 +30,7 @@ class Problem(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_splits", "keys_per_split", "tile_keys", "row_tiles", "grid_x", "grid_y",
-        "grid_z", "combine_blocks", "num_cus", "blocks_per_cu", "kernel", "reserved")] + [
+        "grid_z", "combine_blocks", "num_cus", "blocks_per_cu", "kernel", "pieces_per_group")] + [
         ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):

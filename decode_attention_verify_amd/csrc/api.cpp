@@ -31,6 +31,7 @@ bool log_enabled() {
 
 // Some unit is shared by several work-groups, so a combine launch merges partials.
 bool needs_combine(const rattn::Plan& pl) {
+  if (pl.ws > 1) return false;               // merged by the split kernel itself
   return pl.splits_per_unit > 1 || (pl.splits_per_unit == 0 && pl.split_groups > 1);
 }
 
@@ -50,7 +51,7 @@ void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* i
   info->num_cus = pl.num_cus;
   info->blocks_per_cu = pl.blocks_per_cu;
   info->kernel = pl.prefill ? RATTN_KERNEL_PREFILL : RATTN_KERNEL_SPLIT_KV;
-  info->reserved = 0;
+  info->pieces_per_group = pl.prefill ? 1 : pl.ws;
   info->workspace_bytes = pl.workspace_bytes;
 }
 
@@ -200,7 +201,7 @@ rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
                                  ev ? ev[1] : nullptr) == 0
                ? RATTN_OK
                : RATTN_E_HIP;
-  if (rattn::launch_split_kv(a, plan->plan.waves, fp8, stream, ev ? ev[0] : nullptr,
+  if (rattn::launch_split_kv(a, plan->plan.waves, fp8, plan->plan.ws, stream, ev ? ev[0] : nullptr,
                              ev ? ev[1] : nullptr) != 0)
     return RATTN_E_HIP;
   if (needs_combine(plan->plan) &&

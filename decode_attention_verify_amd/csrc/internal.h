@@ -33,6 +33,12 @@ inline int waves_for(int G, int n) {
   return slice <= 64 * w * kBiasPerThread ? w : 0;
 }
 
+// A unit of single-wave bf16 pieces split in exactly kMergeWaves pieces runs as one
+// work-group of kMergeWaves waves, one piece each, which merges them into the unit's
+// output, so that no combine launch follows. Three waves per group keep the
+// three-quarters occupancy of single-wave groups (one wave per SIMD, four per CU).
+constexpr int kMergeWaves = 3;
+
 // Chunked prefill (G n > kMaxRows): heads per wave of the prefill kernel for G query
 // heads per KV head, 0 if not built. Each head costs a wave 48 registers (its 16 rows'
 // O accumulators and queries): 3 heads of a 6-head group and 2 of a 4- or 8-head group
@@ -66,6 +72,7 @@ struct Plan {
   int64_t unit_info_ints;   // even shares: [units][2] (first work-group, pieces)
   int32_t prefill;          // 1: the prefill kernel (many rows per sequence), no combine
   int32_t prefill_hw;       // heads per wave of the prefill kernel
+  int32_t ws;               // pieces per split work-group (kMergeWaves: merged in it)
 };
 
 // Host-side validation of a problem; no HIP call.
@@ -129,7 +136,7 @@ constexpr float kE4M3Max = 448.f;
 
 // Kernel launchers (kernels.hip). Return 0 on success, else a hipError_t value. With a
 // pair of events (hipEvent_t), the launch stamps them with the kernel's start and end.
-int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream,
+int launch_split_kv(const KernelArgs& a, int waves, bool fp8, int ws, void* stream,
                     void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_combine(const KernelArgs& a, void* stream, void* ev_start = nullptr,
                    void* ev_stop = nullptr);

@@ -25,7 +25,8 @@ namespace rattn {
 // ---------------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------------
-// variant index: waves (1, 2, 4), KV format, partition
+// variant index: waves per piece (1, 2, 4), KV format, partition; single-wave pieces
+// also in merging groups of kMergeWaves
 #define RATTN_VARIANTS(X)                                                               \
   X(1, false, false) X(1, true, false) X(2, false, false) X(2, true, false)              \
   X(4, false, false) X(4, true, false) X(1, false, true) X(1, true, true)                \
@@ -52,13 +53,20 @@ static int launch(Kernel kernel, dim3 grid, dim3 block, void* stream, const Args
                                  (hipEvent_t)ev_start, (hipEvent_t)ev_stop, 0);
 }
 
-int launch_split_kv(const KernelArgs& a, int waves, bool fp8, void* stream, void* ev_start,
-                    void* ev_stop) {
+int launch_split_kv(const KernelArgs& a, int waves, bool fp8, int ws, void* stream,
+                    void* ev_start, void* ev_stop) {
   const dim3 grid((unsigned)a.split_groups);
+  if (ws == kMergeWaves) {
+    if (waves != 1 || fp8 || a.splits_per_unit != kMergeWaves) return (int)hipErrorInvalidValue;
+    return launch(split_kv_kernel<1, false, false, kMergeWaves>, grid, dim3(64 * kMergeWaves),
+                  stream, a, ev_start, ev_stop);
+  }
+  if (ws != 1) return (int)hipErrorInvalidValue;
   const int key = variant_key(waves, fp8, a.splits_per_unit == 0);
 #define RATTN_LAUNCH(WRV, F8, EV)                                                    \
   if (key == variant_key(WRV, F8, EV))                                               \
-    return launch(split_kv_kernel<WRV, F8, EV>, grid, dim3(64 * WRV), stream, a, ev_start, ev_stop);
+    return launch(split_kv_kernel<WRV, F8, EV, 1>, grid, dim3(64 * WRV), stream, a, ev_start, \
+                  ev_stop);
   RATTN_VARIANTS(RATTN_LAUNCH)
 #undef RATTN_LAUNCH
   return (int)hipErrorInvalidValue;
@@ -69,7 +77,7 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
   int nb = 0;
 #define RATTN_OCC(WRV, F8, EV)                                                          \
   if (key == variant_key(WRV, F8, EV)) {                                                \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kv_kernel<WRV, F8, EV>, \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kv_kernel<WRV, F8, EV, 1>, \
                                                         64 * WRV, 0) == hipSuccess ? nb : 0; \
   }
   RATTN_VARIANTS(RATTN_OCC)

@@ -48,13 +48,20 @@ namespace rattn {
 // Multi-wave work-groups ask for two waves per SIMD (at most 256 VGPRs each): on the
 // 8-row verify workload that beat one wave per SIMD by 1.4x despite a few spilled
 // registers, since every tile's barrier waits on the slowest of the group's waves.
-template <int WR, bool FP8, bool EVEN>
-__global__ __launch_bounds__(64 * WR)
+//
+// WS > 1 (single-wave pieces, bf16, a unit split into exactly WS pieces): a work-group
+// holds WS waves, each attending a piece of its own exactly as a single-wave work-group
+// would; the waves then merge their pieces through LDS into the unit's output, so that
+// no combine launch follows (see the epilogue).
+template <int WR, bool FP8, bool EVEN, int WS>
+__global__ __launch_bounds__(64 * WR * WS)
 __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
+  static_assert(WS == 1 || (WR == 1 && !FP8 && !EVEN), "merging work-groups: bf16 pieces");
   constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
-  __shared__ __attribute__((aligned(16))) unsigned char klds[TILE_BUFS][kTileKeys * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char vlds[TILE_BUFS][kTileKeys * 256];
-  __shared__ int pages_lds[kChunkPages + 1];
+  // per wave of a merging work-group (WS > 1): its own tile buffer and page ids
+  __shared__ __attribute__((aligned(16))) unsigned char klds[WS * TILE_BUFS][kTileKeys * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[WS * TILE_BUFS][kTileKeys * 256];
+  __shared__ int pages_lds[WS][kChunkPages + 1];
   // E4M3: a tile's 32 K and 32 V scales, staged beside the tile
   __shared__ __attribute__((aligned(16))) float scale_lds[FP8 ? TILE_BUFS : 1][FP8 ? 64 : 1];
   // Several waves load the bias slice of a tile together and share it through LDS; a
@@ -67,6 +74,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
 
   const int lane = threadIdx.x & 63;
   const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  // WS > 1: the wave's piece within the work-group (its LDS buffers)
+  const int wsi = WS == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lr = lane & 15;        // key (A operand) / query row (B operand) within a tile
   const int lq = lane >> 4;        // k-group of the MFMA operands
   const int n = a.n;
@@ -77,7 +86,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   const int64_t Hkv = a.num_kv_heads;
   const int rpw = (R + WR - 1) / WR;
 
-  const int64_t wg = blockIdx.x;
+  const int64_t wg = (int64_t)blockIdx.x * WS + wsi;   // the piece
   const int k_split = a.splits_per_unit;     // used when !EVEN
   int T = 0;
   int64_t P = 0, t_begin = 0, t_end = 0;
@@ -113,6 +122,54 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   const unsigned char* kc = (const unsigned char*)a.k_cache;
   const unsigned char* vc = (const unsigned char*)a.v_cache;
 
+  // ---- merging work-groups (WS > 1): the WS pieces are the whole unit ----
+  // Each wave stages its piece's normalised partial (O / l and lse per row) in its own
+  // LDS tile buffer; the group merges the WS pieces by the log-sum-exp rule and writes
+  // the unit's output rows. Staging layout: row rho at float offset 128 rho, its 4-float
+  // chunk c at slot c ^ (rho & 15) (so that the 16 rows one store instruction writes
+  // fall into distinct banks); the lse of row rho in the wave's V buffer.
+  auto merge_group = [&](int b, int g, float l, float m_run, const f32x4_t (&o)[8]) {
+    if constexpr (WS > 1) {
+      float* st = reinterpret_cast<float*>(klds[wsi]);
+      float* st_lse = reinterpret_cast<float*>(vlds[wsi]);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int c = 4 * dt + lq;                       // dims 4 c .. 4 c + 3
+        *reinterpret_cast<f32x4_t*>(st + 128 * lr + 4 * (c ^ lr)) = o[dt] * inv;
+      }
+      if (lq == 0) st_lse[lr] = l > 0.f ? m_run + __logf(l) : kNegInf;
+      __syncthreads();
+
+      const SeqRows sr = seq_rows(a, b, false);
+      for (int idx = (int)threadIdx.x; idx < R * 32; idx += 64 * WS) {
+        const int rr = idx >> 5, c = idx & 31;           // packed row, 4-dim chunk
+        const int r = rr / G;
+        if (r >= sr.n) continue;                         // a row the sequence lacks
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < WS; ++w)
+          M = fmaxf(M, reinterpret_cast<const float*>(vlds[w])[rr]);
+        float lsum = 0.f;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < WS; ++w) {
+          const float lw = reinterpret_cast<const float*>(vlds[w])[rr];
+          const float wt = lw == kNegInf ? 0.f : __expf(lw - M);   // an empty piece: 0
+          lsum += wt;
+          acc += wt * *reinterpret_cast<const f32x4_t*>(
+                          reinterpret_cast<const float*>(klds[w]) + 128 * rr + 4 * (c ^ (rr & 15)));
+        }
+        const float inv_s = lsum > 0.f ? 1.f / lsum : 0.f;
+        const f32x4_t og = acc * inv_s;
+        const int64_t orow = (int64_t)(sr.base + r) * a.num_q_heads + g * G + (rr - r * G);
+        const u32x2_t wv = {pack_bf16x2(og[0], og[1]), pack_bf16x2(og[2], og[3])};
+        *reinterpret_cast<u32x2_t*>(a.out + orow * kHeadDim + 4 * c) = wv;
+        if (c == 0 && a.lse != nullptr) a.lse[orow] = lsum > 0.f ? M + __logf(lsum) : kNegInf;
+      }
+    }
+  };
+
   for (bool more = true; more;) {
     // ---- the next piece: tiles [tile0, tile1) of unit (b, g) ----
     int b, g, tile0, tile1;
@@ -130,9 +187,10 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       whole = k_split == 1;
       prow0 = wg * R;
       more = false;
-      if (tile1 == tile0) {
+      if (WS == 1 && tile1 == tile0) {
         // fewer tiles than splits: an empty piece marks its rows, which the combine
-        // skips (a sequence without rows has no tiles and nothing to mark)
+        // skips (a sequence without rows has no tiles and nothing to mark); a wave of a
+        // merging work-group attends no tile and merges an empty piece (l = 0)
         if (row_ok && r_of_row < sg.nb) a.part_lse[prow0 + rho] = kNegInf;
         return;
       }
@@ -227,19 +285,19 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       if (WR > 1) __syncthreads();           // the previous chunk's ids and tiles are done
       chunk_p0 = c0 >> a.page_shift;
       const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
-      for (int i = (int)threadIdx.x; i < np; i += 64 * WR) {
+      for (int i = WS > 1 ? lane : (int)threadIdx.x; i < np; i += 64 * WR) {
         int ph = pt_row[chunk_p0 + i];
         if (ph < 0 || ph >= a.num_pages) {
           atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
           ph = min(max(ph, 0), a.num_pages - 1);
         }
-        pages_lds[i] = ph;
+        pages_lds[wsi][i] = ph;
       }
       if (WR > 1) __syncthreads();
     };
     auto phys_at = [&](int jt) -> int {     // physical page of key jt of the current chunk
       const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
-      return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
+      return __builtin_amdgcn_readfirstlane(pages_lds[wsi][idx]);
     };
 
     // Every load of a tile is issued unconditionally, so that the compiler can count the
@@ -313,8 +371,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
       // a single wave reuses one LDS buffer (its LDS accesses execute in order); several
       // waves alternate two, so that one barrier per tile separates writes from reads
-      unsigned char* kl = klds[TILE_BUFS == 2 ? buf : 0];
-      unsigned char* vl = vlds[TILE_BUFS == 2 ? buf : 0];
+      unsigned char* kl = klds[wsi * TILE_BUFS + (TILE_BUFS == 2 ? buf : 0)];
+      unsigned char* vl = vlds[wsi * TILE_BUFS + (TILE_BUFS == 2 ? buf : 0)];
       float* bl = bias_lds[BIAS_BUFS == 2 ? buf : 0];
       if constexpr (STAGE_BIAS) {
         const int tid = wave * 64 + lane;
@@ -503,6 +561,10 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
 
     // ---- epilogue: the final row when the piece is the whole unit, else a partial ----
     const float l = wave_sum_rows(l_run);
+    if constexpr (WS > 1) {
+      merge_group(b, g, l, m_run, o);
+      return;
+    }
     if (row_live) {
       const int64_t row = (int64_t)(row_base + r_of_row) * a.num_q_heads + row_h;
       const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 2
+#define RATTN_ABI_VERSION 3
 
 typedef struct rattn_plan_s* rattn_plan_t;
 
@@ -112,17 +112,20 @@ typedef struct {
 } rattn_problem;
 
 typedef struct {
-  int32_t num_splits;        /* split work-groups per (sequence, KV head), nominal        */
-  int32_t keys_per_split;    /* keys per split work-group at max_seq_len, nominal         */
+  int32_t num_splits;        /* pieces (key ranges) per (sequence, KV head), nominal      */
+  int32_t keys_per_split;    /* keys per piece at max_seq_len, nominal                    */
   int32_t tile_keys;         /* keys per inner-loop step                                  */
-  int32_t row_tiles;         /* waves per work-group (split: one 16-row MFMA tile each;   */
-                             /* prefill: 8)                                               */
+  int32_t row_tiles;         /* waves per piece (split: one 16-row MFMA tile each;        */
+                             /* prefill: 8 per work-group)                                */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (work-groups, 1, 1)             */
-  int32_t combine_blocks;    /* combine work-groups; 0 when the grid is one work-group    */
+  int32_t combine_blocks;    /* combine work-groups; 0 when nothing is merged after the   */
+                             /* split kernel                                              */
   int32_t num_cus;           /* compute units the plan was sized for                      */
   int32_t blocks_per_cu;     /* resident split-kernel work-groups per CU assumed          */
   int32_t kernel;            /* RATTN_KERNEL_*: which kernel the plan launches            */
-  int32_t reserved;          /* 0                                                         */
+  int32_t pieces_per_group;  /* pieces per split work-group, one wave each: 1, or 3 when  */
+                             /* a unit is 3 single-wave pieces, which one work-group    */
+                             /* attends and merges (no combine launch)                   */
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps, and a flag word         */
 } rattn_plan_info;
 

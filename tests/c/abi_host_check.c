@@ -40,9 +40,17 @@ int main(void) {
   check(rattn_abi_version() == RATTN_ABI_VERSION, "ABI version matches the header");
   check(rattn_plan_describe(&p, 256, &info) == RATTN_OK, "headline plans");
   check(info.kernel == RATTN_KERNEL_SPLIT_KV && info.grid_x > 0 && info.row_tiles == 1,
-        "headline uses the split kernel with single-wave groups");
-  check((int64_t)info.grid_x * info.keys_per_split >= (int64_t)8 * 100000,
+        "headline uses the split kernel with single-wave pieces");
+  check(info.pieces_per_group == 1 && info.combine_blocks > 0,
+        "headline splits its units and merges them in the combine");
+  check((int64_t)info.grid_x * info.pieces_per_group * info.keys_per_split >=
+            (int64_t)8 * 100000,
         "the split covers every key of every KV head");
+  p = headline();
+  p.num_splits = 3;
+  check(rattn_plan_describe(&p, 256, &info) == RATTN_OK && info.pieces_per_group == 3 &&
+            info.combine_blocks == 0 && info.grid_x == 8,
+        "three pieces per unit: one work-group per unit merges them");
   p = headline();
   p.n_query_rows = 2048;
   check(rattn_plan_describe(&p, 256, &info) == RATTN_OK && info.kernel == RATTN_KERNEL_PREFILL &&

@@ -86,15 +86,35 @@ def test_null_arguments():
 
 def test_planner_headline_fills_the_chip():
     info = binding.rattn_plan_describe(headline(), 256)
-    assert info.row_tiles == 1                 # 6 packed rows: one wave per work-group
+    assert info.row_tiles == 1                 # 6 packed rows: one wave per piece
     assert info.grid_y == 1 and info.grid_z == 1
     # one round of resident work-groups (4 per CU on gfx950), three quarters full
     assert info.blocks_per_cu == 4
+    assert info.pieces_per_group == 1
     assert info.grid_x == 256 * 4 * 3 // 4, info.grid_x
     units = 8
     assert info.grid_x * info.keys_per_split >= units * 100000
     assert info.keys_per_split % info.tile_keys == 0
     assert info.combine_blocks == 48 * 4   # 4 work-groups per output row
+
+
+def test_planner_merges_three_pieces_in_one_group():
+    # 64q/16kv window layer at batch 16: 256 units of 4 packed rows, three single-wave
+    # pieces each, which one 3-wave work-group per unit attends and merges
+    p = headline(batch=16, num_q_heads=64, num_kv_heads=16, window=512, dmax=512,
+                 max_seq_len=32768, max_pages_per_seq=2048)
+    info = binding.rattn_plan_describe(p, 256)
+    assert info.num_splits == 3 and info.pieces_per_group == 3
+    assert info.grid_x == 16 * 16 and info.combine_blocks == 0
+    # a forced split in three pieces, whatever the shape, for single-wave bf16 pieces
+    for kw in (dict(), dict(batch=3), dict(n_query_rows=2)):
+        info = binding.rattn_plan_describe(headline(num_splits=3, **kw), 256)
+        assert info.pieces_per_group == 3 and info.combine_blocks == 0
+        assert info.grid_x == headline(**kw).batch * 8
+    # not for multi-wave pieces or an E4M3 cache
+    for kw in (dict(n_query_rows=3), dict(kv_dtype=binding.RATTN_KV_FP8_E4M3)):
+        info = binding.rattn_plan_describe(headline(num_splits=3, **kw), 256)
+        assert info.pieces_per_group == 1 and info.combine_blocks > 0
 
 
 def test_planner_covers_every_key():
@@ -111,15 +131,22 @@ def test_planner_covers_every_key():
         tiles = -(-span // 32)
         for cus in (1, 80, 256, 304):
             info = binding.rattn_plan_describe(p, cus)
-            assert info.grid_x * info.keys_per_split >= units * tiles * 32
+            ppg = info.pieces_per_group
+            assert ppg in (1, 3)
+            pieces = info.grid_x * ppg
+            assert pieces * info.keys_per_split >= units * tiles * 32
             if p.num_splits:
-                assert info.grid_x == min(p.num_splits * units, 1 << 16)
+                assert pieces == min(p.num_splits * units, 1 << 16)
             else:
-                assert info.grid_x <= max(units, units * tiles // 4)
+                assert pieces <= max(units, units * tiles // 4)
             assert 1 <= info.grid_x <= 1 << 16
             rows = 6 * p.n_query_rows
             assert info.row_tiles == (1 if rows <= 16 else 2 if rows <= 32 else 4)
-            if info.combine_blocks == 0:
+            assert ppg == (3 if info.num_splits == 3 and rows <= 16 else 1)
+            if ppg == 3:
+                # one work-group per unit merges its three pieces
+                assert info.combine_blocks == 0 and info.grid_x == units
+            elif info.combine_blocks == 0:
                 # nothing to merge: one work-group per (sequence, KV head) unit, or one in all
                 assert info.grid_x in (1, units)
             else:
@@ -135,6 +162,7 @@ def test_combine_shape_follows_the_pieces():
         rows = p.batch * p.n_query_rows * p.num_q_heads
         want = -(-rows // 8) if k <= 16 else rows * 4
         assert info.combine_blocks == want, (k, info.combine_blocks)
+        assert info.pieces_per_group == 1
     window = binding.rattn_plan_describe(
         headline(batch=16, window=1024, max_seq_len=32768, max_pages_per_seq=2048), 256)
     assert 1 < window.num_splits <= 16 and window.combine_blocks == -(-16 * 48 // 8)
