@@ -107,8 +107,10 @@ typedef struct {
   int32_t dmax;              /* largest distance with its own bias column (>= 0)          */
   float softmax_scale;       /* multiplies q . k (1/sqrt(head_dim) for the pages' models) */
   int32_t kv_dtype;          /* rattn_kv_dtype                                            */
-  int32_t num_splits;        /* 0 = planner; > 0 forces num_splits work-groups per        */
-                             /* (sequence, KV head) unit (at most 4096; grid <= 65536)    */
+  int32_t num_splits;        /* 0 = planner; > 0 forces num_splits pieces (key ranges)    */
+                             /* per (sequence, KV head) unit (at most 4096; at most      */
+                             /* 65536 in all); 3 single-wave bf16 pieces run as one      */
+                             /* work-group per unit (rattn_plan_info.pieces_per_group)   */
 } rattn_problem;
 
 typedef struct {
