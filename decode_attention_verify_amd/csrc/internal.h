@@ -33,10 +33,10 @@ inline int waves_for(int G, int n) {
   return slice <= 64 * w * kBiasPerThread ? w : 0;
 }
 
-// A unit of single-wave bf16 pieces split in exactly kMergeWaves pieces runs as one
-// work-group of kMergeWaves waves, one piece each, which merges them into the unit's
-// output, so that no combine launch follows. Three waves per group keep the
-// three-quarters occupancy of single-wave groups (one wave per SIMD, four per CU).
+// A unit of single-wave bf16 pieces split in 2 or kMergeWaves pieces runs as one
+// work-group of that many waves, one piece each, which merges them into the unit's
+// output, so that no combine launch follows (a wave per SIMD: one 3-wave group or two
+// 2-wave groups per CU).
 constexpr int kMergeWaves = 3;
 
 // Chunked prefill (G n > kMaxRows): heads per wave of the prefill kernel for G query
@@ -72,7 +72,7 @@ struct Plan {
   int64_t unit_info_ints;   // even shares: [units][2] (first work-group, pieces)
   int32_t prefill;          // 1: the prefill kernel (many rows per sequence), no combine
   int32_t prefill_hw;       // heads per wave of the prefill kernel
-  int32_t ws;               // pieces per split work-group (kMergeWaves: merged in it)
+  int32_t ws;               // pieces per split work-group (2 or 3: merged in it)
 };
 
 // Host-side validation of a problem; no HIP call.

@@ -56,10 +56,15 @@ static int launch(Kernel kernel, dim3 grid, dim3 block, void* stream, const Args
 int launch_split_kv(const KernelArgs& a, int waves, bool fp8, int ws, void* stream,
                     void* ev_start, void* ev_stop) {
   const dim3 grid((unsigned)a.split_groups);
-  if (ws == kMergeWaves) {
-    if (waves != 1 || fp8 || a.splits_per_unit != kMergeWaves) return (int)hipErrorInvalidValue;
-    return launch(split_kv_kernel<1, false, false, kMergeWaves>, grid, dim3(64 * kMergeWaves),
-                  stream, a, ev_start, ev_stop);
+  if (ws > 1) {
+    if (waves != 1 || fp8 || a.splits_per_unit != ws) return (int)hipErrorInvalidValue;
+    if (ws == 2)
+      return launch(split_kv_kernel<1, false, false, 2>, grid, dim3(128), stream, a, ev_start,
+                    ev_stop);
+    if (ws == 3)
+      return launch(split_kv_kernel<1, false, false, 3>, grid, dim3(192), stream, a, ev_start,
+                    ev_stop);
+    return (int)hipErrorInvalidValue;
   }
   if (ws != 1) return (int)hipErrorInvalidValue;
   const int key = variant_key(waves, fp8, a.splits_per_unit == 0);

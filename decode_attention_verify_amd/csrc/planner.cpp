@@ -142,15 +142,31 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
     groups = std::min<int64_t>(target, std::max<int64_t>(1, total / 4));
     groups = std::max<int64_t>(1, std::min<int64_t>(groups, kMaxGroups));
   }
-  // a unit of single-wave bf16 pieces split in exactly kMergeWaves pieces: one
-  // work-group of kMergeWaves waves per unit, which merges the pieces itself (on
-  // the 64q/16kv window layer at batch 16, 256 units of 3 pieces: 15.9 us against 19.5
-  // with three single-wave groups and the combine; at 6 pieces per unit the combine
-  // stays faster: 48q/8kv window layer, batch 16, 19.6 us against 20.6-21.0 at 3 merged)
+  // Units of single-wave bf16 pieces that would get at most kMergeWaves pieces each run
+  // as one work-group of w waves per unit, w pieces merged by the group itself, with no
+  // partials and no combine: w = 3 where a group fits on every unit's own CU (units <=
+  // CUs), w = 2 where two groups share a CU (units <= 2 CUs), pieces of 4 tiles or more.
+  // On MI355X: the 64q/16kv window layer at batch 16 (256 units, 3 merged pieces)
+  // 15.9 us against 19.5 with three single-wave groups and the combine; the 48q/8kv
+  // window layer at batch 64 (512 units) 45.4-45.8 us in 2 merged pieces against
+  // 49-51 whole (two waves per CU) and 51.7 in 2 pieces with the combine. At 6 pieces
+  // per unit the combine stays faster (48q/8kv window layer, batch 16: 19.6 us against
+  // 20.6-21.0 at 3 merged). A forced split of 2 or 3 pieces merges the same way.
   pl.ws = 1;
-  if (pl.waves == 1 && p.kv_dtype == RATTN_KV_BF16 && k == kMergeWaves) {
-    pl.ws = kMergeWaves;
-    groups = units;
+  if (pl.waves == 1 && p.kv_dtype == RATTN_KV_BF16 && k >= 1) {   // per-unit splits
+    int64_t w = 1;
+    if (p.num_splits > 0) {
+      w = (k == 2 || k == kMergeWaves) ? k : 1;
+    } else if (k <= kMergeWaves) {
+      const int64_t cus = std::max(num_cus, 1);
+      if (units <= cus && tiles / 4 >= 3) w = 3;
+      else if (units <= 2 * cus && tiles / 4 >= 2) w = 2;
+    }
+    if (w > 1) {
+      k = w;
+      pl.ws = (int32_t)w;
+      groups = units;
+    }
   }
   pl.split_groups = (int32_t)groups;
   pl.splits_per_unit = (int32_t)k;

@@ -109,7 +109,7 @@ typedef struct {
   int32_t kv_dtype;          /* rattn_kv_dtype                                            */
   int32_t num_splits;        /* 0 = planner; > 0 forces num_splits pieces (key ranges)    */
                              /* per (sequence, KV head) unit (at most 4096; at most      */
-                             /* 65536 in all); 3 single-wave bf16 pieces run as one      */
+                             /* 65536 in all); 2 or 3 single-wave bf16 pieces run as one */
                              /* work-group per unit (rattn_plan_info.pieces_per_group)   */
 } rattn_problem;
 
@@ -125,9 +125,9 @@ typedef struct {
   int32_t num_cus;           /* compute units the plan was sized for                      */
   int32_t blocks_per_cu;     /* resident split-kernel work-groups per CU assumed          */
   int32_t kernel;            /* RATTN_KERNEL_*: which kernel the plan launches            */
-  int32_t pieces_per_group;  /* pieces per split work-group, one wave each: 1, or 3 when  */
-                             /* a unit is 3 single-wave pieces, which one work-group    */
-                             /* attends and merges (no combine launch)                   */
+  int32_t pieces_per_group;  /* pieces per split work-group, one wave each: 1, or 2 or 3  */
+                             /* when a unit is that many single-wave pieces, which one   */
+                             /* work-group attends and merges (no combine launch)        */
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps, and a flag word         */
 } rattn_plan_info;
 

@@ -106,11 +106,20 @@ def test_planner_merges_three_pieces_in_one_group():
     info = binding.rattn_plan_describe(p, 256)
     assert info.num_splits == 3 and info.pieces_per_group == 3
     assert info.grid_x == 16 * 16 and info.combine_blocks == 0
-    # a forced split in three pieces, whatever the shape, for single-wave bf16 pieces
-    for kw in (dict(), dict(batch=3), dict(n_query_rows=2)):
-        info = binding.rattn_plan_describe(headline(num_splits=3, **kw), 256)
-        assert info.pieces_per_group == 3 and info.combine_blocks == 0
-        assert info.grid_x == headline(**kw).batch * 8
+    # 48q/8kv window layer at batch 64: 512 units, two merged pieces each (two 2-wave
+    # work-groups per CU)
+    p = headline(batch=64, window=1024, max_seq_len=32768, max_pages_per_seq=2048)
+    info = binding.rattn_plan_describe(p, 256)
+    assert info.num_splits == 2 and info.pieces_per_group == 2
+    assert info.grid_x == 512 and info.combine_blocks == 0
+    # twice the CUs' units or more: whole units, one wave each
+    assert binding.rattn_plan_describe(p, 255).pieces_per_group == 1
+    # a forced split in two or three pieces, whatever the shape, for single-wave bf16
+    for k in (2, 3):
+        for kw in (dict(), dict(batch=3), dict(n_query_rows=2)):
+            info = binding.rattn_plan_describe(headline(num_splits=k, **kw), 256)
+            assert info.pieces_per_group == k and info.combine_blocks == 0
+            assert info.grid_x == headline(**kw).batch * 8
     # not for multi-wave pieces or an E4M3 cache
     for kw in (dict(n_query_rows=3), dict(kv_dtype=binding.RATTN_KV_FP8_E4M3)):
         info = binding.rattn_plan_describe(headline(num_splits=3, **kw), 256)
@@ -132,7 +141,7 @@ def test_planner_covers_every_key():
         for cus in (1, 80, 256, 304):
             info = binding.rattn_plan_describe(p, cus)
             ppg = info.pieces_per_group
-            assert ppg in (1, 3)
+            assert ppg in (1, 2, 3)
             pieces = info.grid_x * ppg
             assert pieces * info.keys_per_split >= units * tiles * 32
             if p.num_splits:
@@ -142,10 +151,13 @@ def test_planner_covers_every_key():
             assert 1 <= info.grid_x <= 1 << 16
             rows = 6 * p.n_query_rows
             assert info.row_tiles == (1 if rows <= 16 else 2 if rows <= 32 else 4)
-            assert ppg == (3 if info.num_splits == 3 and rows <= 16 else 1)
-            if ppg == 3:
-                # one work-group per unit merges its three pieces
+            if p.num_splits:
+                assert ppg == (p.num_splits if p.num_splits in (2, 3) and rows <= 16 else 1)
+            assert ppg in (1, 2, 3) and (ppg == 1 or ppg == info.num_splits)
+            if ppg > 1:
+                # one work-group per unit merges its pieces
                 assert info.combine_blocks == 0 and info.grid_x == units
+                assert rows <= 16 and units <= (cus if ppg == 3 else 2 * cus) or p.num_splits
             elif info.combine_blocks == 0:
                 # nothing to merge: one work-group per (sequence, KV head) unit, or one in all
                 assert info.grid_x in (1, units)
@@ -156,7 +168,7 @@ def test_planner_covers_every_key():
 def test_combine_shape_follows_the_pieces():
     # per-unit splits of up to 16 pieces merge whole rows, 8 per work-group; otherwise
     # 4 work-groups per output row (32 dims each)
-    for k in (2, 7, 16, 17, 64, 255, 256, 4096):
+    for k in (4, 7, 16, 17, 64, 255, 256, 4096):
         p = headline(num_splits=k)
         info = binding.rattn_plan_describe(p, 256)
         rows = p.batch * p.n_query_rows * p.num_q_heads

@@ -159,19 +159,21 @@ def test_full_context_unaligned_lengths(L):
     check_case(small("full_100k", seq_len=L), seed=0, gen_device="cuda", kv_heads=[2, 5])
 
 
+@pytest.mark.parametrize("k", [2, 3])
 @pytest.mark.parametrize("n,seq_len", [(1, ("uniform", 1, 300)), (2, ("uniform", 2, 2500)),
                                        (1, 4099)])
-def test_three_pieces_merged_in_one_group(n, seq_len):
-    # a unit split in exactly three single-wave pieces runs as one 3-wave work-group that
-    # merges them (no combine launch); short sequences leave pieces without keys
+def test_pieces_merged_in_one_group(k, n, seq_len):
+    # a unit split in 2 or 3 single-wave pieces runs as one work-group of as many waves,
+    # which merges them (no combine launch); short sequences leave pieces without keys
     sp = small("full_100k", batch=5, n_rows=n, seq_len=seq_len, dmax=5000, bias_decay=0.0,
-               name="merge3")
-    check_case(sp, seed=60 + n, num_splits=3)
+               name="merge%d" % k)
+    check_case(sp, seed=60 + 10 * k + n, num_splits=k)
 
 
-def test_three_pieces_merged_window():
-    sp = small("window_b16", batch=4, n_rows=1, name="merge3_window")
-    check_case(sp, seed=63, num_splits=3)
+@pytest.mark.parametrize("k", [2, 3])
+def test_pieces_merged_window(k):
+    sp = small("window_b16", batch=4, n_rows=1, name="merge%d_window" % k)
+    check_case(sp, seed=63 + k, num_splits=k)
 
 
 def test_window_fp8():
