@@ -115,8 +115,12 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   // groups (the 8-row verify workload: 2.57 ms at a full round against 3.30 ms at three
   // quarters) and the E4M3 cache, which decodes every element (the 1M-key decode:
   // 529 us against 542 us).
-  // No work-group gets fewer than 4 tiles (128 keys): every piece of a shared unit costs
-  // a partial and a merge. Units of multi-wave groups stay whole when they alone give
+  // Per-unit splits go down to one tile per piece when the units are too few to fill the
+  // round otherwise: the pieces of a latency-bound call end sooner than fewer, longer
+  // ones, partial and merge included (2K-key decode on 6q/1kv: 64 one-tile pieces
+  // 11.0 us, 16 pieces of 4 tiles 13.5; the window layer at batch 1, 8 units: 32 pieces
+  // per unit 12.8 us, 8 pieces 15.7). Even shares keep at least 4 tiles per work-group.
+  // Units of multi-wave groups stay whole when they alone give
   // every CU four waves: then splitting buys little and the merge of their many rows
   // costs more (9-row verify over W = 512 on 64q/16kv, 256 units: 26.6 us whole against
   // 30.7 us in two pieces, 7 us of it the merge; the 8-row verify over W = 1024 on
@@ -132,7 +136,7 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   } else if (!uses_even_shares(p)) {
     // every unit spans about the same keys (a window, or a single sequence): an equal
     // number of pieces per unit is balanced and needs no search for a work-group's unit
-    k = std::max<int64_t>(1, std::min<int64_t>(target / units, tiles / 4));
+    k = std::max<int64_t>(1, std::min<int64_t>(target / units, tiles));
     if (pl.waves > 1 && units * pl.waves >= 4 * (int64_t)std::max(num_cus, 1)) k = 1;
     k = std::min<int64_t>(k, std::max<int64_t>(1, kMaxGroups / units));
     groups = k * units;

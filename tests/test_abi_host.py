@@ -147,7 +147,7 @@ def test_planner_covers_every_key():
             if p.num_splits:
                 assert pieces == min(p.num_splits * units, 1 << 16)
             else:
-                assert pieces <= max(units, units * tiles // 4)
+                assert pieces <= max(units, units * tiles)
             assert 1 <= info.grid_x <= 1 << 16
             rows = 6 * p.n_query_rows
             assert info.row_tiles == (1 if rows <= 16 else 2 if rows <= 32 else 4)
