@@ -98,6 +98,22 @@ def test_planner_headline_fills_the_chip():
     assert info.combine_blocks == 48 * 4   # 4 work-groups per output row
 
 
+def test_planner_one_tile_pieces_when_units_are_few():
+    # 2048 keys on one 6q/1kv unit: 65 tiles, each its own piece (the round of 768 pieces
+    # is far from full); 8 window units of 1024 + 31 keys: 33 one-tile pieces each
+    tiny = headline(num_q_heads=6, num_kv_heads=1, max_seq_len=2048, max_pages_per_seq=128,
+                    dmax=2047)
+    info = binding.rattn_plan_describe(tiny, 256)
+    assert info.num_splits == 65 and info.grid_x == 65 and info.combine_blocks > 0
+    window = headline(window=1024, max_seq_len=32768, max_pages_per_seq=2048)
+    info = binding.rattn_plan_describe(window, 256)
+    assert info.num_splits == 33 and info.grid_x == 8 * 33
+    # where the round binds, the pieces stay longer: 16 window sequences, 6 pieces each
+    info = binding.rattn_plan_describe(
+        headline(batch=16, window=1024, max_seq_len=32768, max_pages_per_seq=2048), 256)
+    assert info.num_splits == 6 and info.keys_per_split >= 4 * info.tile_keys
+
+
 def test_planner_merges_three_pieces_in_one_group():
     # 64q/16kv window layer at batch 16: 256 units of 4 packed rows, three single-wave
     # pieces each, which one 3-wave work-group per unit attends and merges
