@@ -231,7 +231,11 @@ void prefill_kernel(KernelArgs a) {
     const float* bl = bias_lds[buf];
     if (!FAST && (!wave_live || j0 > wave_last_p)) return;   // every key after every row
 
-    // S^T = K Q^T for the HW heads; each K fragment feeds all of them
+    // S^T = K Q^T for the HW heads; each K fragment feeds all of them. The matrix
+    // instructions run at a raised wave priority, so that the SIMD's other wave, in its
+    // exponentials, yields the issue slot to them (the chunked prefill at 100K: 46.5 ms
+    // against 46.9)
+    __builtin_amdgcn_s_setprio(1);
     f32x4_t sacc[HW][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -250,6 +254,7 @@ void prefill_kernel(KernelArgs a) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // logits (with masks on the tiles that need them) of head i, key (kt, c)
     // logits in base 2 (scaled by log2 e): the exponentials need no multiply
     auto logit = [&](int i, int kt, int c) {
@@ -325,9 +330,11 @@ void prefill_kernel(KernelArgs a) {
       const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
                           pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
       const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pk);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, o[i][dt], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
