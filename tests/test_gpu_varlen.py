@@ -91,13 +91,14 @@ def test_rows_and_splits(rows, splits):
     check_varlen(sp, rows, seed=sum(rows) + splits, num_splits=splits)
 
 
+@pytest.mark.parametrize("k", [2, 3])
 @pytest.mark.parametrize("rows", [[1, 2, 0, 2, 1], [0, 0, 2, 0, 0]])
-def test_rows_of_three_merged_pieces(rows):
-    # up to 2 rows of 6 heads: single-wave pieces; three per unit run as one work-group
+def test_rows_of_merged_pieces(rows, k):
+    # up to 2 rows of 6 heads: single-wave pieces; 2 or 3 per unit run as one work-group
     # that merges them, over sequences without rows and pieces without keys
     sp = small("full_100k", batch=5, n_rows=2, seq_len=("uniform", 2, 150), dmax=400,
-               name="varlen_merge3")
-    check_varlen(sp, rows, seed=sum(rows) + 30, num_splits=3)
+               name="varlen_merge%d" % k)
+    check_varlen(sp, rows, seed=sum(rows) + 30 + k, num_splits=k)
 
 
 def test_no_rows_at_all():
