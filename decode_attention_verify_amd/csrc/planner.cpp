@@ -5,8 +5,10 @@
 // chosen from the batch size, the head count and the KV length. Here the planner picks
 // the number of split work-groups from (batch * KV heads, visible KV span, compute
 // units, resident work-groups per CU): the kernel divides the whole call's tiles evenly
-// among them, so the choice sets occupancy, and no work-group gets fewer than a few
-// tiles, because every piece of a shared unit costs a partial write and a combine read.
+// among them, so the choice sets occupancy. Pieces stay long where the round of
+// resident work-groups is full (every piece of a shared unit costs a partial write and
+// a combine read) and go down to one tile where the units are too few to fill it; units
+// of two or three single-wave pieces are merged by one work-group with no combine.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
