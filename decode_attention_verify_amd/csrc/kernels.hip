@@ -93,7 +93,9 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
 // The combine's shape for a partition (see combine_kernel): per-unit splits of up to 16
 // pieces take whole rows, 8 per work-group; even shares (a few to a few tens of pieces
 // per unit) whole rows with 2 stripes, 4 per work-group; per-unit splits of 256 pieces
-// or more 16 waves per 32-dim slice; the rest one wave per 16-dim slice (16 stripes of
+// or more 16 waves per 16-dim slice (256 stripes of 4 lanes: one rank's share of the
+// 100K-key layer under 8-way tensor parallelism, 768 pieces, 0.4 us sooner than 16 waves
+// per 32-dim slice, under 4-way 0.7 us); the rest one wave per 16-dim slice (16 stripes of
 // 4 lanes: on MI355X the 100K-key decode's 96 pieces merge 0.4 us sooner than with one
 // wave per 32-dim slice of 8 stripes, and 0.7 us sooner at 65 pieces; 32 stripes per
 // 8-dim slice were no faster and 64 per 4-dim slice slower).
@@ -110,8 +112,7 @@ int64_t combine_blocks(int64_t rows, int splits_per_unit) {
   switch (combine_shape(splits_per_unit)) {
     case kCombineRows: return (rows + 7) / 8;
     case kCombineRows2: return (rows + 3) / 4;
-    case kCombineSlices: return rows * 8;
-    default: return rows * 4;
+    default: return rows * 8;   // one work-group per 16-dim slice of a row
   }
 }
 
@@ -124,7 +125,7 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_s
     case kCombineRows2:
       return launch(combine_kernel<32, 2, 4, 16>, grid, dim3(256), stream, a, ev_start, ev_stop);
     case kCombineWide:
-      return launch(combine_kernel<8, 128, 1, 8>, grid, dim3(1024), stream, a, ev_start, ev_stop);
+      return launch(combine_kernel<4, 256, 1, 4>, grid, dim3(1024), stream, a, ev_start, ev_stop);
     default:
       return launch(combine_kernel<4, 16, 1, 8>, grid, dim3(64), stream, a, ev_start, ev_stop);
   }

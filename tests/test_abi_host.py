@@ -182,13 +182,13 @@ def test_planner_covers_every_key():
 
 
 def test_combine_shape_follows_the_pieces():
-    # per-unit splits of up to 16 pieces merge whole rows, 8 per work-group; up to 255
-    # pieces 8 work-groups per output row (16 dims each); more, 4 (32 dims each)
+    # per-unit splits of up to 16 pieces merge whole rows, 8 per work-group; more, 8
+    # work-groups per output row (16 dims each)
     for k in (4, 7, 16, 17, 64, 255, 256, 4096):
         p = headline(num_splits=k)
         info = binding.rattn_plan_describe(p, 256)
         rows = p.batch * p.n_query_rows * p.num_q_heads
-        want = -(-rows // 8) if k <= 16 else rows * 8 if k < 256 else rows * 4
+        want = -(-rows // 8) if k <= 16 else rows * 8
         assert info.combine_blocks == want, (k, info.combine_blocks)
         assert info.pieces_per_group == 1
     window = binding.rattn_plan_describe(
