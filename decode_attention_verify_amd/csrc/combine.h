@@ -20,7 +20,7 @@ namespace rattn {
 // pieces arrive in one memory round trip; the stripes are
 // then merged by the same rule, with lane shuffles inside a wave and through LDS
 // across the waves of a row. The shape follows the number of pieces:
-//   * few pieces per unit: 32 lanes (1 stripe) or 64 (2 stripes) cover a whole row;
+//   * few pieces per unit: 64 lanes (2 stripes of 32) cover a whole row;
 //   * tens of pieces: 16 stripes x 4 lanes per 16-dim slice of a row, one wave each;
 //   * hundreds of pieces: 256 stripes x 4 lanes per 16-dim slice, 16 waves (4 pieces in
 //     flight per thread, within the 128 registers of a 1024-thread work-group).

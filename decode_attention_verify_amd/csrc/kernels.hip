@@ -91,8 +91,10 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
 }
 
 // The combine's shape for a partition (see combine_kernel): per-unit splits of up to 16
-// pieces take whole rows, 8 per work-group; even shares (a few to a few tens of pieces
-// per unit) whole rows with 2 stripes, 4 per work-group; per-unit splits of 256 pieces
+// pieces take whole rows with 2 stripes, 4 per work-group, 8 pieces in flight per thread
+// (the window layer at batch 16, 6 pieces per unit: 18.2 us per call against 19.3 with
+// one stripe and 8 rows per work-group); even shares (a few to a few tens of pieces per
+// unit) the same with 16 pieces in flight per thread; per-unit splits of 256 pieces
 // or more 16 waves per 16-dim slice (256 stripes of 4 lanes: one rank's share of the
 // 100K-key layer under 8-way tensor parallelism, 768 pieces, 0.4 us sooner than 16 waves
 // per 32-dim slice, under 4-way 0.7 us); the rest one wave per 16-dim slice (16 stripes of
@@ -110,7 +112,7 @@ static CombineShape combine_shape(int splits_per_unit) {
 
 int64_t combine_blocks(int64_t rows, int splits_per_unit) {
   switch (combine_shape(splits_per_unit)) {
-    case kCombineRows: return (rows + 7) / 8;
+    case kCombineRows:
     case kCombineRows2: return (rows + 3) / 4;
     default: return rows * 8;   // one work-group per 16-dim slice of a row
   }
@@ -121,7 +123,7 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_s
   const dim3 grid((unsigned)combine_blocks(rows, a.splits_per_unit));
   switch (combine_shape(a.splits_per_unit)) {
     case kCombineRows:
-      return launch(combine_kernel<32, 1, 8, 16>, grid, dim3(256), stream, a, ev_start, ev_stop);
+      return launch(combine_kernel<32, 2, 4, 8>, grid, dim3(256), stream, a, ev_start, ev_stop);
     case kCombineRows2:
       return launch(combine_kernel<32, 2, 4, 16>, grid, dim3(256), stream, a, ev_start, ev_stop);
     case kCombineWide:

@@ -182,18 +182,18 @@ def test_planner_covers_every_key():
 
 
 def test_combine_shape_follows_the_pieces():
-    # per-unit splits of up to 16 pieces merge whole rows, 8 per work-group; more, 8
+    # per-unit splits of up to 16 pieces merge whole rows, 4 per work-group; more, 8
     # work-groups per output row (16 dims each)
     for k in (4, 7, 16, 17, 64, 255, 256, 4096):
         p = headline(num_splits=k)
         info = binding.rattn_plan_describe(p, 256)
         rows = p.batch * p.n_query_rows * p.num_q_heads
-        want = -(-rows // 8) if k <= 16 else rows * 8
+        want = -(-rows // 4) if k <= 16 else rows * 8
         assert info.combine_blocks == want, (k, info.combine_blocks)
         assert info.pieces_per_group == 1
     window = binding.rattn_plan_describe(
         headline(batch=16, window=1024, max_seq_len=32768, max_pages_per_seq=2048), 256)
-    assert 1 < window.num_splits <= 16 and window.combine_blocks == -(-16 * 48 // 8)
+    assert 1 < window.num_splits <= 16 and window.combine_blocks == -(-16 * 48 // 4)
     # even shares of a full-context batch: whole rows, 4 per work-group
     verify = binding.rattn_plan_describe(
         headline(batch=16, n_query_rows=8, max_seq_len=262144, max_pages_per_seq=16384,
