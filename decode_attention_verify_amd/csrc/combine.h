@@ -22,8 +22,9 @@ namespace rattn {
 // across the waves of a row. The shape follows the number of pieces:
 //   * few pieces per unit: 64 lanes (2 stripes of 32) cover a whole row;
 //   * tens of pieces: 16 stripes x 4 lanes per 16-dim slice of a row, one wave each;
-//   * hundreds of pieces: 256 stripes x 4 lanes per 16-dim slice, 16 waves (4 pieces in
-//     flight per thread, within the 128 registers of a 1024-thread work-group).
+//   * hundreds of pieces: 128 stripes x 8 lanes per 32-dim slice (or, for few rows,
+//     256 x 4 per 16-dim slice), 16 waves (8 or 4 pieces in flight per thread, within
+//     the 128 registers of a 1024-thread work-group).
 // A unit held whole by one work-group was written by the split kernel and is left
 // alone; a row that its sequence does not have is skipped.
 // ---------------------------------------------------------------------------------

@@ -95,38 +95,44 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
 // (the window layer at batch 16, 6 pieces per unit: 18.2 us per call against 19.3 with
 // one stripe and 8 rows per work-group); even shares (a few to a few tens of pieces per
 // unit) the same with 16 pieces in flight per thread; per-unit splits of 256 pieces
-// or more 16 waves per 16-dim slice (256 stripes of 4 lanes: one rank's share of the
-// 100K-key layer under 8-way tensor parallelism, 768 pieces, 0.4 us sooner than 16 waves
-// per 32-dim slice, under 4-way 0.7 us); the rest one wave per 16-dim slice (16 stripes of
+// or more 16 waves per 32-dim slice (128 stripes of 8 lanes), or, below 32 rows, per
+// 16-dim slice (256 stripes of 4 lanes), so that the few rows still spread over enough
+// work-groups (one rank's share of the 100K-key layer under 8-way tensor parallelism, 6
+// rows of 768 pieces: 0.4 us sooner, under 4-way 0.7 us; the 1M-key E4M3 decode, 48
+// rows of 256 pieces, merges 1.2 us later in 16-dim slices); the rest one wave per
+// 16-dim slice (16 stripes of
 // 4 lanes: on MI355X the 100K-key decode's 96 pieces merge 0.4 us sooner than with one
 // wave per 32-dim slice of 8 stripes, and 0.7 us sooner at 65 pieces; 32 stripes per
 // 8-dim slice were no faster and 64 per 4-dim slice slower).
-enum CombineShape { kCombineRows, kCombineRows2, kCombineSlices, kCombineWide };
+enum CombineShape { kCombineRows, kCombineRows2, kCombineSlices, kCombineWide, kCombineWide16 };
 
-static CombineShape combine_shape(int splits_per_unit) {
+static CombineShape combine_shape(int64_t rows, int splits_per_unit) {
   if (splits_per_unit == 0) return kCombineRows2;
   if (splits_per_unit <= 16) return kCombineRows;
-  if (splits_per_unit >= 256) return kCombineWide;
+  if (splits_per_unit >= 256) return rows < 32 ? kCombineWide16 : kCombineWide;
   return kCombineSlices;
 }
 
 int64_t combine_blocks(int64_t rows, int splits_per_unit) {
-  switch (combine_shape(splits_per_unit)) {
+  switch (combine_shape(rows, splits_per_unit)) {
     case kCombineRows:
     case kCombineRows2: return (rows + 3) / 4;
-    default: return rows * 8;   // one work-group per 16-dim slice of a row
+    case kCombineWide: return rows * 4;   // one work-group per 32-dim slice of a row
+    default: return rows * 8;             // one work-group per 16-dim slice of a row
   }
 }
 
 int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_stop) {
   const int64_t rows = (int64_t)a.batch * a.n * a.num_q_heads;
   const dim3 grid((unsigned)combine_blocks(rows, a.splits_per_unit));
-  switch (combine_shape(a.splits_per_unit)) {
+  switch (combine_shape(rows, a.splits_per_unit)) {
     case kCombineRows:
       return launch(combine_kernel<32, 2, 4, 8>, grid, dim3(256), stream, a, ev_start, ev_stop);
     case kCombineRows2:
       return launch(combine_kernel<32, 2, 4, 16>, grid, dim3(256), stream, a, ev_start, ev_stop);
     case kCombineWide:
+      return launch(combine_kernel<8, 128, 1, 8>, grid, dim3(1024), stream, a, ev_start, ev_stop);
+    case kCombineWide16:
       return launch(combine_kernel<4, 256, 1, 4>, grid, dim3(1024), stream, a, ev_start, ev_stop);
     default:
       return launch(combine_kernel<4, 16, 1, 8>, grid, dim3(64), stream, a, ev_start, ev_stop);

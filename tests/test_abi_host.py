@@ -183,14 +183,18 @@ def test_planner_covers_every_key():
 
 def test_combine_shape_follows_the_pieces():
     # per-unit splits of up to 16 pieces merge whole rows, 4 per work-group; more, 8
-    # work-groups per output row (16 dims each)
+    # work-groups per output row (16 dims each); 256 or more over 48 rows, 4 (32 dims)
     for k in (4, 7, 16, 17, 64, 255, 256, 4096):
         p = headline(num_splits=k)
         info = binding.rattn_plan_describe(p, 256)
         rows = p.batch * p.n_query_rows * p.num_q_heads
-        want = -(-rows // 4) if k <= 16 else rows * 8
+        want = -(-rows // 4) if k <= 16 else rows * 8 if k < 256 else rows * 4
         assert info.combine_blocks == want, (k, info.combine_blocks)
         assert info.pieces_per_group == 1
+    # hundreds of pieces over few rows (one rank's share under 8-way tensor parallelism):
+    # 16-dim slices
+    tp8 = binding.rattn_plan_describe(headline(num_q_heads=6, num_kv_heads=1, num_splits=768), 256)
+    assert tp8.num_splits == 768 and tp8.combine_blocks == 6 * 8
     window = binding.rattn_plan_describe(
         headline(batch=16, window=1024, max_seq_len=32768, max_pages_per_seq=2048), 256)
     assert 1 < window.num_splits <= 16 and window.combine_blocks == -(-16 * 48 // 4)
