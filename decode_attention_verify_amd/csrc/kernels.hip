@@ -90,20 +90,20 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
   return 0;
 }
 
-// The combine's shape for a partition (see combine_kernel): per-unit splits of up to 16
-// pieces take whole rows with 2 stripes, 4 per work-group, 8 pieces in flight per thread
-// (the window layer at batch 16, 6 pieces per unit: 18.2 us per call against 19.3 with
-// one stripe and 8 rows per work-group); even shares (a few to a few tens of pieces per
-// unit) the same with 16 pieces in flight per thread; per-unit splits of 256 pieces
-// or more 16 waves per 32-dim slice (128 stripes of 8 lanes), or, below 32 rows, per
-// 16-dim slice (256 stripes of 4 lanes), so that the few rows still spread over enough
-// work-groups (one rank's share of the 100K-key layer under 8-way tensor parallelism, 6
-// rows of 768 pieces: 0.4 us sooner, under 4-way 0.7 us; the 1M-key E4M3 decode, 48
-// rows of 256 pieces, merges 1.2 us later in 16-dim slices); the rest one wave per
-// 16-dim slice (16 stripes of
-// 4 lanes: on MI355X the 100K-key decode's 96 pieces merge 0.4 us sooner than with one
-// wave per 32-dim slice of 8 stripes, and 0.7 us sooner at 65 pieces; 32 stripes per
-// 8-dim slice were no faster and 64 per 4-dim slice slower).
+// The combine's shape for a partition (see combine_kernel), with what chose it on MI355X:
+//  * per-unit splits of up to 16 pieces: whole rows, 2 stripes of 32 lanes, 4 rows per
+//    work-group, 8 pieces in flight per thread (the window layer at batch 16, 6 pieces
+//    per unit: 18.2 us per call against 19.3 with 1 stripe and 8 rows per work-group);
+//  * even shares (a few to a few tens of pieces per unit): the same, 16 pieces in flight;
+//  * 17 to 255 pieces: one wave per 16-dim slice of a row, 16 stripes of 4 lanes (the
+//    100K-key decode's 96 pieces merge 0.4 us sooner than in 32-dim slices of 8 stripes,
+//    65 pieces 0.7 us sooner; 32 stripes per 8-dim slice were no faster, 64 per 4-dim
+//    slice slower);
+//  * 256 pieces or more: 16 waves per 32-dim slice, 128 stripes of 8 lanes; for a call of
+//    fewer than 32 rows, per 16-dim slice, 256 stripes of 4 lanes, so that the few rows
+//    spread over twice the work-groups (one rank's share of the 100K-key layer under
+//    8-way tensor parallelism, 6 rows of 768 pieces: 0.4 us sooner, under 4-way 0.7 us;
+//    the 1M-key E4M3 decode, 48 rows of 256 pieces, merged 1.2 us later that way).
 enum CombineShape { kCombineRows, kCombineRows2, kCombineSlices, kCombineWide, kCombineWide16 };
 
 static CombineShape combine_shape(int64_t rows, int splits_per_unit) {
