@@ -176,6 +176,15 @@ def test_pieces_merged_window(k):
     check_case(sp, seed=63 + k, num_splits=k)
 
 
+@pytest.mark.parametrize("splits,seq_len", [(300, 5000), (1000, 5000), (256, 20000)])
+def test_many_pieces_few_rows(splits, seq_len):
+    # hundreds of pieces over fewer than 32 rows: the combine's 16-dim slices of 256
+    # stripes; at 5,000 keys (157 tiles) most pieces hold no key and are skipped
+    sp = small("tiny", batch=2, n_rows=2, seq_len=seq_len, dmax=seq_len + 10,
+               permute_pages=True, name="wide16")
+    check_case(sp, seed=splits, num_splits=splits)
+
+
 def test_window_fp8():
     sp = small("window_b16", batch=4, n_rows=8, kv_format=synth.KV_FP8, page_size=64,
                name="window_fp8")
