@@ -29,7 +29,7 @@ the problem statement, not by the pages: parity unpinned by the pages for those 
 """
 
 from .formats import bf16_bits_to_f64, e4m3fn_codes_to_f64
-from .attention import relative_attention, partial_attention, visible_keys
+from .attention import relative_attention, partial_attention
 from .combine import combine_partials
 from .bruteforce import bruteforce_attention
 from .append import append_kv, e4m3fn_encode, quantise_rows_e4m3
@@ -40,7 +40,6 @@ __all__ = [
     "e4m3fn_codes_to_f64",
     "relative_attention",
     "partial_attention",
-    "visible_keys",
     "combine_partials",
     "bruteforce_attention",
     "append_kv",

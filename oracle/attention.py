@@ -32,13 +32,6 @@ import numpy as np
 from .formats import bf16_bits_to_f64, e4m3fn_codes_to_f64
 
 
-def visible_keys(seq_len, n_rows, row, window):
-    """Return the keys j visible to query row ``row`` as an int64 array."""
-    p = seq_len - n_rows + row
-    lo = 0 if window == 0 else max(0, p - window + 1)
-    return np.arange(lo, p + 1, dtype=np.int64)
-
-
 def _decode(values):
     values = np.asarray(values)
     if values.dtype == np.uint16:

@@ -64,6 +64,13 @@ MUTANTS = [
     ("append.py", "slot = t % S", "slot = (t + 1) % S"),                          # slot
     ("append.py", "np.float32(-E4M3_MAX), np.float32(E4M3_MAX))",
      "np.float32(-E4M3_MAX), np.float32(E4M3_MAX) * 0 + np.float32(400))"),  # clamp
+    ("append.py", "y = (x / scale[..., None]).astype(np.float32)",
+     "y = (x * (np.float32(1) / scale[..., None])).astype(np.float32)"),  # reciprocal
+    ("append.py", "y = (x / scale[..., None]).astype(np.float32)",
+     "y = x.astype(np.float64) / np.where(amax > 0, amax.astype(np.float64) / E4M3_MAX,"
+     " 1.0)[..., None]"),                                                 # float64 scale
+    ("append.py", "y = (x / scale[..., None]).astype(np.float32)",
+     "y = x.astype(np.float64) / scale[..., None].astype(np.float64)"),   # float64 quotient
     # rows per sequence
     ("varlen.py", "o, s = relative_attention(q[cu[b]:cu[b + 1]][None]",
      "o, s = relative_attention(q[cu[b] + 1:cu[b + 1] + 1][None]"),       # row offset
@@ -101,3 +108,4 @@ def test_mutant_is_caught(tmp_path, index):
             caught.append((pin.__name__, type(exc).__name__))
             break
     assert caught, "no pin caught mutant %d: %s -> %s" % (index, old, new)
+
