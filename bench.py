@@ -13,9 +13,14 @@ section on vLLM's optimisations: batch-1 decode at 100K context).
 
 Cache hygiene: the inputs are cloned into enough copies that the steps rotate over at
 least 1 GiB, four times the 256 MiB Infinity Cache, so every step streams its K/V from
-HBM. The K timed steps run back to back, bracketed by device synchronisations; on every
-8th step the library launches its kernels with HIP events that the runtime stamps with
-each kernel's start and end, which give the per-kernel durations of the roofline.
+HBM. Three passes of K steps each:
+  1. back to back between two device synchronisations, launched as a caller would:
+     the reported µs/step;
+  2. the library launches each step's kernels with HIP events that the runtime stamps
+     with the kernel's own start and end: the per-kernel durations of the roofline (the
+     stamping adds launch overhead, so this pass is not the figure);
+  3. each step between a pair of events on the launch stream: the median, p10 and p90
+     of single steps.
 
 Output: one JSON line (rank 0, N = 1) with the step time, the achieved HBM bandwidth
 over the algorithmic bytes, the roofline of the dominant kernel and the CPU oracle's
@@ -68,6 +73,11 @@ WORKLOADS = {
                       "log-uniform [32768,262144], bf16 paged KV (page 16)",
     "v1_window_verify": "verify, 9 causal rows, 64q/16kv, d=128, batch 16, W=512, seq_lens "
                         "U[2048,32768], bf16 paged KV (page 16)",
+    "v1_full_mtp9": "verify of a 9-token MTP step, 9 causal rows, 64q/8kv, d=128, batch 4, "
+                    "full layer, seq_lens log-uniform [32768,262144], bf16 paged KV (page 16)",
+    "v1_full_mtp9_varlen": "verify of a 9-token MTP step with 1..9 rows per sequence (seeded), "
+                           "64q/8kv, d=128, batch 4, full layer, seq_lens log-uniform "
+                           "[32768,262144], bf16 paged KV (page 16)",
     "tp4_100k": "one GPU's TP4 share of the full-context layer: 12q/2kv, d=128, batch 1, "
                 "1 row, 100,000 keys, bf16 paged KV (page 16)",
     "tp8_100k": "one GPU's TP8 share of the full-context layer: 6q/1kv, d=128, batch 1, "
@@ -403,8 +413,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-stride", type=int, default=8,
-                    help="record per-kernel HIP events on every N-th timed step")
+    ap.add_argument("--event-stride", type=int, default=1,
+                    help="in the kernel-timing pass, stamp every N-th step's kernels")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events (no roofline)")
     ap.add_argument("--op", default="decode", choices=("decode", "append"),
@@ -524,20 +534,43 @@ def main():
 
     prefill_plan = info["kernel"] == binding.RATTN_KERNEL_PREFILL
     K = args.steps
-    stride = max(1, args.event_stride)
-    nrec = (K + stride - 1) // stride
-    if not args.no_kernel_events:
-        binding.rattn_profile_begin(plan.handle, nrec, stride)
+    # pass 1, the figure: K steps back to back between two device synchronisations,
+    # launched as a caller would launch them (no instrumentation)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # pass 2, the kernels: the same K steps, every stride-th launched with events that
+    # the runtime stamps with each kernel's own start and end (stamping adds launch
+    # overhead, which is why this pass is not the figure)
+    stride = max(1, args.event_stride)
+    nrec = (K + stride - 1) // stride
     if args.no_kernel_events:
         split_ms, comb_ms = [float("nan")], [float("nan")]
     else:
+        binding.rattn_profile_begin(plan.handle, nrec, stride)
+        for i in range(K):
+            step(i)
         split_ms, comb_ms = binding.rattn_profile_end(plan.handle, nrec)
+    # pass 3, single steps: the same K steps, each between a pair of events on the launch
+    # stream (the events add their own small gaps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        evs[i].record()
+        step(i)
+    evs[K].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(K))
+
+    def pct(v, f):
+        return round(v[min(len(v) - 1, int(f * len(v)))], 3)
+    step_stats = {"mean": round(sum(per_step) / K, 3), "median": pct(per_step, 0.5),
+                  "p10": pct(per_step, 0.1), "p90": pct(per_step, 0.9), "samples": K,
+                  "how": "a third pass of the same steps, each between two events on "
+                         "the launch stream"}
     hot_us = None
     if args.hot_cache:
         # secondary: the same steps on one input copy, whose K/V partly stay in the caches
@@ -603,12 +636,15 @@ def main():
         "hbm_GBps": round(tr.total / (us * 1e-6) / 1e9, 1),
         "TFLOPs": round(tr.flops / (us * 1e-6) / 1e12, 2),
         "hbm_frac_of_peak": round(tr.total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_us": step_stats,
         "kernels_us": {
             "split_kv_mean": round(split_mean_s * 1e6, 3),
             "split_kv_median": round(srt[len(srt) // 2] * 1e3, 3),
             "split_kv_p10": round(srt[len(srt) // 10] * 1e3, 3),
             "split_kv_p90": round(srt[(len(srt) * 9) // 10] * 1e3, 3),
             "combine_mean": round(sum(comb_ms) / len(comb_ms) * 1e3, 3),
+            "samples": len(split_ms),
+            "event_stride": stride,
         },
         "plan_host_us": round(plan_us, 1),
         "hot_cache_us_per_step": hot_us,

@@ -11,7 +11,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librattn.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 RATTN_OK, RATTN_E_INVALID, RATTN_E_UNSUPPORTED, RATTN_E_HIP, RATTN_E_NOMEM = range(5)
 RATTN_KV_BF16, RATTN_KV_FP8_E4M3 = 0, 1

@@ -10,7 +10,7 @@ namespace rattn {
 
 constexpr int kHeadDim = 128;     // head size of every layer (page 2, model architecture)
 constexpr int kTileKeys = 32;     // keys per inner-loop step: two 16-key MFMA subtiles
-constexpr int kMaxRows = 64;      // packed query rows per (sequence, KV head): 4 waves
+constexpr int kMaxRows = 128;     // packed query rows per (sequence, KV head): 8 waves
 constexpr int kMaxSplits = 4096;  // largest forced split count per (sequence, KV head)
 constexpr int kMaxGroups = 1 << 16;   // largest split-kernel grid
 constexpr int kChunkPages = 512;  // page ids staged in LDS per chunk of a piece
@@ -18,18 +18,20 @@ constexpr int kChunkPages = 512;  // page ids staged in LDS per chunk of a piece
 // Bias slice of one tile: G heads x (32 + n - 1) distances, loaded by the work-group's
 // threads with kBiasPerThread loads each.
 constexpr int kBiasPerThread = 4;
-constexpr int kMaxBiasSlice = 4 * 64 * kBiasPerThread;   // at 4 waves
+constexpr int kMaxWaves = 8;      // waves of a split work-group (one 16-row tile each)
 
 // Waves per split work-group for G query heads per KV head and n rows: each wave owns
-// one 16-row MFMA tile of ceil(G n / waves) rows. A multi-wave group's threads must
-// cover a tile's bias slice with kBiasPerThread loads each (a single wave gathers its
-// own). Returns 0 when 4 waves do not suffice.
+// one 16-row MFMA tile of ceil(G n / waves) rows (1, 2, 4 or 8 waves for up to 16, 32,
+// 64 or 128 rows; 8 waves run two per SIMD, one work-group per CU). A multi-wave
+// group's threads must cover a tile's bias slice with kBiasPerThread loads each (a
+// single wave gathers its own). Returns 0 when 8 waves do not suffice.
 inline int waves_for(int G, int n) {
   const int rows = G * n;
+  if (rows > kMaxRows) return 0;
   if (rows <= 16) return 1;
-  int w = rows <= 32 ? 2 : 4;
+  int w = rows <= 32 ? 2 : (rows <= 64 ? 4 : 8);
   const int slice = G * (kTileKeys + n - 1);
-  if (slice > 64 * w * kBiasPerThread) w = 4;
+  while (w < kMaxWaves && slice > 64 * w * kBiasPerThread) w *= 2;
   return slice <= 64 * w * kBiasPerThread ? w : 0;
 }
 

@@ -25,12 +25,13 @@ namespace rattn {
 // ---------------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------------
-// variant index: waves per piece (1, 2, 4), KV format, partition; single-wave pieces
+// variant index: waves per piece (1, 2, 4, 8), KV format, partition; single-wave pieces
 // also in merging groups of kMergeWaves
 #define RATTN_VARIANTS(X)                                                               \
   X(1, false, false) X(1, true, false) X(2, false, false) X(2, true, false)              \
-  X(4, false, false) X(4, true, false) X(1, false, true) X(1, true, true)                \
-  X(2, false, true) X(2, true, true) X(4, false, true) X(4, true, true)
+  X(4, false, false) X(4, true, false) X(8, false, false) X(8, true, false)              \
+  X(1, false, true) X(1, true, true) X(2, false, true) X(2, true, true)                 \
+  X(4, false, true) X(4, true, true) X(8, false, true) X(8, true, true)
 
 static int variant_key(int waves, bool fp8, bool even) {
   return waves * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);

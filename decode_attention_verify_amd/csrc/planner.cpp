@@ -64,10 +64,10 @@ rattn_status validate_problem(const rattn_problem* p) {
   if (p->num_splits > kMaxSplits) return RATTN_E_UNSUPPORTED;
   // the bias table is indexed with 32-bit element offsets
   if ((int64_t)p->num_q_heads * ((int64_t)p->dmax + 1) > INT32_MAX) return RATTN_E_UNSUPPORTED;
-  // the work partition multiplies tile counts by the grid size in 64-bit arithmetic
+  // the split kernel counts the call's tiles (every unit's, at lengths up to
+  // max_seq_len) in 32-bit integers: their sum must stay below 2^31
   const int64_t total = (int64_t)p->batch * p->num_kv_heads * unit_tiles_bound(*p);
-  // (the prefill kernel's row and query offsets are 64-bit as well)
-  if (total > ((int64_t)1 << 62) / kMaxGroups) return RATTN_E_UNSUPPORTED;
+  if (total > INT32_MAX) return RATTN_E_UNSUPPORTED;
   return RATTN_OK;
 }
 

@@ -8,9 +8,10 @@
 // bias access, and merges the splits.
 //
 // Design on gfx950:
-//  * one work-group of 1, 2 or 4 waves per piece of a (sequence, KV head) unit; the G*n
-//    packed query rows (G = Hq/Hkv) go to 16-row MFMA tiles, one per wave (6 rows pad to
-//    16 here, not to 64 as in the pages' Blackwell tile);
+//  * one work-group of 1, 2, 4 or 8 waves per piece of a (sequence, KV head) unit; the
+//    G*n packed query rows (G = Hq/Hkv) go to 16-row MFMA tiles, one per wave (6 rows pad
+//    to 16 here, not to 64 as in the pages' Blackwell tile; the 72 rows of a 9-token step
+//    on 8-head groups take 8 waves of 9 rows);
 //  * K and V tiles of 32 keys are read with non-temporal 16-byte loads in row order (a
 //    16-lane pass reads 256 contiguous bytes), two tiles in flight, and stored to LDS
 //    with XOR-swizzled 16-byte chunks; page ids are staged in LDS per chunk of pages;
@@ -70,7 +71,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   // buffers derive from STAGE_BIAS (two buffers exactly when several waves share one).
   constexpr bool STAGE_BIAS = WR > 1;
   constexpr int BIAS_BUFS = STAGE_BIAS ? 2 : 1;
-  __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? kMaxBiasSlice : 1];
+  __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? 64 * WR * kBiasPerThread : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -238,7 +239,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     // clamped to [0, Dmax] (a masked key reads an in-range entry that the mask
     // discards), and every lane then reads its row's entries from LDS.
     const int slice_len = kTileKeys + n - 1;
-    const int slice_elems = G * slice_len;     // <= kMaxBiasSlice (validated)
+    const int slice_elems = G * slice_len;     // <= 64 WR kBiasPerThread (validated)
     const int nbias = (slice_elems + 64 * WR - 1) / (64 * WR);   // slice loads per thread
     const int sub_lo = k_lo & ~15;           // first 16-key subtile holding a visible key
     const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
@@ -379,7 +380,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
 #pragma unroll
         for (int q = 0; q < kBiasPerThread; ++q) {
           if (q > 0 && q >= nbias) break;   // uniform
-          bl[tid + 64 * WR * q] = X.bs[q];   // < kMaxBiasSlice; past the slice: unread
+          bl[tid + 64 * WR * q] = X.bs[q];   // in the buffer; past the slice: unread
         }
       }
       // this wave's share -> LDS as bf16 (swizzled). V of keys outside [k_lo, L) becomes

@@ -101,6 +101,14 @@ def _named_specs():
                                ("loguniform", 32768, 262144), bias_decay=1e-5),
         "v1_window_verify": Spec("v1_window_verify", 16, 9, 64, 16, 128, 512, 520, 16,
                                  KV_BF16, ("uniform", 2048, 32768)),
+        # its full layers during a 9-token step (8 chained MTP heads): 72 packed rows per
+        # (sequence, KV head)
+        "v1_full_mtp9": Spec("v1_full_mtp9", 4, 9, 64, 8, 128, 0, 262143, 16, KV_BF16,
+                             ("loguniform", 32768, 262144), bias_decay=1e-5),
+        # the same step when each sequence verifies its own number of tokens, 1..9
+        "v1_full_mtp9_varlen": Spec("v1_full_mtp9_varlen", 4, 9, 64, 8, 128, 0, 262143, 16,
+                                    KV_BF16, ("loguniform", 32768, 262144), bias_decay=1e-5,
+                                    rows_seed=12),
         # one GPU's share of the headline layer under tensor parallelism over KV heads:
         # TP4 keeps 2 KV heads and their 12 query heads, TP8 one and its 6
         "tp4_100k": Spec("tp4_100k", 1, 1, 12, 2, 128, 0, 131071, 16, KV_BF16, 100000,

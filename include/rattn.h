@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define RATTN_ABI_VERSION 3
+#define RATTN_ABI_VERSION 4
 
 typedef struct rattn_plan_s* rattn_plan_t;
 
@@ -96,9 +96,9 @@ typedef struct {
   int32_t num_q_heads;       /* query heads (48 in the Inkling 2 Small layers)            */
   int32_t num_kv_heads;      /* KV heads (8); num_q_heads % num_kv_heads == 0             */
   int32_t head_dim;          /* 128 (the only supported value)                            */
-  int32_t n_query_rows;      /* rows per sequence: 1 for decode, 1 + drafts for verify,   */
-                             /* the chunk length for a chunked prefill (see              */
-                             /* RATTN_KERNEL_PREFILL)                                    */
+  int32_t n_query_rows;      /* rows per sequence: 1 for decode, 1 + drafts for verify    */
+                             /* (up to 9 tokens for MTP steps), the chunk length for a   */
+                             /* chunked prefill (see RATTN_KERNEL_PREFILL)               */
   int32_t page_size;         /* slots per page: a power of two >= 16                      */
   int32_t num_pages;         /* physical pages in the cache                               */
   int32_t max_pages_per_seq; /* page_table row length                                     */
@@ -117,8 +117,8 @@ typedef struct {
   int32_t num_splits;        /* pieces (key ranges) per (sequence, KV head), nominal      */
   int32_t keys_per_split;    /* keys per piece at max_seq_len, nominal                    */
   int32_t tile_keys;         /* keys per inner-loop step                                  */
-  int32_t row_tiles;         /* waves per piece (split: one 16-row MFMA tile each;        */
-                             /* prefill: 8 per work-group)                                */
+  int32_t row_tiles;         /* waves per piece (split: 1, 2, 4 or 8, one 16-row MFMA     */
+                             /* tile each; prefill: 8 per work-group)                     */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (work-groups, 1, 1)             */
   int32_t combine_blocks;    /* combine work-groups; 0 when nothing is merged after the   */
                              /* split kernel                                              */
@@ -131,16 +131,25 @@ typedef struct {
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps, and a flag word         */
 } rattn_plan_info;
 
-/* rattn_plan_info.kernel. Up to 64 packed rows per (sequence, KV head) (G * n, G =
- * num_q_heads / num_kv_heads): the split-KV kernel and, when a unit is split, the
- * log-sum-exp combine. More rows (chunked prefill): one MFMA kernel per block of query
- * tokens over all the keys they see, no split; built for G = 4, 6 and 8 over a bf16
- * cache, without forced splits (else RATTN_E_UNSUPPORTED). */
+/* rattn_plan_info.kernel. Up to 128 packed rows per (sequence, KV head) (G * n, G =
+ * num_q_heads / num_kv_heads; 1, 2, 4 or 8 waves of one 16-row tile each): the split-KV
+ * kernel and, when a unit is split, the log-sum-exp combine. More rows (chunked
+ * prefill): one MFMA kernel per block of query tokens over all the keys they see, no
+ * split; built for G = 4, 6 and 8 over a bf16 cache, without forced splits (else
+ * RATTN_E_UNSUPPORTED). */
 #define RATTN_KERNEL_SPLIT_KV 0
 #define RATTN_KERNEL_PREFILL 1
 
 /* Validate `prob`, size the launch for the current HIP device and allocate the
- * workspace. On success *plan_out owns the workspace until rattn_free. */
+ * workspace. On success *plan_out owns the workspace until rattn_free.
+ * The split of the key range follows page 2 ("vLLM TML Inkling support", technical
+ * optimisation section, FA4 kernel): the number of splits is chosen from the batch,
+ * the head count and the KV length; here from batch x KV heads, the rows per sequence,
+ * the visible key span, the device's compute units and the split kernel's resident
+ * work-groups per CU, which this call queries. Problems whose tiles (batch x num_kv_heads
+ * x ceil((span + 31) / 32), span = max_seq_len, or window + n - 1 in a window layer)
+ * reach 2^31 are RATTN_E_UNSUPPORTED. Allocates device memory (hipMalloc); see
+ * rattn_decode for the call itself. */
 rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out);
 
 /* Validate `prob` and run the planner for a device with `num_cus` compute units,
@@ -206,7 +215,11 @@ rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const
                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                              int32_t* flags, void* stream);
 
-/* Release the plan and its workspace (NULL is accepted). */
+/* Release the plan and its workspace, the split partials that page 2's split-KV
+ * design ("vLLM TML Inkling support", FA4 kernel: the key range is split and the splits
+ * merged) needs between the split kernel and the combine. NULL is accepted. Frees device
+ * memory (hipFree), so no call that uses the plan may still be in flight: synchronise
+ * its stream first. Returns RATTN_E_HIP if the runtime reports an error. */
 rattn_status rattn_free(rattn_plan_t plan);
 
 /* Read and clear the plan's device flag word (RATTN_FLAG_*). Synchronises `stream`. */

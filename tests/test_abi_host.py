@@ -45,14 +45,17 @@ INVALID = [
 ]
 UNSUPPORTED = [
     dict(head_dim=64), dict(page_size=24, max_pages_per_seq=6250),
-    # more than 64 packed rows go to the prefill kernel, built for G = 4, 6, 8 over a
+    # more than 128 packed rows go to the prefill kernel, built for G = 4, 6, 8 over a
     # bf16 cache without forced splits
-    dict(n_query_rows=11, kv_dtype=binding.RATTN_KV_FP8_E4M3),
+    dict(n_query_rows=22, kv_dtype=binding.RATTN_KV_FP8_E4M3),
     dict(n_query_rows=100, num_q_heads=24), dict(n_query_rows=100, num_splits=4),
+    # the call's tiles are counted in 32-bit integers: 2^31 tiles or more are refused
+    dict(batch=256, num_kv_heads=8, num_q_heads=48, max_seq_len=1 << 25,
+         max_pages_per_seq=1 << 21, num_pages=1 << 21),
     dict(page_size=8, max_pages_per_seq=12500), dict(num_splits=4097),
-    # 64 query heads per KV head: a tile's bias slice (64 x 32 distances) exceeds what
-    # a work-group stages
-    dict(num_q_heads=512, num_kv_heads=8),
+    # 128 query heads per KV head: a tile's bias slice (128 x 32 distances) exceeds what
+    # a work-group stages (64 per KV head fit an 8-wave group)
+    dict(num_q_heads=1024, num_kv_heads=8),
 ]
 
 
@@ -166,7 +169,8 @@ def test_planner_covers_every_key():
                 assert pieces <= max(units, units * tiles)
             assert 1 <= info.grid_x <= 1 << 16
             rows = 6 * p.n_query_rows
-            assert info.row_tiles == (1 if rows <= 16 else 2 if rows <= 32 else 4)
+            assert info.row_tiles == (1 if rows <= 16 else 2 if rows <= 32 else
+                                      4 if rows <= 64 else 8)
             if p.num_splits:
                 assert ppg == (p.num_splits if p.num_splits in (2, 3) and rows <= 16 else 1)
             assert ppg in (1, 2, 3) and (ppg == 1 or ppg == info.num_splits)
@@ -205,12 +209,12 @@ def test_combine_shape_follows_the_pieces():
     assert verify.combine_blocks == 16 * 8 * 48 // 4
 
 
-@pytest.mark.parametrize("hq,n,tokens", [(48, 11, 64), (48, 2048, 64), (32, 17, 64),
-                                         (64, 9, 32), (64, 1000, 32)])
+@pytest.mark.parametrize("hq,n,tokens", [(48, 22, 64), (48, 2048, 64), (32, 33, 64),
+                                         (64, 17, 32), (64, 1000, 32)])
 def test_planner_prefill(hq, n, tokens):
-    # more than 64 packed rows: one 8-wave prefill work-group per (sequence, KV head, block
-    # of query tokens: 4 blocks of 16 for 6- and 4-head groups, 2 for 8-head groups), a
-    # grid rounded up to a multiple of 8 (one share per XCD), no combine
+    # more than 128 packed rows: one 8-wave prefill work-group per (sequence, KV head,
+    # block of query tokens: 4 blocks of 16 for 6- and 4-head groups, 2 for 8-head
+    # groups), a grid rounded up to a multiple of 8 (one share per XCD), no combine
     p = headline(batch=3, num_q_heads=hq, n_query_rows=n)
     info = binding.rattn_plan_describe(p, 256)
     assert info.kernel == binding.RATTN_KERNEL_PREFILL
@@ -228,3 +232,22 @@ def test_read_probe_rejects_bad_arguments():
                  (one, 4, 1000, None, 8, one, None), (one, 4, 4096, None, 0, one, None),
                  (one, 4, 4096, None, 8, None, None)):
         assert lib.rattn_read_probe(*args) == binding.RATTN_E_INVALID
+
+
+@pytest.mark.parametrize("hq,n", [(64, 9), (48, 11), (48, 21), (32, 32), (64, 16)])
+@pytest.mark.parametrize("kv", [binding.RATTN_KV_BF16, binding.RATTN_KV_FP8_E4M3])
+def test_planner_eight_wave_groups(hq, n, kv):
+    # 65 to 128 packed rows (the 9-token step on 8-head groups: 72 rows) stay on the
+    # split kernel, one 16-row tile per wave in 8-wave work-groups, for both cache
+    # formats; a full-context batch is shared evenly and merged by the combine
+    G = hq // 8
+    assert 64 < G * n <= 128
+    p = headline(batch=4, num_q_heads=hq, n_query_rows=n, max_seq_len=262144,
+                 max_pages_per_seq=16384, num_pages=65536, dmax=262143, kv_dtype=kv)
+    info = binding.rattn_plan_describe(p, 256)
+    assert info.kernel == binding.RATTN_KERNEL_SPLIT_KV and info.row_tiles == 8
+    assert info.pieces_per_group == 1 and info.combine_blocks == -(-4 * n * hq // 4)
+    assert info.workspace_bytes >= (info.grid_x + 32) * G * n * 129 * 4
+    # batch 1: the unit's keys cut into pieces of equal length
+    one = binding.rattn_plan_describe(headline(num_q_heads=hq, n_query_rows=n, kv_dtype=kv), 256)
+    assert one.row_tiles == 8 and one.num_splits > 1 and one.grid_x == 8 * one.num_splits

@@ -71,6 +71,38 @@ def test_v1_window_verify():
     check_case(synth.spec("v1_window_verify"), seed=0, gen_device="cuda")
 
 
+# ------------------- 65 to 128 packed rows: 8-wave work-groups (the 9-token MTP step)
+
+def test_v1_full_mtp9_sampled():
+    # the previous generation's full layer (64q/8kv) during a 9-token step: 72 packed rows
+    sp = synth.spec("v1_full_mtp9")
+    check_case(sp, seed=0, gen_device="cuda", batches=[1], kv_heads=None)
+    check_case(sp, seed=0, gen_device="cuda", kv_heads=[5])
+
+
+def test_v1_full_mtp9_fp8_sampled():
+    sp = small("v1_full_mtp9", kv_format=synth.KV_FP8, page_size=64, name="v1_full_mtp9_fp8")
+    check_case(sp, seed=1, gen_device="cuda", kv_heads=[2])
+
+
+@pytest.mark.parametrize("hq,hkv,n,W,splits,batch,fmt", [
+    (64, 8, 9, 0, 0, 5, synth.KV_BF16),       # even shares over mixed lengths
+    (64, 8, 9, 0, 0, 5, synth.KV_FP8),
+    (64, 8, 9, 0, 0, 1, synth.KV_BF16),       # one unit per KV head, cut into pieces
+    (48, 8, 11, 1024, 0, 3, synth.KV_BF16),   # 66 rows over a window
+    (48, 8, 21, 0, 3, 2, synth.KV_BF16),      # 126 rows, 3 forced pieces per unit
+    (64, 8, 16, 17, 0, 3, synth.KV_FP8),      # 128 rows, window 17
+    (32, 8, 32, 0, 7, 2, synth.KV_BF16),      # 4-head groups, 128 rows, 7 pieces
+    (512, 8, 1, 0, 0, 2, synth.KV_BF16),      # 64 heads per KV head: the bias slice
+])
+def test_eight_wave_groups(hq, hkv, n, W, splits, batch, fmt):
+    sp = small("full_100k", batch=batch, n_rows=n, num_q_heads=hq, num_kv_heads=hkv,
+               window=W, kv_format=fmt, page_size=64 if fmt == synth.KV_FP8 else 16,
+               seq_len=("uniform", n, 2600), dmax=3000, name="waves8")
+    _, _, info = check_case(sp, seed=hq + n + W + splits + batch, num_splits=splits)
+    assert info["row_tiles"] == 8
+
+
 # ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
 
 @pytest.mark.parametrize("name", ["tp4_100k", "tp8_100k"])

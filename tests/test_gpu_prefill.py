@@ -23,7 +23,7 @@ def small(base, **kw):
     return dataclasses.replace(synth.spec(base), **kw)
 
 
-@pytest.mark.parametrize("n,lens,W", [(11, (11, 40), 0), (65, (65, 700), 0),
+@pytest.mark.parametrize("n,lens,W", [(22, (22, 40), 0), (65, (65, 700), 0),
                                       (100, (100, 1500), 0), (257, (300, 2100), 0),
                                       (96, (96, 900), 1), (130, (200, 3000), 64),
                                       (128, (128, 2000), 1024)])

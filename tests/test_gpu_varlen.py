@@ -136,6 +136,24 @@ def test_bad_row_ranges_are_flagged():
     assert bool(torch.isnan(lse[2:6].cpu()).all()) and bool(torch.isnan(out[2:6].float()).all())
 
 
+@pytest.mark.parametrize("fmt", [synth.KV_BF16, synth.KV_FP8])
+def test_mtp_rows_gqa8_full(fmt):
+    # the previous generation's full layers (64q/8kv) with 1..9 tokens per sequence: up
+    # to 72 packed rows, 8-wave work-groups
+    sp = small("v1_full_mtp9", batch=7, kv_format=fmt, page_size=64 if fmt == synth.KV_FP8
+               else 16, seq_len=("uniform", 9, 2500), dmax=3000, name="varlen_mtp9")
+    rows = synth.draw_rows_per_seq(7, 9, seed=8)
+    check_varlen(sp, rows, seed=8)
+
+
+@pytest.mark.parametrize("fmt", [synth.KV_BF16, synth.KV_FP8])
+def test_varlen_mtp9_full_size_sampled(fmt):
+    sp = small("v1_full_mtp9_varlen", kv_format=fmt, page_size=64 if fmt == synth.KV_FP8
+               else 16, name="v1_full_mtp9_varlen_" + fmt)
+    rows = synth.draw_rows_per_seq(sp.batch, sp.n_rows, seed=sp.rows_seed, allow_zero=False)
+    check_varlen(sp, rows, seed=0, gen_device="cuda", batches=[0, 3], kv_heads=[1, 6])
+
+
 def test_varlen_verify_full_size_sampled():
     # the verify workload's shapes (16 sequences of 32K-256K keys) with 1..8 rows each
     sp = synth.spec("verify_b16")
