@@ -70,6 +70,7 @@ def load(path=None):
     lib.rattn_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.rattn_decode.argtypes = [vp] * 12
     lib.rattn_decode_varlen.argtypes = [vp] * 9 + [i32] + [vp] * 4
+    lib.rattn_decode_static.argtypes = [ctypes.POINTER(Problem)] + [vp] * 12
     lib.rattn_free.argtypes = [vp]
     lib.rattn_debug_flags.argtypes = [vp, i32p, vp]
     lib.rattn_profile_begin.argtypes = [vp, i32, i32]
@@ -82,7 +83,7 @@ def load(path=None):
     for fn in ("rattn_plan", "rattn_plan_describe", "rattn_plan_get_info", "rattn_decode",
                "rattn_free", "rattn_debug_flags", "rattn_profile_begin", "rattn_profile_end",
                "rattn_abi_version", "rattn_append_kv", "rattn_decode_varlen",
-               "rattn_read_probe"):
+               "rattn_read_probe", "rattn_decode_static"):
         getattr(lib, fn).restype = ctypes.c_int32
     if lib.rattn_abi_version() != ABI_VERSION:
         raise ImportError("librattn ABI %d, binding expects %d" % (lib.rattn_abi_version(),
@@ -223,6 +224,34 @@ def rattn_decode(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_le
     st = load().rattn_decode(*args)
     if st != RATTN_OK:
         raise RattnError(st, "rattn_decode")
+
+
+def rattn_decode_static(problem, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                        bias, out, lse=None, flags=None, stream=None):
+    """Enqueue one call without a plan, whose partials live in the library's static
+    device array (no allocation); shapes are checked against ``problem`` first."""
+    import torch
+    check_shapes(problem, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, bias,
+                 out, lse)
+    dev = q.device
+    args = [
+        ctypes.byref(problem),
+        _ptr(q, "q", (torch.bfloat16,)),
+        _ptr(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev),
+        _ptr(v_cache, "v_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dev),
+        _ptr(k_scale, "k_scale", (torch.float32,), dev),
+        _ptr(v_scale, "v_scale", (torch.float32,), dev),
+        _ptr(page_table, "page_table", (torch.int32,), dev),
+        _ptr(seq_lens, "seq_lens", (torch.int32,), dev),
+        _ptr(bias, "bias", (torch.float32,), dev),
+        _ptr(out, "out", (torch.bfloat16,), dev),
+        _ptr(lse, "lse", (torch.float32,), dev),
+        _ptr(flags, "flags", (torch.int32,), dev),
+        _stream(stream),
+    ]
+    st = load().rattn_decode_static(*args)
+    if st != RATTN_OK:
+        raise RattnError(st, "rattn_decode_static")
 
 
 def rattn_decode_varlen(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,

@@ -47,7 +47,7 @@ def build(verbose=False, save_temps=False):
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
-    for name in ("kernels.hip", "api.cpp", "planner.cpp"):
+    for name in ("kernels.hip", "scratch.hip", "api.cpp", "planner.cpp"):
         src = os.path.join(CSRC, name)
         obj = os.path.join(BUILD_DIR, name + ".o")
         cmd = [hipcc, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS

@@ -3,6 +3,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -148,15 +149,18 @@ rattn_status rattn_plan_get_info(rattn_plan_t plan, rattn_plan_info* info) {
 
 namespace {
 
-rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
+// One call's launches: the problem, its plan, the workspace that holds the split
+// partials (plan.workspace_bytes bytes, the flag word in its last 256), and the flag
+// word the kernels report bad device data in.
+rattn_status decode_call(const rattn_problem& pr, const rattn::Plan& plan, void* workspace,
+                         int32_t* flags, hipEvent_t* ev, const void* q, const void* k_cache,
                          const void* v_cache, const float* k_scale, const float* v_scale,
                          const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* cu_rows, int32_t row_cap, const float* bias, void* out,
                          float* lse, void* stream) {
-  if (plan == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr ||
-      page_table == nullptr || seq_lens == nullptr || bias == nullptr || out == nullptr)
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr ||
+      seq_lens == nullptr || bias == nullptr || out == nullptr)
     return RATTN_E_INVALID;
-  const rattn_problem& pr = plan->prob;
   const bool fp8 = pr.kv_dtype == RATTN_KV_FP8_E4M3;
   if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return RATTN_E_INVALID;
 
@@ -171,10 +175,10 @@ rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
   a.bias = bias;
   a.out = (uint16_t*)out;
   a.lse = lse;
-  a.part_o = (float*)plan->workspace;
-  a.part_lse = a.part_o + plan->plan.part_o_floats;
-  a.unit_info = (int32_t*)(a.part_lse + plan->plan.part_lse_floats);
-  a.flags = plan->flags;
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + plan.part_o_floats;
+  a.unit_info = (int32_t*)(a.part_lse + plan.part_lse_floats);
+  a.flags = flags;
   a.cu_rows = cu_rows;
   a.row_cap = row_cap;
   a.batch = pr.batch;
@@ -190,23 +194,73 @@ rattn_status decode_call(rattn_plan_t plan, const void* q, const void* k_cache,
   a.window = pr.window;
   a.dmax = pr.dmax;
   a.softmax_scale = pr.softmax_scale;
-  a.split_groups = plan->plan.split_groups;
-  a.splits_per_unit = plan->plan.splits_per_unit;
+  a.split_groups = plan.split_groups;
+  a.splits_per_unit = plan.splits_per_unit;
 
-  hipEvent_t* ev = nullptr;
-  if (plan->prof_count < plan->prof_max && plan->prof_calls++ % plan->prof_stride == 0)
-    ev = &plan->prof_events[4 * plan->prof_count++];
-  if (plan->plan.prefill)
-    return rattn::launch_prefill(a, plan->plan.prefill_hw, a.group, stream, ev ? ev[0] : nullptr,
+  if (plan.prefill)
+    return rattn::launch_prefill(a, plan.prefill_hw, a.group, stream, ev ? ev[0] : nullptr,
                                  ev ? ev[1] : nullptr) == 0
                ? RATTN_OK
                : RATTN_E_HIP;
-  if (rattn::launch_split_kv(a, plan->plan.waves, fp8, plan->plan.ws, stream, ev ? ev[0] : nullptr,
+  if (rattn::launch_split_kv(a, plan.waves, fp8, plan.ws, stream, ev ? ev[0] : nullptr,
                              ev ? ev[1] : nullptr) != 0)
     return RATTN_E_HIP;
-  if (needs_combine(plan->plan) &&
+  if (needs_combine(plan) &&
       rattn::launch_combine(a, stream, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr) != 0)
     return RATTN_E_HIP;
+  return RATTN_OK;
+}
+
+rattn_status plan_call(rattn_plan_t plan, const void* q, const void* k_cache,
+                       const void* v_cache, const float* k_scale, const float* v_scale,
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const int32_t* cu_rows, int32_t row_cap, const float* bias, void* out,
+                       float* lse, void* stream) {
+  if (plan == nullptr) return RATTN_E_INVALID;
+  hipEvent_t* ev = nullptr;
+  if (plan->prof_count < plan->prof_max && plan->prof_calls++ % plan->prof_stride == 0)
+    ev = &plan->prof_events[4 * plan->prof_count++];
+  return decode_call(plan->prob, plan->plan, plan->workspace, plan->flags, ev, q, k_cache,
+                     v_cache, k_scale, v_scale, page_table, seq_lens, cu_rows, row_cap, bias,
+                     out, lse, stream);
+}
+
+// Launch shape of the current device, for calls without a plan (rattn_decode_static):
+// the CU count and, per split-kernel variant, the resident work-groups per CU, each
+// queried once per device and kept.
+struct DeviceShape {
+  int cus = 0;
+  int blocks_per_cu[64] = {};   // by variant: waves (1, 2, 4, 8) x format x partition
+};
+std::mutex g_shape_mutex;
+DeviceShape g_shapes[64];
+
+rattn_status device_shape(int dev, const rattn_problem& p, int32_t* cus, int32_t* bpc) {
+  if (dev < 0 || dev >= 64) return RATTN_E_HIP;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const bool prefill = (int64_t)G * p.n_query_rows > rattn::kMaxRows;
+  const int waves = prefill ? 0 : rattn::waves_for(G, p.n_query_rows);
+  const bool fp8 = p.kv_dtype == RATTN_KV_FP8_E4M3;
+  const bool even = rattn::uses_even_shares(p);
+  const int key = (waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0) * 4 +
+                  (fp8 ? 2 : 0) + (even ? 1 : 0);
+  std::lock_guard<std::mutex> lock(g_shape_mutex);
+  DeviceShape& ds = g_shapes[dev];
+  if (ds.cus == 0 &&
+      hipDeviceGetAttribute(&ds.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    ds.cus = 0;
+    return RATTN_E_HIP;
+  }
+  *cus = ds.cus;
+  if (prefill) {
+    *bpc = 1;
+    return RATTN_OK;
+  }
+  if (ds.blocks_per_cu[key] == 0) {
+    const int b = rattn::split_kv_blocks_per_cu(waves, fp8, even);
+    ds.blocks_per_cu[key] = b >= 1 ? b : rattn::kDefaultBlocksPerCU;
+  }
+  *bpc = ds.blocks_per_cu[key];
   return RATTN_OK;
 }
 
@@ -218,8 +272,37 @@ rattn_status rattn_decode(rattn_plan_t plan, const void* q, const void* k_cache,
                           const void* v_cache, const float* k_scale, const float* v_scale,
                           const int32_t* page_table, const int32_t* seq_lens,
                           const float* bias, void* out, float* lse, void* stream) {
-  return decode_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
-                     nullptr, 0, bias, out, lse, stream);
+  return plan_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                   nullptr, 0, bias, out, lse, stream);
+}
+
+rattn_status rattn_decode_static(const rattn_problem* prob, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* page_table,
+                                 const int32_t* seq_lens, const float* bias, void* out,
+                                 float* lse, int32_t* flags, void* stream) {
+  const rattn_status st = rattn::validate_problem(prob);
+  if (st != RATTN_OK) return st;
+  // pointer checks before any HIP call, as for rattn_decode
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || page_table == nullptr ||
+      seq_lens == nullptr || bias == nullptr || out == nullptr)
+    return RATTN_E_INVALID;
+  const bool fp8 = prob->kv_dtype == RATTN_KV_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return RATTN_E_INVALID;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return RATTN_E_HIP;
+  int32_t cus = 0, bpc = 0;
+  if (device_shape(dev, *prob, &cus, &bpc) != RATTN_OK) return RATTN_E_HIP;
+  const rattn::Plan plan = rattn::make_plan(*prob, cus, bpc);
+  if (plan.workspace_bytes > rattn::kStaticScratchBytes) return RATTN_E_UNSUPPORTED;
+  void* scratch = nullptr;    // this device's static array (resolved on its first call)
+  if (rattn::static_scratch_ptr(dev, &scratch) != 0) return RATTN_E_HIP;
+  // the flag word: the caller's, or the scratch's last 256 bytes (never read)
+  int32_t* fl = flags != nullptr
+                    ? flags
+                    : (int32_t*)((char*)scratch + rattn::kStaticScratchBytes - 256);
+  return decode_call(*prob, plan, scratch, fl, nullptr, q, k_cache, v_cache, k_scale, v_scale,
+                     page_table, seq_lens, nullptr, 0, bias, out, lse, stream);
 }
 
 rattn_status rattn_decode_varlen(rattn_plan_t plan, const void* q, const void* k_cache,
@@ -230,8 +313,8 @@ rattn_status rattn_decode_varlen(rattn_plan_t plan, const void* q, const void* k
                                  void* stream) {
   if (plan == nullptr || cu_rows == nullptr || num_rows < 0) return RATTN_E_INVALID;
   if (plan->plan.prefill) return RATTN_E_UNSUPPORTED;   // rows per sequence: decode/verify
-  return decode_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
-                     cu_rows, num_rows, bias, out, lse, stream);
+  return plan_call(plan, q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens,
+                   cu_rows, num_rows, bias, out, lse, stream);
 }
 
 rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const void* v_new,

@@ -145,6 +145,12 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start = nullptr,
 // Work-groups of the combine launch for `rows` output rows (host function).
 int64_t combine_blocks(int64_t rows, int splits_per_unit);
 int launch_append_kv(const AppendArgs& a, void* stream);
+
+// The static scratch array of rattn_decode_static (scratch.hip): its size, and its
+// address on `device`, which must be the current device on the first call for that
+// device (resolved then with hipGetSymbolAddress and kept). Returns 0 or a hipError_t.
+constexpr int64_t kStaticScratchBytes = (int64_t)32 << 20;
+int static_scratch_ptr(int device, void** ptr);
 int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_read_probe(const void* buf, int64_t nblocks, int block_bytes, const int32_t* order,

@@ -215,6 +215,31 @@ rattn_status rattn_append_kv(const rattn_problem* prob, const void* k_new, const
                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                              int32_t* flags, void* stream);
 
+/* As rattn_decode, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. There is no plan: the
+ * call validates `prob` and plans on the host each time (the device's CU count and the
+ * split kernel's occupancy are queried once per device and kept), and its split
+ * partials, unit records and flag word live in a static device array of 32 MiB that the
+ * library's code object gives each GPU it runs on, held until the process ends. The
+ * array's address is resolved with hipGetSymbolAddress on the first call on each device
+ * (that device current). Nothing is allocated or freed: no hipMalloc, hipFree or
+ * allocating library routine.
+ *   prob       the problem, as for rattn_plan; a call whose partials would exceed the
+ *              array (plan workspace_bytes > 32 MiB, e.g. thousands of forced splits over
+ *              many rows) returns RATTN_E_UNSUPPORTED and launches nothing
+ *   flags      device int32, RATTN_FLAG_* bits OR-ed in for clamped bad device data (the
+ *              caller clears it); NULL = not reported
+ *   others     as for rattn_decode (device pointers, layouts, stream)
+ * Every call on a GPU shares that GPU's array, which keeps the last call's contents; no
+ * part of it needs clearing between calls (every partial is written before the combine
+ * reads it). Calls that overlap on one GPU (on two streams, or from two host threads
+ * without ordering) race on the array and give wrong results: order them on one stream. */
+rattn_status rattn_decode_static(const rattn_problem* prob, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* page_table,
+                                 const int32_t* seq_lens, const float* bias, void* out,
+                                 float* lse, int32_t* flags, void* stream);
+
 /* Release the plan and its workspace, the split partials that page 2's split-KV
  * design ("vLLM TML Inkling support", FA4 kernel: the key range is split and the splits
  * merged) needs between the split kernel and the combine. NULL is accepted. Frees device

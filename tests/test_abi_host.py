@@ -251,3 +251,26 @@ def test_planner_eight_wave_groups(hq, n, kv):
     # batch 1: the unit's keys cut into pieces of equal length
     one = binding.rattn_plan_describe(headline(num_q_heads=hq, n_query_rows=n, kv_dtype=kv), 256)
     assert one.row_tiles == 8 and one.num_splits > 1 and one.grid_x == 8 * one.num_splits
+
+
+def test_static_entry_checks_on_the_host():
+    # rattn_decode_static validates the problem and its pointers before any HIP call
+    lib = binding.load()
+    vp = ctypes.c_void_p
+    one = vp(16)                               # never dereferenced: rejected on the host
+    # q, k_cache, v_cache, k_scale, v_scale, page_table, seq_lens, bias, out, lse, flags,
+    # stream: a bf16 cache takes no scales
+    ptrs = [one, one, one, None, None, one, one, one, one, one, None, None]
+    assert len(ptrs) == len(lib.rattn_decode_static.argtypes) - 1
+    bad = headline(num_kv_heads=7)
+    assert lib.rattn_decode_static(ctypes.byref(bad), *ptrs) == binding.RATTN_E_INVALID
+    prob = headline()
+    for i in (0, 1, 2, 5, 6, 7, 8):            # q, k, v, table, lengths, bias, out
+        args = list(ptrs)
+        args[i] = None
+        assert lib.rattn_decode_static(ctypes.byref(prob), *args) == binding.RATTN_E_INVALID
+    args = list(ptrs)
+    args[3] = one                              # a scale array for a bf16 cache
+    assert lib.rattn_decode_static(ctypes.byref(prob), *args) == binding.RATTN_E_INVALID
+    fp8 = headline(kv_dtype=binding.RATTN_KV_FP8_E4M3)
+    assert lib.rattn_decode_static(ctypes.byref(fp8), *ptrs) == binding.RATTN_E_INVALID
