@@ -31,7 +31,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_splits", "keys_per_split", "tile_keys", "row_tiles", "grid_x", "grid_y",
         "grid_z", "combine_blocks", "num_cus", "blocks_per_cu", "kernel", "pieces_per_group")] + [
-        ("workspace_bytes", ctypes.c_int64)]
+        ("workspace_bytes", ctypes.c_int64), ("tiles_per_wave", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -54,6 +54,7 @@ void fill_info(const rattn_problem& p, const rattn::Plan& pl, rattn_plan_info* i
   info->kernel = pl.prefill ? RATTN_KERNEL_PREFILL : RATTN_KERNEL_SPLIT_KV;
   info->pieces_per_group = pl.prefill ? 1 : pl.ws;
   info->workspace_bytes = pl.workspace_bytes;
+  info->tiles_per_wave = pl.prefill ? 1 : pl.rt;
 }
 
 void destroy_events(rattn_plan_s* p) {
@@ -105,11 +106,12 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   if (p == nullptr) return RATTN_E_NOMEM;
   p->prob = *prob;
   const int G = prob->num_q_heads / prob->num_kv_heads;
+  const int rt = rattn::row_tiles_for(*prob);
   int bpc = (int64_t)G * prob->n_query_rows > rattn::kMaxRows
                 ? 1
-                : rattn::split_kv_blocks_per_cu(rattn::waves_for(G, prob->n_query_rows),
-                                                prob->kv_dtype == RATTN_KV_FP8_E4M3,
-                                                rattn::uses_even_shares(*prob));
+                : rattn::split_kv_blocks_per_cu(
+                      rt > 1 ? 1 : rattn::waves_for(G, prob->n_query_rows),
+                      prob->kv_dtype == RATTN_KV_FP8_E4M3, rattn::uses_even_shares(*prob), rt);
   if (bpc < 1) bpc = rattn::kDefaultBlocksPerCU;
   p->plan = rattn::make_plan(*prob, cus, bpc);
   p->device = dev;
@@ -202,7 +204,7 @@ rattn_status decode_call(const rattn_problem& pr, const rattn::Plan& plan, void*
                                  ev ? ev[1] : nullptr) == 0
                ? RATTN_OK
                : RATTN_E_HIP;
-  if (rattn::launch_split_kv(a, plan.waves, fp8, plan.ws, stream, ev ? ev[0] : nullptr,
+  if (rattn::launch_split_kv(a, plan.waves, fp8, plan.ws, plan.rt, stream, ev ? ev[0] : nullptr,
                              ev ? ev[1] : nullptr) != 0)
     return RATTN_E_HIP;
   if (needs_combine(plan) &&
@@ -239,11 +241,12 @@ rattn_status device_shape(int dev, const rattn_problem& p, int32_t* cus, int32_t
   if (dev < 0 || dev >= 64) return RATTN_E_HIP;
   const int G = p.num_q_heads / p.num_kv_heads;
   const bool prefill = (int64_t)G * p.n_query_rows > rattn::kMaxRows;
-  const int waves = prefill ? 0 : rattn::waves_for(G, p.n_query_rows);
+  const int rt = prefill ? 1 : rattn::row_tiles_for(p);
+  const int waves = prefill ? 0 : rt > 1 ? 1 : rattn::waves_for(G, p.n_query_rows);
   const bool fp8 = p.kv_dtype == RATTN_KV_FP8_E4M3;
   const bool even = rattn::uses_even_shares(p);
-  const int key = (waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0) * 4 +
-                  (fp8 ? 2 : 0) + (even ? 1 : 0);
+  const int shape = rt > 1 ? 2 + rt : (waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0);
+  const int key = shape * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);
   std::lock_guard<std::mutex> lock(g_shape_mutex);
   DeviceShape& ds = g_shapes[dev];
   if (ds.cus == 0 &&
@@ -257,7 +260,7 @@ rattn_status device_shape(int dev, const rattn_problem& p, int32_t* cus, int32_t
     return RATTN_OK;
   }
   if (ds.blocks_per_cu[key] == 0) {
-    const int b = rattn::split_kv_blocks_per_cu(waves, fp8, even);
+    const int b = rattn::split_kv_blocks_per_cu(waves, fp8, even, rt);
     ds.blocks_per_cu[key] = b >= 1 ? b : rattn::kDefaultBlocksPerCU;
   }
   *bpc = ds.blocks_per_cu[key];

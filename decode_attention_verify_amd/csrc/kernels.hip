@@ -25,16 +25,17 @@ namespace rattn {
 // ---------------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------------
-// variant index: waves per piece (1, 2, 4, 8), KV format, partition; single-wave pieces
-// also in merging groups of kMergeWaves
+// variant index: waves per piece (1, 2, 4, 8) or row tiles of a one-wave piece (3),
+// KV format, partition; single-wave pieces also in merging groups of kMergeWaves
 #define RATTN_VARIANTS(X)                                                               \
-  X(1, false, false) X(1, true, false) X(2, false, false) X(2, true, false)              \
-  X(4, false, false) X(4, true, false) X(8, false, false) X(8, true, false)              \
-  X(1, false, true) X(1, true, true) X(2, false, true) X(2, true, true)                 \
-  X(4, false, true) X(4, true, true) X(8, false, true) X(8, true, true)
+  X(1, false, false, 1) X(1, true, false, 1) X(2, false, false, 1) X(2, true, false, 1)  \
+  X(4, false, false, 1) X(4, true, false, 1) X(8, false, false, 1) X(8, true, false, 1)  \
+  X(1, false, true, 1) X(1, true, true, 1) X(2, false, true, 1) X(2, true, true, 1)      \
+  X(4, false, true, 1) X(4, true, true, 1) X(8, false, true, 1) X(8, true, true, 1)      \
+  X(1, false, false, 3) X(1, false, true, 3)
 
-static int variant_key(int waves, bool fp8, bool even) {
-  return waves * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);
+static int variant_key(int waves, bool fp8, bool even, int rt) {
+  return (rt * 16 + waves) * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);
 }
 
 // A launch on `stream`; with events, through hipExtLaunchKernel, which stamps them with
@@ -54,37 +55,39 @@ static int launch(Kernel kernel, dim3 grid, dim3 block, void* stream, const Args
                                  (hipEvent_t)ev_start, (hipEvent_t)ev_stop, 0);
 }
 
-int launch_split_kv(const KernelArgs& a, int waves, bool fp8, int ws, void* stream,
+int launch_split_kv(const KernelArgs& a, int waves, bool fp8, int ws, int rt, void* stream,
                     void* ev_start, void* ev_stop) {
   const dim3 grid((unsigned)a.split_groups);
   if (ws > 1) {
-    if (waves != 1 || fp8 || a.splits_per_unit != ws) return (int)hipErrorInvalidValue;
+    if (waves != 1 || fp8 || rt != 1 || a.splits_per_unit != ws) return (int)hipErrorInvalidValue;
     if (ws == 2)
-      return launch(split_kv_kernel<1, false, false, 2>, grid, dim3(128), stream, a, ev_start,
+      return launch(split_kv_kernel<1, false, false, 2, 1>, grid, dim3(128), stream, a, ev_start,
                     ev_stop);
     if (ws == 3)
-      return launch(split_kv_kernel<1, false, false, 3>, grid, dim3(192), stream, a, ev_start,
+      return launch(split_kv_kernel<1, false, false, 3, 1>, grid, dim3(192), stream, a, ev_start,
                     ev_stop);
     return (int)hipErrorInvalidValue;
   }
   if (ws != 1) return (int)hipErrorInvalidValue;
-  const int key = variant_key(waves, fp8, a.splits_per_unit == 0);
-#define RATTN_LAUNCH(WRV, F8, EV)                                                    \
-  if (key == variant_key(WRV, F8, EV))                                               \
-    return launch(split_kv_kernel<WRV, F8, EV, 1>, grid, dim3(64 * WRV), stream, a, ev_start, \
-                  ev_stop);
+  const int key = variant_key(waves, fp8, a.splits_per_unit == 0, rt);
+#define RATTN_LAUNCH(WRV, F8, EV, RTV)                                               \
+  if (key == variant_key(WRV, F8, EV, RTV))                                          \
+    return launch(split_kv_kernel<WRV, F8, EV, 1, RTV>, grid, dim3(64 * WRV), stream, a,  \
+                  ev_start, ev_stop);
   RATTN_VARIANTS(RATTN_LAUNCH)
 #undef RATTN_LAUNCH
   return (int)hipErrorInvalidValue;
 }
 
-int split_kv_blocks_per_cu(int waves, bool fp8, bool even) {
-  const int key = variant_key(waves, fp8, even);
+int split_kv_blocks_per_cu(int waves, bool fp8, bool even, int rt) {
+  const int key = variant_key(waves, fp8, even, rt);
   int nb = 0;
-#define RATTN_OCC(WRV, F8, EV)                                                          \
-  if (key == variant_key(WRV, F8, EV)) {                                                \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kv_kernel<WRV, F8, EV, 1>, \
-                                                        64 * WRV, 0) == hipSuccess ? nb : 0; \
+#define RATTN_OCC(WRV, F8, EV, RTV)                                                     \
+  if (key == variant_key(WRV, F8, EV, RTV)) {                                           \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                               \
+               &nb, split_kv_kernel<WRV, F8, EV, 1, RTV>, 64 * WRV, 0) == hipSuccess     \
+               ? nb                                                                     \
+               : 0;                                                                     \
   }
   RATTN_VARIANTS(RATTN_OCC)
 #undef RATTN_OCC

@@ -85,6 +85,7 @@ static Plan make_prefill_plan(const rattn_problem& p, int32_t num_cus, int32_t b
   pl.prefill = 1;
   pl.prefill_hw = prefill_heads_per_wave(G);
   pl.ws = 1;
+  pl.rt = 1;
   pl.waves = kPrefillWaves;
   pl.num_cus = num_cus;
   pl.blocks_per_cu = blocks_per_cu;
@@ -103,7 +104,8 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int32_t rows = G * p.n_query_rows;
   if (rows > kMaxRows) return make_prefill_plan(p, num_cus, blocks_per_cu);
   Plan pl{};
-  pl.waves = waves_for(G, p.n_query_rows);
+  pl.rt = row_tiles_for(p);
+  pl.waves = pl.rt > 1 ? 1 : waves_for(G, p.n_query_rows);
   pl.num_cus = num_cus;
   pl.blocks_per_cu = blocks_per_cu;
   const int64_t units = (int64_t)p.batch * p.num_kv_heads;
@@ -128,7 +130,7 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   // 30.7 us in two pieces, 7 us of it the merge; the 8-row verify over W = 1024 on
   // 48q/8kv has 128 units and is fastest in four pieces, 30.2 us against 32.3 in two).
   const int64_t slots = (int64_t)std::max(num_cus, 1) * std::max(blocks_per_cu, 1);
-  const bool latency_bound = pl.waves > 1 || p.kv_dtype == RATTN_KV_FP8_E4M3;
+  const bool latency_bound = pl.waves > 1 || pl.rt > 1 || p.kv_dtype == RATTN_KV_FP8_E4M3;
   const int64_t target = std::max<int64_t>(1, latency_bound ? slots : slots * 3 / 4);
   int64_t k = 0;                             // pieces per unit; 0 = even shares
   int64_t groups;
@@ -139,7 +141,9 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
     // every unit spans about the same keys (a window, or a single sequence): an equal
     // number of pieces per unit is balanced and needs no search for a work-group's unit
     k = std::max<int64_t>(1, std::min<int64_t>(target / units, tiles));
-    if (pl.waves > 1 && units * pl.waves >= 4 * (int64_t)std::max(num_cus, 1)) k = 1;
+    if (pl.waves * pl.rt > 1 &&
+        units * pl.waves * pl.rt >= 4 * (int64_t)std::max(num_cus, 1))
+      k = 1;
     k = std::min<int64_t>(k, std::max<int64_t>(1, kMaxGroups / units));
     groups = k * units;
   } else {
@@ -159,7 +163,7 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   // per unit the combine stays faster (48q/8kv window layer, batch 16: 19.6 us against
   // 20.6-21.0 at 3 merged). A forced split of 2 or 3 pieces merges the same way.
   pl.ws = 1;
-  if (pl.waves == 1 && p.kv_dtype == RATTN_KV_BF16 && k >= 1) {   // per-unit splits
+  if (pl.waves == 1 && pl.rt == 1 && p.kv_dtype == RATTN_KV_BF16 && k >= 1) {   // per-unit
     int64_t w = 1;
     if (p.num_splits > 0) {
       w = (k == 2 || k == kMergeWaves) ? k : 1;

@@ -11,7 +11,9 @@
 //  * one work-group of 1, 2, 4 or 8 waves per piece of a (sequence, KV head) unit; the
 //    G*n packed query rows (G = Hq/Hkv) go to 16-row MFMA tiles, one per wave (6 rows pad
 //    to 16 here, not to 64 as in the pages' Blackwell tile; the 72 rows of a 9-token step
-//    on 8-head groups take 8 waves of 9 rows);
+//    on 8-head groups take 8 waves of 9 rows); or one wave holding RT 16-row tiles, which
+//    reads each K and V fragment from LDS once for all of them (the 48 rows of an 8-row
+//    verify: 3 tiles, no padding, no barrier);
 //  * K and V tiles of 32 keys are read with non-temporal 16-byte loads in row order (a
 //    16-lane pass reads 256 contiguous bytes), two tiles in flight, and stored to LDS
 //    with XOR-swizzled 16-byte chunks; page ids are staged in LDS per chunk of pages;
@@ -54,10 +56,18 @@ namespace rattn {
 // holds WS waves, each attending a piece of its own exactly as a single-wave work-group
 // would; the waves then merge their pieces through LDS into the unit's output, so that
 // no combine launch follows (see the epilogue).
-template <int WR, bool FP8, bool EVEN, int WS>
+//
+// RT > 1 (one wave, WR = 1): the wave holds RT 16-row MFMA tiles of the unit's packed
+// rows. Each K fragment and V^T fragment it reads from LDS feeds RT matrix instructions;
+// the queries and the tile's sheared bias slice are staged in LDS. The O accumulators
+// (32 registers per row tile) leave the arithmetic registers to the tiles in flight, so
+// the wave runs alone on its SIMD with the full register file.
+template <int WR, bool FP8, bool EVEN, int WS, int RT>
 __global__ __launch_bounds__(64 * WR * WS)
-__attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kernel(KernelArgs a) {
+__attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void split_kv_kernel(
+    KernelArgs a) {
   static_assert(WS == 1 || (WR == 1 && !FP8 && !EVEN), "merging work-groups: bf16 pieces");
+  static_assert(RT == 1 || (WR == 1 && WS == 1), "row tiles of one wave: a one-wave group");
   constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
   // per wave of a merging work-group (WS > 1): its own tile buffer and page ids
   __shared__ __attribute__((aligned(16))) unsigned char klds[WS * TILE_BUFS][kTileKeys * 256];
@@ -65,13 +75,18 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   __shared__ int pages_lds[WS][kChunkPages + 1];
   // E4M3: a tile's 32 K and 32 V scales, staged beside the tile
   __shared__ __attribute__((aligned(16))) float scale_lds[FP8 ? TILE_BUFS : 1][FP8 ? 64 : 1];
-  // Several waves load the bias slice of a tile together and share it through LDS; a
-  // single wave reads its row's entries one tile ahead in registers, which keeps the
-  // read off each tile's critical path. Both the buffer count and every index into the
-  // buffers derive from STAGE_BIAS (two buffers exactly when several waves share one).
-  constexpr bool STAGE_BIAS = WR > 1;
-  constexpr int BIAS_BUFS = STAGE_BIAS ? 2 : 1;
-  __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? 64 * WR * kBiasPerThread : 1];
+  // Several waves load the bias slice of a tile together and share it through LDS, and
+  // so does a wave of several row tiles; a wave of one row tile reads its row's entries
+  // one tile ahead in registers, which keeps the read off each tile's critical path.
+  // Both the buffer count and every index into the buffers derive from STAGE_BIAS and
+  // WR (two buffers exactly when several waves share one).
+  constexpr bool STAGE_BIAS = WR > 1 || RT > 1;
+  constexpr int BIAS_BUFS = WR > 1 ? 2 : 1;
+  constexpr int BPT = RT > 1 ? kBiasPerThreadRows : kBiasPerThread;   // slice loads per lane
+  __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? 64 * WR * BPT : 1];
+  // RT > 1: the queries of the wave's RT * 16 rows, row i's 16-byte chunk c at
+  // klds_off(i, c) (the B operand reads of one instruction hit distinct banks)
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[RT > 1 ? RT * 16 * 256 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -99,11 +114,18 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     t_end = (wg + 1) * T / P;
   }
 
-  // ---- this wave's query row (row rho of the unit's packed rows) ----
-  const int rho = wave * rpw + lr;
-  const bool row_ok = lr < rpw && rho < R;
-  const int r_of_row = row_ok ? rho / G : 0;
-  const int hl_of_row = row_ok ? rho - r_of_row * G : 0;
+  // ---- this lane's query row in each of the wave's row tiles (row rho[t] of the unit's
+  // packed rows): with one tile per wave, the wave's share of rpw rows; with RT tiles,
+  // rows 16 t + lr ----
+  int rho[RT], r_of_row[RT], hl_of_row[RT];
+  bool row_ok[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    rho[t] = RT == 1 ? wave * rpw + lr : 16 * t + lr;
+    row_ok[t] = (RT > 1 || lr < rpw) && rho[t] < R;
+    r_of_row[t] = row_ok[t] ? rho[t] / G : 0;
+    hl_of_row[t] = row_ok[t] ? rho[t] - r_of_row[t] * G : 0;
+  }
 
   // ---- per-tile registers: this wave's share of the tile's 16-byte loads ----
   constexpr int SLOTS = FP8 ? 8 : 16;        // 16-byte loads per lane for one whole tile
@@ -111,9 +133,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
   struct Tile {
     u32x4_t x[NSLOT];
     float sc;    // E4M3: lane l's scale, of key l (K) or key l - 32 (V) of the tile
-    // multi-wave groups: this thread's elements of the tile's bias slice; one wave:
-    // the bias of its row for keys 4 lq + i of each subtile, gathered directly
-    float bs[STAGE_BIAS ? kBiasPerThread : 8];
+    // staged slices: this thread's elements of the tile's bias slice; one wave of one
+    // row tile: the bias of its row for keys 4 lq + i of each subtile, gathered directly
+    float bs[STAGE_BIAS ? BPT : 8];
   };
   constexpr int ROW_BYTES = FP8 ? kHeadDim : 2 * kHeadDim;
   // lane offset within a 16-key subtile block: each 16-lane pass of a load reads 256
@@ -192,7 +214,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         // fewer tiles than splits: an empty piece marks its rows, which the combine
         // skips (a sequence without rows has no tiles and nothing to mark); a wave of a
         // merging work-group attends no tile and merges an empty piece (l = 0)
-        if (row_ok && r_of_row < sg.nb) a.part_lse[prow0 + rho] = kNegInf;
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          if (row_ok[t] && r_of_row[t] < sg.nb) a.part_lse[prow0 + rho[t]] = kNegInf;
         return;
       }
     } else {
@@ -223,7 +247,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     const int L = sg.L;
     const int k_lo = sg.k_lo;
     const int nb = sg.nb;                    // this sequence's rows (<= n)
-    const bool row_live = row_ok && r_of_row < nb;
+    bool row_live[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) row_live[t] = row_ok[t] && r_of_row[t] < nb;
     const int row_base = seq_rows(a, b, false).base;
     const int j_begin = sg.base + tile0 * kTileKeys;
     const int j_end = min(sg.base + tile1 * kTileKeys, L);
@@ -239,36 +265,61 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     // clamped to [0, Dmax] (a masked key reads an in-range entry that the mask
     // discards), and every lane then reads its row's entries from LDS.
     const int slice_len = kTileKeys + n - 1;
-    const int slice_elems = G * slice_len;     // <= 64 WR kBiasPerThread (validated)
+    const int slice_elems = G * slice_len;     // <= 64 WR BPT (validated)
     const int nbias = (slice_elems + 64 * WR - 1) / (64 * WR);   // slice loads per thread
     const int sub_lo = k_lo & ~15;           // first 16-key subtile holding a visible key
     const int sub_hi = (L - 1) & ~15;        // last subtile holding a key of the sequence
 
-    const int row_h = g * G + hl_of_row;
-    const int row_p = L - nb + r_of_row;
-    bf16x8_t qreg[4];
-    {
+    int row_p[RT], bias_pos[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      row_p[t] = L - nb + r_of_row[t];
+      // this lane's position in its head's slice for key 4 lq of subtile 0
+      bias_pos[t] = hl_of_row[t] * slice_len + 4 * lq + max(nb - 1 - r_of_row[t], 0);
+    }
+    const int row_h = g * G + hl_of_row[0];
+    bf16x8_t qreg[RT == 1 ? 4 : 1];
+    if constexpr (RT == 1) {
       const uint16_t* qrow =
-          a.q + ((int64_t)(row_base + r_of_row) * a.num_q_heads + row_h) * kHeadDim;
+          a.q + ((int64_t)(row_base + r_of_row[0]) * a.num_q_heads + row_h) * kHeadDim;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         // the K operand of MFMA s gives lane (lr, lq) the dims 32 s + 8 lq .. + 7
-        const u32x4_t v = row_live ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
+        const u32x4_t v = row_live[0] ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
         qreg[s] = __builtin_bit_cast(bf16x8_t, v);
       }
+    } else {
+      // the unit's queries into LDS: 16 lanes read one 256-byte row, four rows per pass.
+      // Every load is issued before the first store (a row the sequence lacks reads its
+      // first row and stores zeros), so that they share one memory round trip.
+      u32x4_t qv[4 * RT];
+      bool qlive[4 * RT];
+#pragma unroll
+      for (int k = 0; k < 4 * RT; ++k) {
+        const int i = 4 * k + lq;                    // packed row
+        const int r = i / G;
+        qlive[k] = i < R && r < nb;
+        const int rr = qlive[k] ? r : 0, hh = qlive[k] ? i - r * G : 0;
+        qv[k] = ld16(a.q + ((int64_t)(row_base + rr) * a.num_q_heads + g * G + hh) * kHeadDim +
+                     8 * lr);
+      }
+#pragma unroll
+      for (int k = 0; k < 4 * RT; ++k) {
+        const unsigned keep = qlive[k] ? ~0u : 0u;
+        *reinterpret_cast<u32x4_t*>(q_lds + klds_off(4 * k + lq, lr)) =
+            qv[k] & u32x4_t{keep, keep, keep, keep};
+      }
     }
-    // this lane's position in its head's slice for key 4 lq of subtile 0, and its row's
-    // table offset (for the direct gather)
-    const int bias_pos = hl_of_row * slice_len + 4 * lq + max(nb - 1 - r_of_row, 0);
+    // the row's table offset (for the direct gather of a one-tile wave)
     const int bias_row = row_h * (a.dmax + 1);
     // this thread's slice elements: element e = tid + 64 WR q of the group's slices is
     // position e % slice_len of head e / slice_len; bs_row is that head's table offset
     // (-1: no element), bs_pos the position
-    int bs_row[kBiasPerThread], bs_pos[kBiasPerThread];
+    int bs_row[BPT], bs_pos[BPT];
     {
       const int tid = wave * 64 + lane;
 #pragma unroll
-      for (int q = 0; q < kBiasPerThread; ++q) {
+      for (int q = 0; q < BPT; ++q) {
         const int e = tid + 64 * WR * q;
         const int hl = e / slice_len;
         bs_pos[q] = e - hl * slice_len;
@@ -282,17 +333,30 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
     // the loop would make every tile wait for all of its predecessors' K/V loads.
     const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
     int chunk_p0 = 0;
+    // The ids are loaded in batches of up to four per thread, each batch issued before
+    // its first id is checked (an index past the chunk re-reads its last id), so that a
+    // batch costs one memory round trip.
+    constexpr int PAGE_BATCH = 4;
     auto stage_pages = [&](int c0, int c1) {
       if (WR > 1) __syncthreads();           // the previous chunk's ids and tiles are done
       chunk_p0 = c0 >> a.page_shift;
       const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
-      for (int i = WS > 1 ? lane : (int)threadIdx.x; i < np; i += 64 * WR) {
-        int ph = pt_row[chunk_p0 + i];
-        if (ph < 0 || ph >= a.num_pages) {
-          atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
-          ph = min(max(ph, 0), a.num_pages - 1);
+      const int tid = WS > 1 ? lane : (int)threadIdx.x;
+      for (int i0 = 0; i0 < np; i0 += 64 * WR * PAGE_BATCH) {   // uniform
+        int ids[PAGE_BATCH];
+#pragma unroll
+        for (int k = 0; k < PAGE_BATCH; ++k)
+          ids[k] = pt_row[chunk_p0 + min(i0 + tid + 64 * WR * k, np - 1)];
+#pragma unroll
+        for (int k = 0; k < PAGE_BATCH; ++k) {
+          const int i = i0 + tid + 64 * WR * k;
+          int ph = ids[k];
+          if (ph < 0 || ph >= a.num_pages) {
+            atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
+            ph = min(max(ph, 0), a.num_pages - 1);
+          }
+          if (i < np) pages_lds[wsi][i] = ph;
         }
-        pages_lds[wsi][i] = ph;
       }
       if (WR > 1) __syncthreads();
     };
@@ -312,7 +376,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         // 8-row verify workload reads 1.04x its algorithmic bytes this way, 1.08x with
         // non-temporal loads)
 #pragma unroll
-        for (int q = 0; q < kBiasPerThread; ++q) {
+        for (int q = 0; q < BPT; ++q) {
           if (q > 0 && q >= nbias) break;   // uniform
           const int d = min(max(L - 1 - j0 - bs_pos[q], 0), a.dmax);
           X.bs[q] = a.bias[bs_row[q] >= 0 ? (unsigned)(bs_row[q] + d) : 0u];
@@ -346,7 +410,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         // vector-memory instructions), else one by one with the distances clamped
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const int d0 = row_p - (j0 + 16 * kt + 4 * lq);
+          const int d0 = row_p[0] - (j0 + 16 * kt + 4 * lq);
           if (d0 >= 3 && d0 <= a.dmax) {
             const f32x4_t v = ldf4u_stream(a.bias + (unsigned)(bias_row + d0 - 3));
 #pragma unroll
@@ -362,13 +426,21 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       }
     };
 
-    // ---- running state of this lane's row ----
-    f32x4_t o[8];
-    float m_run = kNegInf, l_run = 0.f;
+    // ---- running state of this lane's row in each row tile ----
+    f32x4_t o[RT][8];
+    float m_run[RT], l_run[RT];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0, 0, 0, 0};
+    for (int t = 0; t < RT; ++t) {
+      m_run[t] = kNegInf;
+      l_run[t] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4_t{0, 0, 0, 0};
+    }
 
-    auto process_tile = [&](const Tile& X, int j0, int buf) {
+    // A tile is attended in two steps: its registers are stored to LDS (stage_tile), then
+    // the wave computes from LDS (attend_tile); between the two the registers are free
+    // for the next tile's loads.
+    auto stage_tile = [&](const Tile& X, int j0, int buf) {
       const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
       // a single wave reuses one LDS buffer (its LDS accesses execute in order); several
       // waves alternate two, so that one barrier per tile separates writes from reads
@@ -378,7 +450,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       if constexpr (STAGE_BIAS) {
         const int tid = wave * 64 + lane;
 #pragma unroll
-        for (int q = 0; q < kBiasPerThread; ++q) {
+        for (int q = 0; q < BPT; ++q) {
           if (q > 0 && q >= nbias) break;   // uniform
           bl[tid + 64 * WR * q] = X.bs[q];   // in the buffer; past the slice: unread
         }
@@ -430,31 +502,48 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       float* sl = scale_lds[FP8 && TILE_BUFS == 2 ? buf : 0];
       if (FP8 && wave == 0) sl[lane] = X.sc;
       if (WR > 1) __syncthreads();            // the whole tile is in LDS buffer `buf`
+    };
+
+    auto attend_tile = [&](const Tile& X, int j0, int buf) {
+      const bool fast = (j0 >= fast_lo) && (j0 <= fast_hi);   // uniform
+      const unsigned char* kl = klds[wsi * TILE_BUFS + (TILE_BUFS == 2 ? buf : 0)];
+      const unsigned char* vl = vlds[wsi * TILE_BUFS + (TILE_BUFS == 2 ? buf : 0)];
+      const float* bl = bias_lds[BIAS_BUFS == 2 ? buf : 0];
+      const float* sl = scale_lds[FP8 && TILE_BUFS == 2 ? buf : 0];
+      (void)bl;
+      (void)sl;
 
       // S^T = K Q^T : lane (lr, lq) of MFMA s reads key 16 kt + lr, dims 32 s + 8 lq ..;
-      // the result gives lane (lr, lq) row lr and keys 4 lq + i of each 16-key subtile
-      f32x4_t sacc[2];
+      // the result gives lane (lr, lq) row lr and keys 4 lq + i of each 16-key subtile.
+      // Each K fragment feeds the MFMAs of all the wave's row tiles.
+      f32x4_t sacc[RT][2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x4_t acc = {0, 0, 0, 0};
+      for (int t = 0; t < RT; ++t) sacc[t][0] = sacc[t][1] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_t kop = __builtin_bit_cast(
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t kop[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          kop[kt] = __builtin_bit_cast(
               bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          bf16x8_t qop;
+          if constexpr (RT == 1) qop = qreg[s];
+          else
+            qop = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(q_lds + klds_off(16 * t + lr, 4 * s + lq)));
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            sacc[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kt], qop, sacc[t][kt], 0, 0, 0);
         }
-        sacc[kt] = acc;
       }
 
-      // the bias of this lane's row for its keys 4 lq + i of each subtile
-      float bv[2][4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (STAGE_BIAS) bv[kt][i] = bl[bias_pos + 16 * kt + i];
-          else bv[kt][i] = X.bs[4 * kt + i];
-        }
+      // Several row tiles: the scheduler may not move the work of one phase (logits,
+      // softmax, PV) into another, so that each phase's temporaries die before the next
+      // one's are made (with the full register file of a lone wave it otherwise hoists
+      // the V^T reads and the next tile's work until the accumulators spill).
+      if constexpr (RT > 1) __builtin_amdgcn_sched_barrier(0);
 
       // E4M3: the scales of this lane's keys 4 lq + i of each subtile
       f32x4_t ks[2], vs[2];
@@ -466,58 +555,75 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
         }
       }
 
-      // logits, mask, online softmax; P packed as the B operand of O^T += V^T P^T
-      float sv[2][4];
-      float mt = kNegInf;
+      // per row tile: bias, logits, mask, online softmax; P packed as the B operand of
+      // O^T += V^T P^T
+      bf16x8_t pop[RT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int t = 0; t < RT; ++t) {
+        // the bias of this lane's row for its keys 4 lq + i of each subtile
+        float bv[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float scl = FP8 ? a.softmax_scale * ks[kt][i] : a.softmax_scale;
-          float sc = __builtin_fmaf(sacc[kt][i], scl, bv[kt][i]);
-          if (!fast) {
-            const int dist = row_p - (j0 + 16 * kt + 4 * lq + i);
-            const bool vis = row_live && dist >= 0 && (W == 0 || dist < W);
-            sc = vis ? sc : kNegInf;
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (STAGE_BIAS) bv[kt][i] = bl[bias_pos[t] + 16 * kt + i];
+            else bv[kt][i] = X.bs[4 * kt + i];
           }
-          sv[kt][i] = sc;
-          mt = fmaxf(mt, sc);
+        float sv[2][4];
+        float mt = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float scl = FP8 ? a.softmax_scale * ks[kt][i] : a.softmax_scale;
+            float sc = __builtin_fmaf(sacc[t][kt][i], scl, bv[kt][i]);
+            if (!fast) {
+              const int dist = row_p[t] - (j0 + 16 * kt + 4 * lq + i);
+              const bool vis = row_live[t] && dist >= 0 && (W == 0 || dist < W);
+              sc = vis ? sc : kNegInf;
+            }
+            sv[kt][i] = sc;
+            mt = fmaxf(mt, sc);
+          }
         }
-      }
-      mt = wave_max_rows(mt);
-      // The reference point m of a row moves only when the tile's maximum exceeds it by
-      // more than kRescaleSlack, so that the accumulators are rescaled on few tiles;
-      // p = exp(s - m) then stays below exp(kRescaleSlack). O and l share m, so the
-      // quotient O / l and lse = m + ln l are unchanged by the choice of m.
-      const bool grow = mt > m_run + kRescaleSlack;      // false while mt = -inf
-      if (__ballot(grow) != 0) {                         // wave-uniform
-        const float m_new = grow ? mt : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
-        l_run *= alpha;
+        mt = wave_max_rows(mt);
+        // The reference point m of a row moves only when the tile's maximum exceeds it
+        // by more than kRescaleSlack, so that the accumulators are rescaled on few
+        // tiles; p = exp(s - m) then stays below exp(kRescaleSlack). O and l share m, so
+        // the quotient O / l and lse = m + ln l are unchanged by the choice of m.
+        const bool grow = mt > m_run[t] + kRescaleSlack;   // false while mt = -inf
+        if (__ballot(grow) != 0) {                         // wave-uniform
+          const float m_new = grow ? mt : m_run[t];
+          const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[t] - m_new) * kLog2e) : 1.f;
+          l_run[t] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float mb = -(m_run == kNegInf ? 0.f : m_run) * kLog2e;
-      float psum = 0.f;
-      float pv[2][4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][i], kLog2e, mb));
-          psum += p;
-          pv[kt][i] = FP8 ? (p > 0.f ? p * vs[kt][i] : 0.f) : p;
+          for (int dt = 0; dt < 8; ++dt) o[t][dt] *= alpha;
+          m_run[t] = m_new;
         }
+        const float mb = -(m_run[t] == kNegInf ? 0.f : m_run[t]) * kLog2e;
+        float psum = 0.f;
+        float pv[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kt][i], kLog2e, mb));
+            psum += p;
+            pv[kt][i] = FP8 ? (p > 0.f ? p * vs[kt][i] : 0.f) : p;
+          }
+        }
+        l_run[t] += psum;
+        const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                            pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+        pop[t] = __builtin_bit_cast(bf16x8_t, pk);
       }
-      l_run += psum;
-      const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                          pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pk);
+
+      if constexpr (RT > 1) __builtin_amdgcn_sched_barrier(0);
 
       // O^T += V^T P^T : V^T operand by transpose reads of the LDS tile. Lane (lr, lq)
       // supplies the address of 4 dims of key 16 e + 4 lq + lr/4; the read returns to
-      // lane lr the dim 16 dt + lr of keys 16 e + 4 lq + 0..3.
+      // lane lr the dim 16 dt + lr of keys 16 e + 4 lq + 0..3. Each V^T fragment feeds
+      // the MFMAs of all the wave's row tiles.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int cc = 2 * dt + ((lr & 3) >> 1);
@@ -530,14 +636,39 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
             (i16x4_t __attribute__((address_space(3)))*)(vl + off1));
         const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
         const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, o[dt], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], o[t][dt], 0, 0, 0);
       }
     };
 
-    // ---- tile loop: two tiles in flight, chunks of at most kChunkPages pages ----
+    auto process_tile = [&](const Tile& X, int j0, int buf) {
+      stage_tile(X, j0, buf);
+      attend_tile(X, j0, buf);
+    };
+
+    // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave: two
+    // tiles in flight in registers. Several row tiles (their accumulators take the
+    // registers): one, whose loads are issued as soon as the tile before it is in LDS,
+    // so that they are in flight while the wave attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
+    if constexpr (RT > 1) {
+      Tile A;
+      for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+        const int c1 = min(c0 + chunk_keys, j_end);
+        stage_pages(c0, c1);
+        const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+        load_tile(A, c0);
+        for (int i = 0; i < nt; ++i) {
+          const int j0 = c0 + i * kTileKeys;
+          stage_tile(A, j0, 0);
+          if (i + 1 < nt) load_tile(A, j0 + kTileKeys);
+          attend_tile(A, j0, 0);
+        }
+      }
+    }
     Tile A, B;
-    for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+    for (int c0 = j_begin; RT == 1 && c0 < j_end; c0 += chunk_keys) {
       const int c1 = min(c0 + chunk_keys, j_end);
       stage_pages(c0, c1);
       const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
@@ -560,31 +691,34 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && !FP8 ? 1 : 2))) void split_kv_kern
       }
     }
 
-    // ---- epilogue: the final row when the piece is the whole unit, else a partial ----
-    const float l = wave_sum_rows(l_run);
+    // ---- epilogue: the final rows when the piece is the whole unit, else partials ----
     if constexpr (WS > 1) {
-      merge_group(b, g, l, m_run, o);
+      merge_group(b, g, wave_sum_rows(l_run[0]), m_run[0], o[0]);
       return;
     }
-    if (row_live) {
-      const int64_t row = (int64_t)(row_base + r_of_row) * a.num_q_heads + row_h;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const float l = wave_sum_rows(l_run[t]);
+      if (!row_live[t]) continue;
+      const int64_t row =
+          (int64_t)(row_base + r_of_row[t]) * a.num_q_heads + g * G + hl_of_row[t];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      const float lse = l > 0.f ? m_run + __logf(l) : kNegInf;
+      const float lse = l > 0.f ? m_run[t] + __logf(l) : kNegInf;
       if (whole) {
         uint16_t* op = a.out + row * kHeadDim;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const f32x4_t v = o[dt] * inv;
+          const f32x4_t v = o[t][dt] * inv;
           const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2_t*>(op + 16 * dt + 4 * lq) = w;
         }
         if (lq == 0 && a.lse != nullptr) a.lse[row] = lse;
       } else {
-        const int64_t prow = prow0 + rho;
+        const int64_t prow = prow0 + rho[t];
         float* pp = a.part_o + prow * kHeadDim;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * lq) = o[dt] * inv;
+          *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * lq) = o[t][dt] * inv;
         if (lq == 0) a.part_lse[prow] = lse;
       }
     }

@@ -117,8 +117,8 @@ typedef struct {
   int32_t num_splits;        /* pieces (key ranges) per (sequence, KV head), nominal      */
   int32_t keys_per_split;    /* keys per piece at max_seq_len, nominal                    */
   int32_t tile_keys;         /* keys per inner-loop step                                  */
-  int32_t row_tiles;         /* waves per piece (split: 1, 2, 4 or 8, one 16-row MFMA     */
-                             /* tile each; prefill: 8 per work-group)                     */
+  int32_t row_tiles;         /* waves per piece (split: 1, 2, 4 or 8, each with          */
+                             /* tiles_per_wave 16-row MFMA tiles; prefill: 8 per group)   */
   int32_t grid_x, grid_y, grid_z;   /* split kernel grid: (work-groups, 1, 1)             */
   int32_t combine_blocks;    /* combine work-groups; 0 when nothing is merged after the   */
                              /* split kernel                                              */
@@ -129,6 +129,9 @@ typedef struct {
                              /* when a unit is that many single-wave pieces, which one   */
                              /* work-group attends and merges (no combine launch)        */
   int64_t workspace_bytes;   /* partial outputs and log-sum-exps, and a flag word         */
+  int32_t tiles_per_wave;    /* 16-row MFMA tiles per split wave: 1, or 3 when one wave    */
+                             /* holds all 33-48 packed rows of a piece (full-context      */
+                             /* layers over a bf16 cache)                                 */
 } rattn_plan_info;
 
 /* rattn_plan_info.kernel. Up to 128 packed rows per (sequence, KV head) (G * n, G =

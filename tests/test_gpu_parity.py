@@ -103,6 +103,23 @@ def test_eight_wave_groups(hq, hkv, n, W, splits, batch, fmt):
     assert info["row_tiles"] == 8
 
 
+# ------- 33 to 48 packed rows over long spans: one wave holding three 16-row tiles
+
+@pytest.mark.parametrize("n,batch,splits,dmax,lens", [
+    (8, 12, 0, 3000, ("uniform", 8, 2000)),     # even shares over mixed lengths
+    (6, 1, 7, 4000, 3000),                      # 36 rows, 7 pieces per unit
+    (7, 3, 0, 37, ("uniform", 7, 1500)),        # 42 rows, the Dmax clamp
+    (8, 2, 200, 3000, ("uniform", 8, 2500)),    # pieces without keys
+])
+def test_three_row_tiles_per_wave(n, batch, splits, dmax, lens):
+    # the planning bound (max_seq_len = 9,000) picks the one-wave layout; the sequences
+    # themselves stay short so that the oracle checks every row
+    sp = small("full_100k", batch=batch, n_rows=n, seq_len=lens, dmax=dmax, max_seq_len=9000,
+               name="rows3")
+    _, _, info = check_case(sp, seed=n + batch + splits, num_splits=splits, poison=dmax > 37)
+    assert info["row_tiles"] == 1 and info["tiles_per_wave"] == 3
+
+
 # ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
 
 @pytest.mark.parametrize("name", ["tp4_100k", "tp8_100k"])

@@ -136,6 +136,16 @@ def test_bad_row_ranges_are_flagged():
     assert bool(torch.isnan(lse[2:6].cpu()).all()) and bool(torch.isnan(out[2:6].float()).all())
 
 
+@pytest.mark.parametrize("splits", [0, 5])
+def test_rows_three_row_tiles(splits):
+    # 1..8 rows of 6-head groups under a long planning bound: one wave of three row
+    # tiles per piece, rows past a sequence's own count left out
+    sp = small("full_100k", batch=9, n_rows=8, seq_len=("uniform", 8, 2500), dmax=3000,
+               max_seq_len=9000, name="varlen_rows3")
+    rows = synth.draw_rows_per_seq(9, 8, seed=21 + splits)
+    check_varlen(sp, rows, seed=21 + splits, num_splits=splits)
+
+
 @pytest.mark.parametrize("fmt", [synth.KV_BF16, synth.KV_FP8])
 def test_mtp_rows_gqa8_full(fmt):
     # the previous generation's full layers (64q/8kv) with 1..9 tokens per sequence: up
