@@ -163,7 +163,10 @@ int launch_split_kv(const KernelArgs& a, int waves, bool fp8, int ws, int rt, vo
                     void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_combine(const KernelArgs& a, void* stream, void* ev_start = nullptr,
                    void* ev_stop = nullptr);
-// Work-groups of the combine launch for `rows` output rows (host function).
+// The combine kernel's shape for `rows` output rows and the partition (planner.cpp),
+// and its work-groups (host functions).
+enum CombineShape { kCombineRows, kCombineRows2, kCombineSlices, kCombineWide, kCombineWide16 };
+CombineShape combine_shape(int64_t rows, int splits_per_unit);
 int64_t combine_blocks(int64_t rows, int splits_per_unit);
 int launch_append_kv(const AppendArgs& a, void* stream);
 

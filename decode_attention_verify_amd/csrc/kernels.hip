@@ -94,38 +94,6 @@ int split_kv_blocks_per_cu(int waves, bool fp8, bool even, int rt) {
   return 0;
 }
 
-// The combine's shape for a partition (see combine_kernel), with what chose it on MI355X:
-//  * per-unit splits of up to 16 pieces: whole rows, 2 stripes of 32 lanes, 4 rows per
-//    work-group, 8 pieces in flight per thread (the window layer at batch 16, 6 pieces
-//    per unit: 18.2 us per call against 19.3 with 1 stripe and 8 rows per work-group);
-//  * even shares (a few to a few tens of pieces per unit): the same, 16 pieces in flight;
-//  * 17 to 255 pieces: one wave per 16-dim slice of a row, 16 stripes of 4 lanes (the
-//    100K-key decode's 96 pieces merge 0.4 us sooner than in 32-dim slices of 8 stripes,
-//    65 pieces 0.7 us sooner; 32 stripes per 8-dim slice were no faster, 64 per 4-dim
-//    slice slower);
-//  * 256 pieces or more: 16 waves per 32-dim slice, 128 stripes of 8 lanes; for a call of
-//    fewer than 32 rows, per 16-dim slice, 256 stripes of 4 lanes, so that the few rows
-//    spread over twice the work-groups (one rank's share of the 100K-key layer under
-//    8-way tensor parallelism, 6 rows of 768 pieces: 0.4 us sooner, under 4-way 0.7 us;
-//    the 1M-key E4M3 decode, 48 rows of 256 pieces, merged 1.2 us later that way).
-enum CombineShape { kCombineRows, kCombineRows2, kCombineSlices, kCombineWide, kCombineWide16 };
-
-static CombineShape combine_shape(int64_t rows, int splits_per_unit) {
-  if (splits_per_unit == 0) return kCombineRows2;
-  if (splits_per_unit <= 16) return kCombineRows;
-  if (splits_per_unit >= 256) return rows < 32 ? kCombineWide16 : kCombineWide;
-  return kCombineSlices;
-}
-
-int64_t combine_blocks(int64_t rows, int splits_per_unit) {
-  switch (combine_shape(rows, splits_per_unit)) {
-    case kCombineRows:
-    case kCombineRows2: return (rows + 3) / 4;
-    case kCombineWide: return rows * 4;   // one work-group per 32-dim slice of a row
-    default: return rows * 8;             // one work-group per 16-dim slice of a row
-  }
-}
-
 int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_stop) {
   const int64_t rows = (int64_t)a.batch * a.n * a.num_q_heads;
   const dim3 grid((unsigned)combine_blocks(rows, a.splits_per_unit));

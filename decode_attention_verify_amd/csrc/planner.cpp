@@ -51,8 +51,11 @@ rattn_status validate_problem(const rattn_problem* p) {
     // over a bf16 cache, without forced splits
     if (prefill_heads_per_wave(G) == 0) return RATTN_E_UNSUPPORTED;
     if (p->kv_dtype != RATTN_KV_BF16 || p->num_splits != 0) return RATTN_E_UNSUPPORTED;
+    // one 8-wave work-group per (sequence, KV head, block of query tokens): the grid's
+    // work-items must stay below 2^31
     const int64_t blocks = (p->n_query_rows + prefill_tokens(G) - 1) / prefill_tokens(G);
-    if ((int64_t)p->batch * p->num_kv_heads * blocks > ((int64_t)1 << 31) - 8)
+    if (((int64_t)p->batch * p->num_kv_heads * blocks + 7) * 64 * kPrefillWaves >=
+        ((int64_t)1 << 31))
       return RATTN_E_UNSUPPORTED;
   } else if (waves_for(G, p->n_query_rows) == 0) {
     // a tile's bias slice (G heads x (32 + n - 1) distances) must fit the work-group's
@@ -68,6 +71,11 @@ rattn_status validate_problem(const rattn_problem* p) {
   // max_seq_len) in 32-bit integers: their sum must stay below 2^31
   const int64_t total = (int64_t)p->batch * p->num_kv_heads * unit_tiles_bound(*p);
   if (total > INT32_MAX) return RATTN_E_UNSUPPORTED;
+  // a split grid holds at least one work-group of up to 8 waves per (sequence, KV head)
+  // unit; its work-items must stay below 2^31
+  if (rows <= kMaxRows &&
+      (int64_t)p->batch * p->num_kv_heads * 64 * kMaxWaves >= ((int64_t)1 << 31))
+    return RATTN_E_UNSUPPORTED;
   return RATTN_OK;
 }
 
@@ -195,6 +203,36 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   bytes = (bytes + 255) / 256 * 256;
   pl.workspace_bytes = bytes + 256;
   return pl;
+}
+
+// The combine's shape for a partition (see combine_kernel), with what chose it on MI355X:
+//  * per-unit splits of up to 16 pieces: whole rows, 2 stripes of 32 lanes, 4 rows per
+//    work-group, 8 pieces in flight per thread (the window layer at batch 16, 6 pieces
+//    per unit: 18.2 us per call against 19.3 with 1 stripe and 8 rows per work-group);
+//  * even shares (a few to a few tens of pieces per unit): the same, 16 pieces in flight;
+//  * 17 to 255 pieces: one wave per 16-dim slice of a row, 16 stripes of 4 lanes (the
+//    100K-key decode's 96 pieces merge 0.4 us sooner than in 32-dim slices of 8 stripes,
+//    65 pieces 0.7 us sooner; 32 stripes per 8-dim slice were no faster, 64 per 4-dim
+//    slice slower);
+//  * 256 pieces or more: 16 waves per 32-dim slice, 128 stripes of 8 lanes; for a call of
+//    fewer than 32 rows, per 16-dim slice, 256 stripes of 4 lanes, so that the few rows
+//    spread over twice the work-groups (one rank's share of the 100K-key layer under
+//    8-way tensor parallelism, 6 rows of 768 pieces: 0.4 us sooner, under 4-way 0.7 us;
+//    the 1M-key E4M3 decode, 48 rows of 256 pieces, merged 1.2 us later that way).
+CombineShape combine_shape(int64_t rows, int splits_per_unit) {
+  if (splits_per_unit == 0) return kCombineRows2;
+  if (splits_per_unit <= 16) return kCombineRows;
+  if (splits_per_unit >= 256) return rows < 32 ? kCombineWide16 : kCombineWide;
+  return kCombineSlices;
+}
+
+int64_t combine_blocks(int64_t rows, int splits_per_unit) {
+  switch (combine_shape(rows, splits_per_unit)) {
+    case kCombineRows:
+    case kCombineRows2: return (rows + 3) / 4;
+    case kCombineWide: return rows * 4;   // one work-group per 32-dim slice of a row
+    default: return rows * 8;             // one work-group per 16-dim slice of a row
+  }
 }
 
 }  // namespace rattn

@@ -49,6 +49,8 @@ UNSUPPORTED = [
     # bf16 cache without forced splits
     dict(n_query_rows=22, kv_dtype=binding.RATTN_KV_FP8_E4M3),
     dict(n_query_rows=100, num_q_heads=24), dict(n_query_rows=100, num_splits=4),
+    # a split grid of 2^31 work-items or more (a work-group of up to 8 waves per unit)
+    dict(batch=1 << 19, max_seq_len=1, max_pages_per_seq=1),
     # the call's tiles are counted in 32-bit integers: 2^31 tiles or more are refused
     dict(batch=256, num_kv_heads=8, num_q_heads=48, max_seq_len=1 << 25,
          max_pages_per_seq=1 << 21, num_pages=1 << 21),
