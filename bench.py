@@ -85,6 +85,9 @@ WORKLOADS = {
     "prefill_8x2k": "chunked prefill: 8 sequences, a chunk of 2048 query tokens each at "
                     "100,000 keys (the chunk included), 48q/8kv, d=128, causal, bf16 paged "
                     "KV (page 16)",
+    "prefill_8x2k_fp8": "chunked prefill: 8 sequences, a chunk of 2048 query tokens each at "
+                        "100,000 keys (the chunk included), 48q/8kv, d=128, causal, E4M3 KV + "
+                        "fp32 per-token-per-head scales, paged (page 64)",
     "verify_b16_varlen": "speculative verify with 1..8 rows per sequence (seeded), 48q/8kv, "
                          "d=128, batch 16, full layer, seq_lens log-uniform [32768,262144], "
                          "bf16 paged KV (page 16)",
@@ -234,7 +237,10 @@ def cpu_baseline_rows(case_cpu, tr, budget_s, block=32):
     a = case_cpu
     sp = a.spec
     n, G = sp.n_rows, sp.num_q_heads // sp.num_kv_heads
-    kc, vc = a.k_cache.view(torch.uint16).numpy(), a.v_cache.view(torch.uint16).numpy()
+    tv = torch.uint16 if a.k_cache.dtype == torch.bfloat16 else torch.uint8
+    kc, vc = a.k_cache.view(tv).numpy(), a.v_cache.view(tv).numpy()
+    ks = None if a.k_scale is None else a.k_scale.numpy()
+    vs = None if a.v_scale is None else a.v_scale.numpy()
     q = a.q.view(torch.uint16).numpy()
     lens = [int(x) for x in a.seq_lens]
     total_work = sum(accounting.rows_keys(L, n, sp.window) for L in lens) * sp.num_kv_heads
@@ -252,7 +258,7 @@ def cpu_baseline_rows(case_cpu, tr, budget_s, block=32):
         o, l = oracle.relative_attention(
             q[b:b + 1, r0:r1], kc, vc, a.page_table[b:b + 1].numpy(), np.array([L_cut]),
             a.bias.numpy(), n_query_rows=r1 - r0, window=sp.window, dmax=sp.dmax,
-            softmax_scale=a.softmax_scale, kv_heads=[g])
+            softmax_scale=a.softmax_scale, k_scale=ks, v_scale=vs, kv_heads=[g])
         hs = slice(g * G, (g + 1) * G)
         out[b, r0:r1, hs] = o[0, :, hs]
         lse[b, r0:r1, hs] = l[0, :, hs]
@@ -611,7 +617,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        # the arithmetic: bf16 matrix operands with fp32 accumulation and softmax (an
+        # E4M3 cache is decoded exactly to bf16; config.kv_cache names the storage)
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": WORKLOADS[args.workload],

@@ -200,7 +200,7 @@ rattn_status decode_call(const rattn_problem& pr, const rattn::Plan& plan, void*
   a.splits_per_unit = plan.splits_per_unit;
 
   if (plan.prefill)
-    return rattn::launch_prefill(a, plan.prefill_hw, a.group, stream, ev ? ev[0] : nullptr,
+    return rattn::launch_prefill(a, plan.prefill_hw, a.group, fp8, stream, ev ? ev[0] : nullptr,
                                  ev ? ev[1] : nullptr) == 0
                ? RATTN_OK
                : RATTN_E_HIP;

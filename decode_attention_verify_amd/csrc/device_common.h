@@ -56,6 +56,13 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// What pack_bf16x2(lo, hi) = `packed` left out, rounded to bf16 in turn: the pair
+// `packed` + this remainder carries lo and hi to about 2^-17 of their size (a P scaled
+// by an E4M3 value scale goes to the matrix units as these two bf16 parts).
+__device__ __forceinline__ unsigned int pack_bf16x2_rem(float lo, float hi, unsigned int packed) {
+  return pack_bf16x2(lo - __uint_as_float(packed << 16), hi - __uint_as_float(packed & 0xffff0000u));
+}
+
 // Four E4M3 codes (one dword) -> four bf16 values (two dwords), in code order. Exact:
 // every E4M3 value, subnormals included, is a bf16 value. v_cvt_scalef32_pk_bf16_fp8
 // (gfx950) converts two codes per instruction (scale 1); checked on MI355X against the

@@ -175,7 +175,7 @@ int launch_append_kv(const AppendArgs& a, void* stream);
 // device (resolved then with hipGetSymbolAddress and kept). Returns 0 or a hipError_t.
 constexpr int64_t kStaticScratchBytes = (int64_t)32 << 20;
 int static_scratch_ptr(int device, void** ptr);
-int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
+int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, bool fp8, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_read_probe(const void* buf, int64_t nblocks, int block_bytes, const int32_t* order,
                       int waves, void* sink, void* stream);

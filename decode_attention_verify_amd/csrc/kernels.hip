@@ -111,15 +111,16 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_s
   }
 }
 
-int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, void* stream,
+int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, bool fp8, void* stream,
                    void* ev_start, void* ev_stop) {
   const dim3 grid((unsigned)a.split_groups), block(64 * kPrefillWaves);
-  if (heads_per_wave == 3 && group == 6)
-    return launch(prefill_kernel<3, 2, kPrefillWaves>, grid, block, stream, a, ev_start, ev_stop);
-  if (heads_per_wave == 2 && group == 4)
-    return launch(prefill_kernel<2, 2, kPrefillWaves>, grid, block, stream, a, ev_start, ev_stop);
-  if (heads_per_wave == 2 && group == 8)
-    return launch(prefill_kernel<2, 4, kPrefillWaves>, grid, block, stream, a, ev_start, ev_stop);
+#define RATTN_PREFILL(HWV, HGV, F8)                                                          \
+  if (heads_per_wave == HWV && group == HWV * HGV && fp8 == F8)                              \
+    return launch(prefill_kernel<HWV, HGV, kPrefillWaves, F8>, grid, block, stream, a,       \
+                  ev_start, ev_stop);
+  RATTN_PREFILL(3, 2, false) RATTN_PREFILL(2, 2, false) RATTN_PREFILL(2, 4, false)
+  RATTN_PREFILL(3, 2, true) RATTN_PREFILL(2, 2, true) RATTN_PREFILL(2, 4, true)
+#undef RATTN_PREFILL
   return (int)hipErrorInvalidValue;
 }
 

@@ -48,9 +48,9 @@ rattn_status validate_problem(const rattn_problem* p) {
   const int64_t rows = (int64_t)G * p->n_query_rows;
   if (rows > kMaxRows) {
     // many rows per sequence: the prefill kernel, for the group sizes it is built for,
-    // over a bf16 cache, without forced splits
+    // without forced splits
     if (prefill_heads_per_wave(G) == 0) return RATTN_E_UNSUPPORTED;
-    if (p->kv_dtype != RATTN_KV_BF16 || p->num_splits != 0) return RATTN_E_UNSUPPORTED;
+    if (p->num_splits != 0) return RATTN_E_UNSUPPORTED;
     // one 8-wave work-group per (sequence, KV head, block of query tokens): the grid's
     // work-items must stay below 2^31
     const int64_t blocks = (p->n_query_rows + prefill_tokens(G) - 1) / prefill_tokens(G);

@@ -36,7 +36,12 @@
 //    ds_read_b64_tr_b16;
 //  * work-groups are numbered so that the token blocks of one (sequence, KV head) run
 //    back to back on one XCD (work-group w runs on XCD w mod 8): they stream the same
-//    K/V at about the same time and share that XCD's L2.
+//    K/V at about the same time and share that XCD's L2;
+//  * an E4M3 cache (page 2's roadmap, page 3's support section: FP8 KV): one 16-byte load
+//    per thread covers a whole 32-key tile (8 lanes per 128-byte key row), decoded
+//    exactly to bf16 on its way into LDS; the tile's 32 K and 32 V scales are staged in
+//    LDS beside it, the K scale multiplies each logit column and the V scale each P
+//    column before its bf16 rounding (the row sums take P unscaled).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,7 +53,7 @@
 
 namespace rattn {
 
-template <int HW, int HG, int NW>
+template <int HW, int HG, int NW, bool FP8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(KernelArgs a) {
   constexpr int NT = 64 * NW;                // threads
@@ -61,10 +66,15 @@ void prefill_kernel(KernelArgs a) {
   constexpr int KPP = NT / 16;               // keys one load pass of the group covers
   constexpr int SPK = kTileKeys / KPP;       // passes per K (or V) tile
   static_assert(TB * HG == NW && TB >= 1 && SPK >= 1 && SPK * KPP == kTileKeys, "shape");
+  // E4M3: 32 keys x 128 bytes of K, then of V, one 16-byte load per thread
+  static_assert(!FP8 || NT == 2 * kTileKeys * 8, "one E4M3 load per thread per tile");
+  constexpr int NLOAD = FP8 ? 1 : 2 * SPK;   // 16-byte tile loads per thread
   __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
   __shared__ float bias_lds[2][BIAS_ELEMS];
   __shared__ int pages_lds[kChunkPages + 1];
+  // E4M3: a tile's 32 K scales, then its 32 V scales
+  __shared__ __attribute__((aligned(16))) float scale_lds[2][FP8 ? 64 : 1];
   // each wave's queries in MFMA operand order: block (head i, k-step s) holds lane l's
   // 16 bytes at l * 16, read back with one 16-byte LDS read per lane
   __shared__ __attribute__((aligned(16))) unsigned char q_lds[NW][HW][4][1024];
@@ -151,13 +161,18 @@ void prefill_kernel(KernelArgs a) {
   // ---- a tile's loads: slot m = (K|V, 16-key subtile); thread tid reads 16 bytes of key
   // tid / 16 of the subtile (a wave reads 4 whole key rows, 1 KiB contiguous) ----
   struct Tile {
-    u32x4_t x[2 * SPK];
+    u32x4_t x[NLOAD];
+    float sc;                                // E4M3, threads 0..63: a K or V scale
     float bs[BIAS_PER_THREAD];
   };
   const unsigned char* kc = (const unsigned char*)a.k_cache;
   const unsigned char* vc = (const unsigned char*)a.v_cache;
   const int ld_key = tid >> 4;               // key within a subtile
   const int ld_ch = tid & 15;                // 16-byte chunk of the key row
+  // E4M3: thread tid reads K (tid < 256) or V, key f_key of the tile, 16 codes at f_ch
+  const int f_kv = (tid >> 8) & 1;
+  const int f_key = (tid >> 3) & 31;
+  const int f_ch = tid & 7;
   auto load_tile = [&](Tile& X, int j0) {
     int64_t tok0[2];
 #pragma unroll
@@ -166,12 +181,21 @@ void prefill_kernel(KernelArgs a) {
       const int js = min(max(j0 + 16 * kt, sub_lo), sub_hi);
       tok0[kt] = ((int64_t)phys_at(js) * Hkv + g) * S + (js & (S - 1));
     }
+    if constexpr (FP8) {
+      const int64_t tok = (f_key >> 4 ? tok0[1] : tok0[0]) + (f_key & 15);
+      X.x[0] = ld16((f_kv ? vc : kc) + tok * kHeadDim + 16 * f_ch);
+      if (tid < 64) {
+        const int64_t st = (tid & 16 ? tok0[1] : tok0[0]) + (tid & 15);
+        X.sc = (tid & 32 ? a.v_scale : a.k_scale)[st];
+      }
+    } else {
 #pragma unroll
-    for (int m = 0; m < 2 * SPK; ++m) {
-      const int kk = (m % SPK) * KPP + ld_key;    // key of the tile
-      const int64_t tok = (kk >> 4 ? tok0[1] : tok0[0]) + (kk & 15);
-      const unsigned char* base = (m / SPK ? vc : kc) + tok * 256;
-      X.x[m] = ld16(base + 16 * ld_ch);   // cached: the unit's other blocks read it too
+      for (int m = 0; m < 2 * SPK; ++m) {
+        const int kk = (m % SPK) * KPP + ld_key;    // key of the tile
+        const int64_t tok = (kk >> 4 ? tok0[1] : tok0[0]) + (kk & 15);
+        const unsigned char* base = (m / SPK ? vc : kc) + tok * 256;
+        X.x[m] = ld16(base + 16 * ld_ch);   // cached: the unit's other blocks read it too
+      }
     }
 #pragma unroll
     for (int q = 0; q < BIAS_PER_THREAD; ++q) {
@@ -205,16 +229,34 @@ void prefill_kernel(KernelArgs a) {
     unsigned char* vl = vlds[buf];
     float* bl = bias_lds[buf];
     const bool edge = j0 < k_lo || j0 + kTileKeys > L;
-#pragma unroll
-    for (int m = 0; m < 2 * SPK; ++m) {
-      const int kk = (m % SPK) * KPP + ld_key;
-      u32x4_t v = X.x[m];
-      if (m / SPK) {
-        const int j = j0 + kk;
-        if (edge && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, ld_ch)) = v;
+    if constexpr (FP8) {
+      // 16 codes -> 16 bf16 values (two 16-byte chunks of the row)
+      u32x4_t raw = X.x[0];
+      const int j = j0 + f_key;
+      if (f_kv && edge && (j < k_lo || j >= L)) raw = u32x4_t{0, 0, 0, 0};
+      const u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
+      const u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
+      const u32x4_t lo = {c0.x, c0.y, c1.x, c1.y}, hi = {c2.x, c2.y, c3.x, c3.y};
+      if (f_kv) {
+        *reinterpret_cast<u32x4_t*>(vl + vlds_off(f_key, 2 * f_ch)) = lo;
+        *reinterpret_cast<u32x4_t*>(vl + vlds_off(f_key, 2 * f_ch + 1)) = hi;
       } else {
-        *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, ld_ch)) = v;
+        *reinterpret_cast<u32x4_t*>(kl + klds_off(f_key, 2 * f_ch)) = lo;
+        *reinterpret_cast<u32x4_t*>(kl + klds_off(f_key, 2 * f_ch + 1)) = hi;
+      }
+      if (tid < 64) scale_lds[buf][tid] = X.sc;
+    } else {
+#pragma unroll
+      for (int m = 0; m < 2 * SPK; ++m) {
+        const int kk = (m % SPK) * KPP + ld_key;
+        u32x4_t v = X.x[m];
+        if (m / SPK) {
+          const int j = j0 + kk;
+          if (edge && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
+          *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, ld_ch)) = v;
+        } else {
+          *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, ld_ch)) = v;
+        }
       }
     }
 #pragma unroll
@@ -255,10 +297,18 @@ void prefill_kernel(KernelArgs a) {
     }
 
     __builtin_amdgcn_s_setprio(0);
+    // E4M3: the K scales of this lane's keys 4 lq + c of each subtile (times the logit
+    // scale); the V scales are read where P is made
+    f32x4_t ks[2];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        ks[kt] = *reinterpret_cast<const f32x4_t*>(&scale_lds[buf][16 * kt + 4 * lq]) * scale2;
+    }
     // logits (with masks on the tiles that need them) of head i, key (kt, c)
     // logits in base 2 (scaled by log2 e): the exponentials need no multiply
     auto logit = [&](int i, int kt, int c) {
-      float sc = __builtin_fmaf(sacc[i][kt][c], scale2,
+      float sc = __builtin_fmaf(sacc[i][kt][c], FP8 ? ks[kt][c] : scale2,
                                 bl[bias_pos0 + i * SL - 16 * kt - c]);
       if (!FAST) {
         const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
@@ -311,6 +361,12 @@ void prefill_kernel(KernelArgs a) {
       const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
       vop[dt] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
     }
+    f32x4_t vs[2];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        vs[kt] = *reinterpret_cast<const f32x4_t*>(&scale_lds[buf][32 + 16 * kt + 4 * lq]);
+    }
     // per head: P = exp(s - m) from the logits again, packed as the B operand, then
     // O^T += V^T P^T (the next head's exponentials overlap these MFMAs)
 #pragma unroll
@@ -324,7 +380,7 @@ void prefill_kernel(KernelArgs a) {
         for (int c = 0; c < 4; ++c) {
           const float p = __builtin_amdgcn_exp2f(sv[i][kt][c] + mb);
           psum += p;
-          pv[kt][c] = p;
+          pv[kt][c] = FP8 ? (p > 0.f ? p * vs[kt][c] : 0.f) : p;
         }
       l_run[i] += psum;
       const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
@@ -334,6 +390,19 @@ void prefill_kernel(KernelArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, o[i][dt], 0, 0, 0);
+      if constexpr (FP8) {
+        // P times the V scales is not a bf16 value: its rounding remainder in a second
+        // PV product, so that one visible key gives its value to within the output's
+        // own rounding
+        const u32x4_t pr = {pack_bf16x2_rem(pv[0][0], pv[0][1], pk.x),
+                            pack_bf16x2_rem(pv[0][2], pv[0][3], pk.y),
+                            pack_bf16x2_rem(pv[1][0], pv[1][1], pk.z),
+                            pack_bf16x2_rem(pv[1][2], pv[1][3], pk.w)};
+        const bf16x8_t pop_lo = __builtin_bit_cast(bf16x8_t, pr);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop_lo, o[i][dt], 0, 0, 0);
+      }
       __builtin_amdgcn_s_setprio(0);
     }
   };

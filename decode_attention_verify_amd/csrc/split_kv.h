@@ -557,7 +557,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
 
       // per row tile: bias, logits, mask, online softmax; P packed as the B operand of
       // O^T += V^T P^T
-      bf16x8_t pop[RT];
+      bf16x8_t pop[RT], pop_lo[FP8 ? RT : 1];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         // the bias of this lane's row for its keys 4 lq + i of each subtile
@@ -616,6 +616,16 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
                             pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
         pop[t] = __builtin_bit_cast(bf16x8_t, pk);
+        if constexpr (FP8) {
+          // P times the V scales is not a bf16 value: its rounding remainder goes to the
+          // matrix units too (a second PV product), so that one visible key gives its
+          // value to within the output's own bf16 rounding
+          const u32x4_t pr = {pack_bf16x2_rem(pv[0][0], pv[0][1], pk.x),
+                              pack_bf16x2_rem(pv[0][2], pv[0][3], pk.y),
+                              pack_bf16x2_rem(pv[1][0], pv[1][1], pk.z),
+                              pack_bf16x2_rem(pv[1][2], pv[1][3], pk.w)};
+          pop_lo[t] = __builtin_bit_cast(bf16x8_t, pr);
+        }
       }
 
       if constexpr (RT > 1) __builtin_amdgcn_sched_barrier(0);
@@ -637,8 +647,11 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
         const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t) {
           o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t], o[t][dt], 0, 0, 0);
+          if constexpr (FP8)
+            o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[t], o[t][dt], 0, 0, 0);
+        }
       }
     };
 

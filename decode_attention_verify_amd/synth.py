@@ -119,6 +119,9 @@ def _named_specs():
         # on coding agents speeding up the implementation)
         "prefill_8x2k": Spec("prefill_8x2k", 8, 2048, 48, 8, 128, 0, 131071, 16, KV_BF16,
                              100000, bias_decay=1e-5),
+        # the same chunks over an E4M3 cache (page 2's roadmap: FP8 global attention)
+        "prefill_8x2k_fp8": Spec("prefill_8x2k_fp8", 8, 2048, 48, 8, 128, 0, 131071, 64,
+                                 KV_FP8, 100000, bias_decay=1e-5),
         # verify where each sequence checks its own number of drafts, 1..8 (page 3,
         # adaptive verification)
         "verify_b16_varlen": Spec("verify_b16_varlen", 16, 8, 48, 8, 128, 0, 262143, 16,

@@ -9,7 +9,7 @@ namespace rattn {
 int launch_split_kv(const KernelArgs&, int, bool, int, int, void*, void*, void*) { return 1; }
 int launch_combine(const KernelArgs&, void*, void*, void*) { return 1; }
 int launch_append_kv(const AppendArgs&, void*) { return 1; }
-int launch_prefill(const KernelArgs&, int, int, void*, void*, void*) { return 1; }
+int launch_prefill(const KernelArgs&, int, int, bool, void*, void*, void*) { return 1; }
 int launch_read_probe(const void*, int64_t, int, const int32_t*, int, void*, void*) { return 1; }
 int split_kv_blocks_per_cu(int, bool, bool, int) { return kDefaultBlocksPerCU; }
 int static_scratch_ptr(int, void** ptr) {

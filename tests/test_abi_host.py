@@ -47,7 +47,6 @@ UNSUPPORTED = [
     dict(head_dim=64), dict(page_size=24, max_pages_per_seq=6250),
     # more than 128 packed rows go to the prefill kernel, built for G = 4, 6, 8 over a
     # bf16 cache without forced splits
-    dict(n_query_rows=22, kv_dtype=binding.RATTN_KV_FP8_E4M3),
     dict(n_query_rows=100, num_q_heads=24), dict(n_query_rows=100, num_splits=4),
     # a split grid of 2^31 work-items or more (a work-group of up to 8 waves per unit)
     dict(batch=1 << 19, max_seq_len=1, max_pages_per_seq=1),
@@ -226,6 +225,10 @@ def test_planner_prefill(hq, n, tokens):
     assert info.grid_x % 8 == 0 and blocks <= info.grid_x < blocks + 8
     assert info.combine_blocks == 0 and info.row_tiles == 8
     assert binding.rattn_plan_describe(headline(), 256).kernel == binding.RATTN_KERNEL_SPLIT_KV
+    # the same over an E4M3 cache
+    p8 = headline(batch=3, num_q_heads=hq, n_query_rows=n, kv_dtype=binding.RATTN_KV_FP8_E4M3)
+    info8 = binding.rattn_plan_describe(p8, 256)
+    assert info8.kernel == binding.RATTN_KERNEL_PREFILL and info8.grid_x == info.grid_x
 
 
 def test_read_probe_rejects_bad_arguments():

@@ -234,10 +234,13 @@ def test_many_pieces_few_rows(splits, seq_len):
     check_case(sp, seed=splits, num_splits=splits)
 
 
-def test_window_fp8():
-    sp = small("window_b16", batch=4, n_rows=8, kv_format=synth.KV_FP8, page_size=64,
-               name="window_fp8")
-    check_case(sp, seed=4)
+@pytest.mark.parametrize("W,n", [(1024, 8), (1, 1), (1, 8), (2, 3)])
+def test_window_fp8(W, n):
+    # windows of one or two keys: a row's output is one or two dequantised V rows, which
+    # the P x V-scale products must carry to within the output's bf16 rounding
+    sp = small("window_b16", batch=4, n_rows=n, window=W, kv_format=synth.KV_FP8,
+               page_size=64, name="window_fp8")
+    check_case(sp, seed=4 + W + n)
 
 
 # ---------------------------------------------------------------- properties
