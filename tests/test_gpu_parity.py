@@ -10,8 +10,8 @@ import dataclasses
 import pytest
 import torch
 
-from decode_attention_verify_amd import synth
-from tests.parity import check_case, run_hip, say
+from decode_attention_verify_amd import binding, synth
+from tests.parity import check_case, compare, oracle_of, run_hip, say
 
 pytestmark = pytest.mark.gpu
 
@@ -241,6 +241,66 @@ def test_window_fp8(W, n):
     sp = small("window_b16", batch=4, n_rows=n, window=W, kv_format=synth.KV_FP8,
                page_size=64, name="window_fp8")
     check_case(sp, seed=4 + W + n)
+
+
+# ------------------------------------------------ one plan reused with different inputs
+
+def _redrawn(case, seed):
+    """The case's shapes, lengths, pages and NaN poison with new q, K, V and bias values
+    (E4M3 codes redrawn among the finite ones)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    new = dataclasses.replace(case, seed=seed, q=case.q.clone(), k_cache=case.k_cache.clone(),
+                              v_cache=case.v_cache.clone(), bias=case.bias.clone())
+    new.q.copy_(torch.randn(case.q.shape, generator=g, device="cuda").to(torch.bfloat16))
+    for c in (new.k_cache, new.v_cache):
+        if c.dtype == torch.bfloat16:
+            r = torch.randn(c.shape, generator=g, device="cuda").to(torch.bfloat16)
+            c.copy_(torch.where(torch.isnan(c), c, r))
+        else:
+            r = torch.randint(0, 0x7F, c.shape, generator=g, device="cuda").to(torch.uint8)
+            r |= (torch.randint(0, 2, c.shape, generator=g, device="cuda") * 0x80).to(torch.uint8)
+            c.copy_(torch.where((c & 0x7F) == 0x7F, c, r))
+    b = 0.5 * torch.randn(case.bias.shape, generator=g, device="cuda")
+    new.bias.copy_(torch.where(torch.isfinite(case.bias), b, case.bias))
+    return new
+
+
+@pytest.mark.parametrize("base,kw,splits", [
+    ("window_b16", dict(), 0),                                          # 6 pieces + combine
+    ("window_b16", dict(batch=5, n_rows=2, seq_len=("uniform", 2, 400)), 8),   # empty pieces
+    ("fp8_1m", dict(batch=3, n_rows=2, seq_len=("uniform", 50, 3000), dmax=3000), 5),
+    ("tiny", dict(batch=2, seq_len=("uniform", 1, 700), dmax=800, permute_pages=True), 3),
+    ("verify_b16", dict(batch=5, seq_len=("loguniform", 200, 9000)), 0),   # even shares
+])
+def test_plan_reused_with_alternating_inputs(base, kw, splits):
+    # two input sets of the same shapes alternate through one plan, whose workspace
+    # (partials, unit records) they share: every call must give its own inputs' output
+    # bit for bit (a merge that read another call's partials would not); the first
+    # output of each set is checked against the oracle
+    sp = small(base, name="lastmerge", **kw)
+    first = synth.make_case(sp, seed=31, device="cuda", poison=True)
+    cases = [first, _redrawn(first, seed=32)]
+    prob = binding.problem_from_case(cases[0], splits)
+    shape = (sp.batch, sp.n_rows, sp.num_q_heads)
+    with binding.Plan(prob) as plan:
+        say("reused plan", plan.info.as_dict())
+        refs = []
+        for i in range(24):
+            c = cases[i % 2]
+            out = torch.empty(shape + (sp.head_dim,), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty(shape, dtype=torch.float32, device="cuda")
+            plan.decode(c.q, c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.page_table,
+                        c.seq_lens, c.bias, out, lse)
+            if i < 2:
+                refs.append((out, lse))
+            else:
+                ro, rl = refs[i % 2]
+                assert torch.equal(out, ro) and torch.equal(lse, rl), "call %d" % i
+        torch.cuda.synchronize()
+        assert plan.debug_flags() == 0
+    for (out, lse), c in zip(refs, cases):
+        ref, ref_lse, _ = oracle_of(c.to("cpu"))
+        compare(out, lse, ref, ref_lse, "reused plan, seed %d" % c.seed)
 
 
 # ---------------------------------------------------------------- properties
