@@ -62,6 +62,10 @@ WORKLOADS = {
                          "d=128, batch 16, seq_lens U[2048,32768], bf16 paged KV (page 16)",
     "verify_b16": "speculative verify, 8 causal rows, 48q/8kv, d=128, batch 16, full layer, "
                   "seq_lens log-uniform [32768,262144], bf16 paged KV (page 16)",
+    "verify4_100k": "single-user speculative step, 4 causal rows, 48q/8kv, d=128, batch 1, "
+                    "100,000 keys, full layer, bf16 paged KV (page 16)",
+    "verify3_b16": "speculative verify, 3 causal rows (2 drafts), 48q/8kv, d=128, batch 16, "
+                   "full layer, seq_lens log-uniform [32768,262144], bf16 paged KV (page 16)",
     "fp8_1m": "full-context layer decode, 48q/8kv, d=128, batch 1, 1 row, 1,048,576 keys, "
               "E4M3 KV + fp32 per-token-per-head scales, paged (page 64)",
     "tiny": "full-context decode, 6q/1kv, d=128, batch 1, 1 row, 2048 keys, contiguous bf16",

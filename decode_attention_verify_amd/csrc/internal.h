@@ -38,17 +38,17 @@ inline int waves_for(int G, int n) {
   return slice <= 64 * w * kBiasPerThread ? w : 0;
 }
 
-// Row tiles of a one-wave piece: 3 for 33 to 48 packed rows (the 8-row verify of
-// 6-head groups) over a bf16 cache when every row sees at least kRowTilesMinSpan keys,
-// else 1 (the multi-wave groups of waves_for). The wave reads each K and V fragment once
-// for its 3 tiles, with no padded rows and no per-tile barrier, but keeps one tile in
-// flight: on MI355X the 8-row verify over 32K-256K keys ran 7 % faster, the same step
-// over a 1,024-key window 26 % slower. (4 and 5 tiles per wave spill registers.)
+// Row tiles of a one-wave piece: 2 or 3 for 17 to 48 packed rows (the 3- to 8-row verify
+// of 6-head groups) over a bf16 cache when every row sees at least kRowTilesMinSpan
+// keys, else 1 (the multi-wave groups of waves_for). The wave reads each K and V
+// fragment once for its tiles, with no per-tile barrier, but keeps one tile in flight:
+// on MI355X the 8-row verify over 32K-256K keys ran 7 % faster, the same step over a
+// 1,024-key window 26 % slower. (4 and 5 tiles per wave spill registers.)
 constexpr int kRowTilesMinSpan = 8192;
 inline int row_tiles_for(const rattn_problem& p) {
   const int G = p.num_q_heads / p.num_kv_heads;
   const int64_t rows = (int64_t)G * p.n_query_rows;
-  if (p.kv_dtype != RATTN_KV_BF16 || rows <= 32 || rows > 16 * kMaxRowTiles) return 1;
+  if (p.kv_dtype != RATTN_KV_BF16 || rows <= 16 || rows > 16 * kMaxRowTiles) return 1;
   const int64_t span = p.window > 0 ? (int64_t)p.window : (int64_t)p.max_seq_len;
   if (span < kRowTilesMinSpan) return 1;
   if ((int64_t)G * (kTileKeys + p.n_query_rows - 1) > 64 * kBiasPerThreadRows) return 1;

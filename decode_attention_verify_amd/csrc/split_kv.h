@@ -665,7 +665,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
     // registers): one, whose loads are issued as soon as the tile before it is in LDS,
     // so that they are in flight while the wave attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-    if constexpr (RT > 1) {
+    constexpr bool ONE_IN_FLIGHT = RT > 1;
+    if constexpr (ONE_IN_FLIGHT) {
       Tile A;
       for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
         const int c1 = min(c0 + chunk_keys, j_end);
@@ -681,7 +682,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
       }
     }
     Tile A, B;
-    for (int c0 = j_begin; RT == 1 && c0 < j_end; c0 += chunk_keys) {
+    for (int c0 = j_begin; !ONE_IN_FLIGHT && c0 < j_end; c0 += chunk_keys) {
       const int c1 = min(c0 + chunk_keys, j_end);
       stage_pages(c0, c1);
       const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;

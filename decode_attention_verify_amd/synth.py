@@ -88,6 +88,13 @@ def _named_specs():
         # speculative verify: 8 rows per sequence, batch 16, 32K-256K log-uniform
         "verify_b16": Spec("verify_b16", 16, 8, 48, 8, 128, 0, 262143, 16, KV_BF16,
                            ("loguniform", 32768, 262144), bias_decay=1e-5),
+        # a single user's speculative step at 100K context: 4 rows (page 1: about 3.5
+        # tokens accepted per step), 24 packed rows per (sequence, KV head)
+        "verify4_100k": Spec("verify4_100k", 1, 4, 48, 8, 128, 0, 131071, 16, KV_BF16,
+                             100000, bias_decay=1e-5),
+        # the same step with two drafts (3 rows: 18 packed rows per (sequence, KV head))
+        "verify3_b16": Spec("verify3_b16", 16, 3, 48, 8, 128, 0, 262143, 16, KV_BF16,
+                            ("loguniform", 32768, 262144), bias_decay=1e-5),
         # FP8 cache at 1M context, page 64
         "fp8_1m": Spec("fp8_1m", 1, 1, 48, 8, 128, 0, 1048575, 64, KV_FP8, 1048576),
         # the previous model generation's layer shapes (page 1, model table, Inkling

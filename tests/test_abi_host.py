@@ -170,8 +170,8 @@ def test_planner_covers_every_key():
                 assert pieces <= max(units, units * tiles)
             assert 1 <= info.grid_x <= 1 << 16
             rows = 6 * p.n_query_rows
-            one_wave = 32 < rows <= 48 and p.window == 0 and p.max_seq_len >= 8192
-            assert info.tiles_per_wave == (3 if one_wave else 1)
+            one_wave = 16 < rows <= 48 and p.window == 0 and p.max_seq_len >= 8192
+            assert info.tiles_per_wave == (-(-rows // 16) if one_wave else 1)
             assert info.row_tiles == (1 if rows <= 16 or one_wave else 2 if rows <= 32 else
                                       4 if rows <= 64 else 8)
             if p.num_splits:
@@ -284,17 +284,19 @@ def test_static_entry_checks_on_the_host():
 
 
 def test_planner_one_wave_of_three_row_tiles():
-    # 33 to 48 packed rows over a bf16 cache whose rows see 8,192 keys or more: one wave
-    # per piece holding three 16-row tiles; shorter spans (window layers), an E4M3 cache
-    # and other row counts keep the multi-wave groups
+    # 17 to 48 packed rows over a bf16 cache whose rows see 8,192 keys or more: one wave
+    # per piece holding two or three 16-row tiles; shorter spans (window layers), an E4M3
+    # cache and other row counts keep the multi-wave groups
     verify = dict(batch=16, n_query_rows=8, max_seq_len=262144, max_pages_per_seq=16384,
                   dmax=262143)
     info = binding.rattn_plan_describe(headline(**verify), 256)
     assert info.row_tiles == 1 and info.tiles_per_wave == 3
     info = binding.rattn_plan_describe(headline(n_query_rows=6), 256)      # 36 rows, 100K
     assert info.row_tiles == 1 and info.tiles_per_wave == 3
+    for n in (3, 5):                                                        # 18, 30 rows
+        info = binding.rattn_plan_describe(headline(**dict(verify, n_query_rows=n)), 256)
+        assert info.row_tiles == 1 and info.tiles_per_wave == 2
     for kw in (dict(verify, window=1024, dmax=1031), dict(verify, max_seq_len=8191),
-               dict(verify, kv_dtype=binding.RATTN_KV_FP8_E4M3), dict(verify, n_query_rows=9),
-               dict(verify, n_query_rows=5)):
+               dict(verify, kv_dtype=binding.RATTN_KV_FP8_E4M3), dict(verify, n_query_rows=9)):
         info = binding.rattn_plan_describe(headline(**kw), 256)
         assert info.tiles_per_wave == 1 and info.row_tiles in (2, 4, 8), kw

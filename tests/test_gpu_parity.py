@@ -110,14 +110,17 @@ def test_eight_wave_groups(hq, hkv, n, W, splits, batch, fmt):
     (6, 1, 7, 4000, 3000),                      # 36 rows, 7 pieces per unit
     (7, 3, 0, 37, ("uniform", 7, 1500)),        # 42 rows, the Dmax clamp
     (8, 2, 200, 3000, ("uniform", 8, 2500)),    # pieces without keys
+    (3, 12, 0, 3000, ("uniform", 3, 2000)),     # 18 rows: two tiles, even shares
+    (5, 1, 9, 4000, 3000),                      # 30 rows: two tiles, 9 pieces per unit
+    (4, 3, 0, 29, ("uniform", 4, 1500)),        # 24 rows, the Dmax clamp
 ])
-def test_three_row_tiles_per_wave(n, batch, splits, dmax, lens):
-    # the planning bound (max_seq_len = 9,000) picks the one-wave layout; the sequences
-    # themselves stay short so that the oracle checks every row
+def test_row_tiles_per_wave(n, batch, splits, dmax, lens):
+    # the planning bound (max_seq_len = 9,000) picks the one-wave layout of two or three
+    # row tiles; the sequences themselves stay short so that the oracle checks every row
     sp = small("full_100k", batch=batch, n_rows=n, seq_len=lens, dmax=dmax, max_seq_len=9000,
-               name="rows3")
+               name="rows_rt")
     _, _, info = check_case(sp, seed=n + batch + splits, num_splits=splits, poison=dmax > 37)
-    assert info["row_tiles"] == 1 and info["tiles_per_wave"] == 3
+    assert info["row_tiles"] == 1 and info["tiles_per_wave"] == -(-6 * n // 16)
 
 
 # ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
