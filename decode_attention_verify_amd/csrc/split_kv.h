@@ -15,7 +15,8 @@
 //    reads each K and V fragment from LDS once for all of them (the 48 rows of an 8-row
 //    verify: 3 tiles, no padding, no barrier);
 //  * K and V tiles of 32 keys are read with non-temporal 16-byte loads in row order (a
-//    16-lane pass reads 256 contiguous bytes), two tiles in flight, and stored to LDS
+//    16-lane pass reads 256 contiguous bytes), two tiles in registers (four for 8-wave
+//    groups over a bf16 cache), and stored to LDS
 //    with XOR-swizzled 16-byte chunks; page ids are staged in LDS per chunk of pages;
 //  * S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 with K (read back from LDS) as the A
 //    operand; the S^T accumulator layout (lane = query row, 4 keys per lane) is exactly
@@ -69,6 +70,10 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
   static_assert(WS == 1 || (WR == 1 && !FP8 && !EVEN), "merging work-groups: bf16 pieces");
   static_assert(RT == 1 || (WR == 1 && WS == 1), "row tiles of one wave: a one-wave group");
   constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
+  // Tiles in registers. Eight waves hold 2 of a tile's 16-byte loads each, so four tiles
+  // cost them 32 registers: the 9-token step on 8-head groups over 32K-256K keys (72
+  // rows) ran 705 -> 678 us with four, 692 with three. An E4M3 cache gained nothing.
+  constexpr int TILE_DEPTH = WR == 8 && !FP8 ? 4 : 2;
   // per wave of a merging work-group (WS > 1): its own tile buffer and page ids
   __shared__ __attribute__((aligned(16))) unsigned char klds[WS * TILE_BUFS][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[WS * TILE_BUFS][kTileKeys * 256];
@@ -660,8 +665,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
       attend_tile(X, j0, buf);
     };
 
-    // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave: two
-    // tiles in flight in registers. Several row tiles (their accumulators take the
+    // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave:
+    // TILE_DEPTH tiles in registers. Several row tiles (their accumulators take the
     // registers): one, whose loads are issued as soon as the tile before it is in LDS,
     // so that they are in flight while the wave attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
@@ -681,8 +686,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         }
       }
     }
+    // Two tiles in registers: the loads of tile i + 1 are issued before tile i is staged.
     Tile A, B;
-    for (int c0 = j_begin; !ONE_IN_FLIGHT && c0 < j_end; c0 += chunk_keys) {
+    for (int c0 = j_begin; !ONE_IN_FLIGHT && TILE_DEPTH == 2 && c0 < j_end; c0 += chunk_keys) {
       const int c1 = min(c0 + chunk_keys, j_end);
       stage_pages(c0, c1);
       const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
@@ -702,6 +708,38 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         process_tile(B, j0 + kTileKeys, 1);
       } else {
         process_tile(A, c0 + i * kTileKeys, 0);
+      }
+    }
+    // D = TILE_DEPTH > 2 tiles in registers (D even): the loads of tile i + D - 1 are
+    // issued before tile i is staged, so that D - 1 tiles are in flight while one is
+    // attended. Tile i + d sits in X[d % D] and LDS buffer d & 1 (i is a multiple of D).
+    constexpr int D = TILE_DEPTH > 2 ? TILE_DEPTH : 2;
+    static_assert(D % 2 == 0, "the LDS buffer of a tile follows its slot");
+    Tile X[TILE_DEPTH > 2 ? D : 1];
+    for (int c0 = j_begin; !ONE_IN_FLIGHT && TILE_DEPTH > 2 && c0 < j_end; c0 += chunk_keys) {
+      const int c1 = min(c0 + chunk_keys, j_end);
+      stage_pages(c0, c1);
+      const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+#pragma unroll
+      for (int d = 0; d + 1 < D; ++d)
+        if (d < nt) load_tile(X[d], c0 + d * kTileKeys);
+      int i = 0;
+      // every load of the loop body is issued unconditionally
+      for (; i + 2 * D - 1 <= nt; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int j0 = c0 + (i + d) * kTileKeys;
+          load_tile(X[(d + D - 1) % D], j0 + (D - 1) * kTileKeys);
+          process_tile(X[d], j0, d & 1);
+        }
+      }
+      // the last D - 1 .. 2 D - 2 tiles of the chunk
+#pragma unroll
+      for (int d = 0; d < 2 * D - 2; ++d) {
+        if (i + d >= nt) break;              // uniform
+        const int j0 = c0 + (i + d) * kTileKeys;
+        if (i + d + D - 1 < nt) load_tile(X[(d + D - 1) % D], j0 + (D - 1) * kTileKeys);
+        process_tile(X[d % D], j0, d & 1);
       }
     }
 
