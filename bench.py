@@ -674,7 +674,7 @@ def main():
             # a chunk of thousands of rows is a dense contraction: priced against the
             # bf16 matrix peak, 4 D flops per (row, query head, visible key)
             "bound": "mfma",
-            "kernel": "prefill_kernel",
+            "kernel": "prefill_e4m3_kernel" if fp8 else "prefill_kernel",
             "achieved": round(tr.flops / split_mean_s / 1e12, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",

@@ -7,7 +7,7 @@
 //  * append.h: the KV-cache write of each sequence's newest tokens, with E4M3
 //    quantisation for an FP8 cache;
 //  * prefill.h: the same attention for chunks of many query rows per sequence (chunked
-//    prefill), on the MFMA units;
+//    prefill) over a bf16 cache, on the MFMA units; prefill_e4m3.h: over an E4M3 cache;
 //  * probe.h: a streaming-read probe with the split kernel's load pattern (measurement);
 //  * device_common.h: device helpers and the work partition.
 #include <hip/hip_runtime.h>
@@ -17,6 +17,7 @@
 #include "append.h"
 #include "combine.h"
 #include "prefill.h"
+#include "prefill_e4m3.h"
 #include "probe.h"
 #include "split_kv.h"
 
@@ -114,12 +115,13 @@ int launch_combine(const KernelArgs& a, void* stream, void* ev_start, void* ev_s
 int launch_prefill(const KernelArgs& a, int heads_per_wave, int group, bool fp8, void* stream,
                    void* ev_start, void* ev_stop) {
   const dim3 grid((unsigned)a.split_groups), block(64 * kPrefillWaves);
-#define RATTN_PREFILL(HWV, HGV, F8)                                                          \
-  if (heads_per_wave == HWV && group == HWV * HGV && fp8 == F8)                              \
-    return launch(prefill_kernel<HWV, HGV, kPrefillWaves, F8>, grid, block, stream, a,       \
-                  ev_start, ev_stop);
-  RATTN_PREFILL(3, 2, false) RATTN_PREFILL(2, 2, false) RATTN_PREFILL(2, 4, false)
-  RATTN_PREFILL(3, 2, true) RATTN_PREFILL(2, 2, true) RATTN_PREFILL(2, 4, true)
+#define RATTN_PREFILL(HWV, HGV)                                                              \
+  if (heads_per_wave == HWV && group == HWV * HGV)                                           \
+    return fp8 ? launch(prefill_e4m3_kernel<HWV, HGV, kPrefillWaves>, grid, block, stream, a,  \
+                        ev_start, ev_stop)                                                     \
+               : launch(prefill_kernel<HWV, HGV, kPrefillWaves>, grid, block, stream, a,       \
+                        ev_start, ev_stop);
+  RATTN_PREFILL(3, 2) RATTN_PREFILL(2, 2) RATTN_PREFILL(2, 4)
 #undef RATTN_PREFILL
   return (int)hipErrorInvalidValue;
 }

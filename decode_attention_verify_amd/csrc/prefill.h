@@ -7,41 +7,40 @@
 // term added to the logits before the softmax).
 //
 // With thousands of rows per (sequence, KV head) the work is a dense contraction, so
-// this kernel is built around the MFMA units rather than around streaming:
-//  * one work-group of NW = 8 waves (two per SIMD, so that one wave's exponentials and
-//    logits overlap the other's matrix instructions) per (sequence, KV head, block of M
-//    query tokens); a wave takes 16 consecutive tokens for HW query heads of the group,
-//    one 16-row MFMA tile per head (3 heads for a 6-head group, 2 for 4- and 8-head
-//    groups: a head's O accumulators take 32 of a wave's 256 registers), so
-//    M = 16 * NW / (G / HW);
-//  * each wave's queries sit in LDS in MFMA operand order (one 16-byte read per lane and
-//    head per k-step), which leaves the registers to the O accumulators;
-//  * 32-key K/V tiles are loaded by all the group's threads (16-byte loads through the
-//    caches, which the unit's other blocks hit; 16 lanes read a 256-byte key row); the
-//    next tile's loads are in flight while a tile is attended; tiles are double-buffered
-//    in LDS with one barrier per tile; every K or V fragment read from LDS feeds the
-//    MFMAs of all HW heads;
+// this kernel is built around the MFMA units rather than around streaming (a bf16
+// cache; prefill_e4m3.h serves the E4M3 cache):
+//  * one work-group of NW = 8 waves per (sequence, KV head, block of M query tokens); a
+//    wave takes 16 consecutive tokens for HW query heads of the group, one 16-row MFMA
+//    tile per head (3 heads for a 6-head group, 2 for 4- and 8-head groups), so
+//    M = 16 * NW / (G / HW); its queries stay in registers as the B operands of
+//    S^T = K Q^T;
+//  * ping-pong: waves w and w + 4 share a SIMD. Each wave alternates a half of matrix
+//    instructions only (P V of the previous tile, then S^T of the current one) and a
+//    half of VALU work (softmax and exponentials, then its share of the next tile's
+//    loads and LDS stores), and waves 4-7 run half a period behind waves 0-3, so that
+//    one wave of each SIMD issues MFMAs while the other issues VALU instructions. On
+//    MI355X a wave of matrix instructions and a wave of VALU instructions on one SIMD
+//    run nearly as fast as each alone, while one wave mixing both gets no overlap; two
+//    waves of one SIMD in the same phase (one barrier per tile) left the matrix units
+//    idle while both ran their softmax;
+//  * 32-key K/V tiles double-buffered in LDS, each thread loading 16 bytes of a K row
+//    and 16 of a V row (16 lanes read a 256-byte row, through the caches, which the
+//    unit's other blocks hit); every K or V^T fragment read from LDS feeds the MFMAs of
+//    all HW heads;
 //  * the bias is sheared: for a tile at key j0, head h needs distances p0 - j0 - 31 ..
 //    p0 + M - 1 - j0 (p0 the position of the block's first token), one contiguous slice
-//    of M + 31 entries which the work-group stages in LDS next to the tile; row t reads
-//    key j at slice position (t - t0) - (j - j0) + 31;
-//  * logits, masks (causal and window, compiled only into the instance for tiles that
-//    cross the diagonal or the window edge), lazy online softmax (one rescale test per
-//    tile for all heads) and P V follow the decode kernel's layouts; the logits are kept
-//    in base 2 (scale and staged bias multiplied by log2 e) and held in registers from
-//    the tile maximum to the exponentials; the V^T fragments are
-//    read once per tile and each head's P V MFMAs follow its exponentials, so that the
-//    next head's VALU work overlaps them. S^T = K Q^T leaves lane (lr, lq) row lr with
-//    keys 4 lq + i, which is the B operand of O^T += V^T P^T, and V^T is read back with
-//    ds_read_b64_tr_b16;
+//    of M + 31 entries which the work-group stages in LDS (divided by the softmax
+//    scale) next to the tile; row t reads key j at slice position (t - t0) - (j - j0) +
+//    31, as the initial value of its S^T accumulator, so that the MFMAs leave s / scale;
+//  * logits in base 2 (s / scale times scale log2 e, one FMA that also subtracts the
+//    row's reference point before the exponential), masks (causal and window, compiled
+//    only into the instance for tiles that cross the diagonal or the window edge), lazy
+//    online softmax (one rescale test per tile for all heads, on each lane's own
+//    maximum); S^T = K Q^T leaves lane (lr, lq) row lr with keys 4 lq + i, which is the
+//    B operand of O^T += V^T P^T, and V^T is read back with ds_read_b64_tr_b16;
 //  * work-groups are numbered so that the token blocks of one (sequence, KV head) run
 //    back to back on one XCD (work-group w runs on XCD w mod 8): they stream the same
-//    K/V at about the same time and share that XCD's L2;
-//  * an E4M3 cache (page 2's roadmap, page 3's support section: FP8 KV): one 16-byte load
-//    per thread covers a whole 32-key tile (8 lanes per 128-byte key row), decoded
-//    exactly to bf16 on its way into LDS; the tile's 32 K and 32 V scales are staged in
-//    LDS beside it, the K scale multiplies each logit column and the V scale each P
-//    column before its bf16 rounding (the row sums take P unscaled).
+//    K/V at about the same time and share that XCD's L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,7 +52,7 @@
 
 namespace rattn {
 
-template <int HW, int HG, int NW, bool FP8>
+template <int HW, int HG, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(KernelArgs a) {
   constexpr int NT = 64 * NW;                // threads
@@ -66,18 +65,10 @@ void prefill_kernel(KernelArgs a) {
   constexpr int KPP = NT / 16;               // keys one load pass of the group covers
   constexpr int SPK = kTileKeys / KPP;       // passes per K (or V) tile
   static_assert(TB * HG == NW && TB >= 1 && SPK >= 1 && SPK * KPP == kTileKeys, "shape");
-  // E4M3: 32 keys x 128 bytes of K, then of V, one 16-byte load per thread
-  static_assert(!FP8 || NT == 2 * kTileKeys * 8, "one E4M3 load per thread per tile");
-  constexpr int NLOAD = FP8 ? 1 : 2 * SPK;   // 16-byte tile loads per thread
   __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
   __shared__ float bias_lds[2][BIAS_ELEMS];
-  __shared__ int pages_lds[kChunkPages + 1];
-  // E4M3: a tile's 32 K scales, then its 32 V scales
-  __shared__ __attribute__((aligned(16))) float scale_lds[2][FP8 ? 64 : 1];
-  // each wave's queries in MFMA operand order: block (head i, k-step s) holds lane l's
-  // 16 bytes at l * 16, read back with one 16-byte LDS read per lane
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[NW][HW][4][1024];
+  __shared__ int pages_lds[2][kChunkPages + 1];   // two chunks of page ids
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,7 +97,7 @@ void prefill_kernel(KernelArgs a) {
   const int g = (int)(u - (int64_t)b * Hkv);
 
   const SeqGeom sg = seq_geom(a, b, n, true);              // length clamped into [n, max]
-  const int L = sg.L;
+  const int L = __builtin_amdgcn_readfirstlane(sg.L);     // uniform (the tile loop is scalar)
   const int t0 = blk * M;                                  // tokens [t0, t1) of the chunk
   const int t1 = min(t0 + M, n);
   const int p0 = L - n + t0;                               // position of token t0
@@ -123,6 +114,8 @@ void prefill_kernel(KernelArgs a) {
   const int row_p = p0 + 16 * tb + lr;
   const int wave_last_p = p0 + min(16 * tb + 15, t1 - t0 - 1);   // last row of the wave
   const bool wave_live = 16 * tb < t1 - t0;
+  // the queries of the wave's rows and heads in registers, as the B operands of S^T = K Q^T
+  bf16x8_t qreg[HW][4];
 #pragma unroll
   for (int i = 0; i < HW; ++i) {
     const int h = g * G + hg * HW + i;
@@ -131,81 +124,121 @@ void prefill_kernel(KernelArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4_t v = row_ok ? ld16(qrow + 32 * s + 8 * lq) : u32x4_t{0, 0, 0, 0};
-      *reinterpret_cast<u32x4_t*>(&q_lds[wave][i][s][16 * lane]) = v;
+      qreg[i][s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  // (each wave reads only its own queries, after its own writes: no barrier needed)
 
-  // ---- page ids of a chunk of keys, staged in LDS ----
+  // ---- the schedule. Group A (waves 0-3) and group B (waves 4-7) hold one wave on each
+  // SIMD. A wave alternates an M half (P V of tile t - 1, then S^T of tile t: matrix
+  // instructions only) and a V half (logits, softmax and exponentials of tile t, then its
+  // share of the LDS stores and the next loads: VALU and memory instructions), and group
+  // B runs half a period behind group A: each SIMD holds one wave in its M half and one
+  // in its V half. (On MI355X a wave issuing only matrix instructions and a wave issuing
+  // only VALU instructions on one SIMD each run nearly as fast as alone, while a wave
+  // that mixes them gets no overlap.) A barrier ends every half: A's M(t) shares a half
+  // with B's V(t - 1), A's V(t) with B's M(t).
+  //
+  // LDS lifetimes (half h lies between barriers h - 1 and h; A's M(t) is in half 2t + 1,
+  // A's V(t) in 2t + 2, B's M(t) in 2t + 2, B's V(t) in 2t + 3):
+  //  * K_t and the bias slice of tile t (buffers t & 1) are read in halves 2t + 1 and
+  //    2t + 2 (the M(t) halves); V_t (buffer t & 1) in 2t + 3 and 2t + 4 (the M(t + 1)
+  //    halves);
+  //  * so in its V(t) a wave of group g stores its shares of K_{t+1+g}, of the bias
+  //    slice of tile t + 1 + g and of V_{t+g}: each buffer is written after its
+  //    previous tile's last read and before its tile's first read.
+  static_assert(NW == 8, "two groups of one wave per SIMD");
+  static_assert(SPK == 1, "one K and one V load per thread and tile");
+  const int grp = wave >> 2;
+  const int nt = (j_end - j_begin + kTileKeys - 1) / kTileKeys;   // tiles, >= 1
+  const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);   // a power of 2
+  const int chunk_shift = __builtin_ctz(chunk_keys);
+  const int chunk_tiles = chunk_keys / kTileKeys;                // >= 16, a power of 2
+
+  // ---- page ids, staged in LDS per chunk of keys, two chunk buffers. The ids of chunk
+  // c + 1 are staged in the V half of the chunk's first tile: the first load of chunk
+  // c + 1 comes at least 2 chunk_tiles - 3 halves later, and the last load of chunk c - 1
+  // (the buffer's previous chunk) came before. ----
   const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
-  int chunk_p0 = 0;
-  auto stage_pages = [&](int c0, int c1) {
-    __syncthreads();                         // the previous chunk's ids and tiles are done
-    chunk_p0 = c0 >> a.page_shift;
-    const int np = ((c1 - 1) >> a.page_shift) - chunk_p0 + 1;   // <= kChunkPages + 1
+  auto stage_chunk = [&](int c) {
+    const int c0 = j_begin + c * chunk_keys;
+    const int c1 = min(c0 + chunk_keys, j_end);
+    const int cp0 = c0 >> a.page_shift;
+    const int np = ((c1 - 1) >> a.page_shift) - cp0 + 1;   // <= kChunkPages + 1
     for (int i = tid; i < np; i += NT) {
-      int ph = pt_row[chunk_p0 + i];
+      int ph = pt_row[cp0 + i];
       if (ph < 0 || ph >= a.num_pages) {
         atomicOr(a.flags, RATTN_FLAG_PAGE_CLAMPED);
         ph = min(max(ph, 0), a.num_pages - 1);
       }
-      pages_lds[i] = ph;
+      pages_lds[c & 1][i] = ph;
     }
-    __syncthreads();
   };
-  auto phys_at = [&](int jt) -> int {
-    const int idx = min(max((jt >> a.page_shift) - chunk_p0, 0), kChunkPages);
-    return __builtin_amdgcn_readfirstlane(pages_lds[idx]);
+  // first token (in the cache) of the 16-key subtile kt of tile x (uniform arguments)
+  auto tile_tok = [&](int x, int kt) -> int64_t {
+    const int js = min(max(j_begin + x * kTileKeys + 16 * kt, sub_lo), sub_hi);
+    const int c = (js - j_begin) >> chunk_shift;
+    const int idx = min(max((js >> a.page_shift) - ((j_begin + (c << chunk_shift)) >> a.page_shift), 0),
+                        kChunkPages);
+    const int ph = __builtin_amdgcn_readfirstlane(pages_lds[c & 1][idx]);
+    return ((int64_t)ph * Hkv + g) * S + (js & (S - 1));
   };
 
-  // ---- a tile's loads: slot m = (K|V, 16-key subtile); thread tid reads 16 bytes of key
-  // tid / 16 of the subtile (a wave reads 4 whole key rows, 1 KiB contiguous) ----
-  struct Tile {
-    u32x4_t x[NLOAD];
-    float sc;                                // E4M3, threads 0..63: a K or V scale
-    float bs[BIAS_PER_THREAD];
+  // ---- a wave's shares of the tiles it stores in V(p): loaded in V(p - 1). Tile
+  // indices outside [0, nt) load tile 0 or nt - 1 again (every load is issued) and are
+  // not stored. ----
+  struct Shares {
+    u32x4_t k, v;                            // 16 bytes of a K row and of a V row
+    float bs[BIAS_PER_THREAD];               // bias slice elements
   };
   const unsigned char* kc = (const unsigned char*)a.k_cache;
   const unsigned char* vc = (const unsigned char*)a.v_cache;
-  const int ld_key = tid >> 4;               // key within a subtile
+  const int ld_key = tid >> 4;               // key of the tile (wave w: 4 w .. 4 w + 3)
   const int ld_ch = tid & 15;                // 16-byte chunk of the key row
-  // E4M3: thread tid reads K (tid < 256) or V, key f_key of the tile, 16 codes at f_ch
-  const int f_kv = (tid >> 8) & 1;
-  const int f_key = (tid >> 3) & 31;
-  const int f_ch = tid & 7;
-  auto load_tile = [&](Tile& X, int j0) {
-    int64_t tok0[2];
+  const unsigned ld_off = (ld_key & 15) * 256 + 16 * ld_ch;   // bytes from the subtile's row 0
+  auto clamp_tile = [&](int x) { return min(max(x, 0), nt - 1); };
+  // this thread's bias slice elements e = tid + NT q: position e % SL of head e / SL
+  // (table row bs_row, -1: no element)
+  int bs_pos[BIAS_PER_THREAD], bs_row[BIAS_PER_THREAD];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // a subtile with no key in [k_lo, p_last] reads the nearest one that has
-      const int js = min(max(j0 + 16 * kt, sub_lo), sub_hi);
-      tok0[kt] = ((int64_t)phys_at(js) * Hkv + g) * S + (js & (S - 1));
-    }
-    if constexpr (FP8) {
-      const int64_t tok = (f_key >> 4 ? tok0[1] : tok0[0]) + (f_key & 15);
-      X.x[0] = ld16((f_kv ? vc : kc) + tok * kHeadDim + 16 * f_ch);
-      if (tid < 64) {
-        const int64_t st = (tid & 16 ? tok0[1] : tok0[0]) + (tid & 15);
-        X.sc = (tid & 32 ? a.v_scale : a.k_scale)[st];
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 2 * SPK; ++m) {
-        const int kk = (m % SPK) * KPP + ld_key;    // key of the tile
-        const int64_t tok = (kk >> 4 ? tok0[1] : tok0[0]) + (kk & 15);
-        const unsigned char* base = (m / SPK ? vc : kc) + tok * 256;
-        X.x[m] = ld16(base + 16 * ld_ch);   // cached: the unit's other blocks read it too
-      }
-    }
+  for (int q = 0; q < BIAS_PER_THREAD; ++q) {
+    const int e = tid + NT * q;
+    const int hi = e / SL;
+    bs_pos[q] = e - hi * SL;
+    bs_row[q] = e < BIAS_ELEMS ? (g * G + hi) * (a.dmax + 1) : -1;
+  }
+  auto load_shares = [&](Shares& X, int p) {
+    const int xk = clamp_tile(p + 1 + grp), xv = clamp_tile(p + grp), xb = xk;
+    // wave w reads keys 4 w .. 4 w + 3: subtile grp
+    X.k = ld16(kc + tile_tok(xk, grp) * 256 + ld_off);
+    X.v = ld16(vc + tile_tok(xv, grp) * 256 + ld_off);
+    // slice element e: head e / SL of the group, distance p0 - j0 - 31 + e % SL, clamped
+    // to [0, Dmax] (a masked key reads an in-range entry)
+    const int d0 = p0 - (j_begin + xb * kTileKeys) - (kTileKeys - 1);
 #pragma unroll
     for (int q = 0; q < BIAS_PER_THREAD; ++q) {
-      // slice element e: head e / SL of the group, distance p0 - j0 - 31 + e % SL,
-      // clamped to [0, Dmax] (a masked key reads an in-range entry)
-      const int e = tid + NT * q;
-      const int hi = e / SL;
-      const int d = min(max(p0 - j0 - (kTileKeys - 1) + (e - hi * SL), 0), a.dmax);
-      const unsigned idx = e < BIAS_ELEMS ? (unsigned)((g * G + hi) * (a.dmax + 1) + d) : 0u;
-      X.bs[q] = a.bias[idx];
+      const int d = min(max(d0 + bs_pos[q], 0), a.dmax);
+      X.bs[q] = a.bias[bs_row[q] >= 0 ? (unsigned)(bs_row[q] + d) : 0u];
+    }
+  };
+  // the shares into LDS (V of keys outside [k_lo, L) as zero, so that P = 0 times a stale
+  // or NaN value cannot reach the accumulator)
+  auto store_shares = [&](const Shares& X, int p) {
+    const int xk = p + 1 + grp, xv = p + grp;
+    if (xk >= 0 && xk < nt) {
+      *reinterpret_cast<u32x4_t*>(klds[xk & 1] + klds_off(ld_key, ld_ch)) = X.k;
+      // the bias divided by the softmax scale: the S accumulators' initial value
+      const float bmul = 1.f / a.softmax_scale;
+#pragma unroll
+      for (int q = 0; q < BIAS_PER_THREAD; ++q) {
+        const int e = tid + NT * q;
+        if (e < BIAS_ELEMS) bias_lds[xk & 1][e] = X.bs[q] * bmul;
+      }
+    }
+    if (xv >= 0 && xv < nt) {
+      u32x4_t v = X.v;
+      const int j = j_begin + xv * kTileKeys + ld_key;
+      if (j < k_lo || j >= L) v = u32x4_t{0, 0, 0, 0};
+      *reinterpret_cast<u32x4_t*>(vlds[xv & 1] + vlds_off(ld_key, ld_ch)) = v;
     }
   };
 
@@ -221,223 +254,183 @@ void prefill_kernel(KernelArgs a) {
   }
   // this lane's bias slice position for key 4 lq of subtile 0, at head 0 of the wave
   const int bias_pos0 = (hg * HW) * SL + 16 * tb + lr - 4 * lq + (kTileKeys - 1);
+  // tile x has a key that one of the wave's rows sees (tiles run in key order: after
+  // the first tile past the wave's last row, none has)
+  auto live = [&](int x) { return wave_live && j_begin + x * kTileKeys <= wave_last_p; };
 
-  // the tile in registers -> LDS buffer `buf` (V of keys outside [k_lo, L) as zero, so
-  // that P = 0 times a stale or NaN value cannot reach the accumulator)
-  auto store_tile = [&](const Tile& X, int j0, int buf) {
-    unsigned char* kl = klds[buf];
-    unsigned char* vl = vlds[buf];
-    float* bl = bias_lds[buf];
-    const bool edge = j0 < k_lo || j0 + kTileKeys > L;
-    if constexpr (FP8) {
-      // 16 codes -> 16 bf16 values (two 16-byte chunks of the row)
-      u32x4_t raw = X.x[0];
-      const int j = j0 + f_key;
-      if (f_kv && edge && (j < k_lo || j >= L)) raw = u32x4_t{0, 0, 0, 0};
-      const u32x2_t c0 = e4m3x4_to_bf16x4(raw.x), c1 = e4m3x4_to_bf16x4(raw.y);
-      const u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
-      const u32x4_t lo = {c0.x, c0.y, c1.x, c1.y}, hi = {c2.x, c2.y, c3.x, c3.y};
-      if (f_kv) {
-        *reinterpret_cast<u32x4_t*>(vl + vlds_off(f_key, 2 * f_ch)) = lo;
-        *reinterpret_cast<u32x4_t*>(vl + vlds_off(f_key, 2 * f_ch + 1)) = hi;
-      } else {
-        *reinterpret_cast<u32x4_t*>(kl + klds_off(f_key, 2 * f_ch)) = lo;
-        *reinterpret_cast<u32x4_t*>(kl + klds_off(f_key, 2 * f_ch + 1)) = hi;
-      }
-      if (tid < 64) scale_lds[buf][tid] = X.sc;
-    } else {
-#pragma unroll
-      for (int m = 0; m < 2 * SPK; ++m) {
-        const int kk = (m % SPK) * KPP + ld_key;
-        u32x4_t v = X.x[m];
-        if (m / SPK) {
-          const int j = j0 + kk;
-          if (edge && (j < k_lo || j >= L)) v = u32x4_t{0, 0, 0, 0};
-          *reinterpret_cast<u32x4_t*>(vl + vlds_off(kk, ld_ch)) = v;
-        } else {
-          *reinterpret_cast<u32x4_t*>(kl + klds_off(kk, ld_ch)) = v;
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < BIAS_PER_THREAD; ++q) {
-      const int e = tid + NT * q;
-      if (e < BIAS_ELEMS) bl[e] = X.bs[q] * kLog2e;   // base-2 logits
-    }
-  };
-  // attention of this wave's rows over the tile in LDS buffer `buf`
-  auto compute_tile = [&](int j0, int buf, auto fast_tag) {
-    constexpr bool FAST = decltype(fast_tag)::value;
-    const unsigned char* kl = klds[buf];
-    const unsigned char* vl = vlds[buf];
-    const float* bl = bias_lds[buf];
-    if (!FAST && (!wave_live || j0 > wave_last_p)) return;   // every key after every row
+  f32x4_t sacc[HW][2];                       // S^T of the current tile, M(t) -> V(t)
+  bf16x8_t pop[HW];                          // P of the current tile, V(t) -> M(t + 1)
 
-    // S^T = K Q^T for the HW heads; each K fragment feeds all of them. The matrix
-    // instructions run at a raised wave priority, so that the SIMD's other wave, in its
-    // exponentials, yields the issue slot to them (the chunked prefill at 100K: 46.5 ms
-    // against 46.9)
-    __builtin_amdgcn_s_setprio(1);
-    f32x4_t sacc[HW][2];
+  // M(t): P V of tile t - 1, then S^T = K Q^T of tile t; each K or V^T fragment read
+  // from LDS feeds the MFMAs of all HW heads
+  auto m_half = [&](int t) {
+    if (t >= 1 && live(t - 1)) {
+      const unsigned char* vl = vlds[(t - 1) & 1];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int i = 0; i < HW; ++i) sacc[i][kt] = f32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8_t kop = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
+      for (int dt = 0; dt < 8; ++dt) {
+        const int cc = 2 * dt + ((lr & 3) >> 1);
+        const int k0 = 4 * lq + (lr >> 2);
+        const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
+        const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off0));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off1));
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
+        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
 #pragma unroll
         for (int i = 0; i < HW; ++i) {
-          const bf16x8_t qop = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(&q_lds[wave][i][s][16 * lane]));
-          sacc[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop, sacc[i][kt], 0, 0, 0);
+          o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[i], o[i][dt], 0, 0, 0);
         }
       }
     }
-
-    __builtin_amdgcn_s_setprio(0);
-    // E4M3: the K scales of this lane's keys 4 lq + c of each subtile (times the logit
-    // scale); the V scales are read where P is made
-    f32x4_t ks[2];
-    if constexpr (FP8) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < nt && live(t)) {
+      const unsigned char* kl = klds[t & 1];
+      const float* bl = bias_lds[t & 1];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        ks[kt] = *reinterpret_cast<const f32x4_t*>(&scale_lds[buf][16 * kt + 4 * lq]) * scale2;
-    }
-    // logits (with masks on the tiles that need them) of head i, key (kt, c)
-    // logits in base 2 (scaled by log2 e): the exponentials need no multiply
-    auto logit = [&](int i, int kt, int c) {
-      float sc = __builtin_fmaf(sacc[i][kt][c], FP8 ? ks[kt][c] : scale2,
-                                bl[bias_pos0 + i * SL - 16 * kt - c]);
-      if (!FAST) {
-        const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
-        const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
-        sc = vis ? sc : kNegInf;
-      }
-      return sc;
-    };
-    // each head's tile maximum; one test for all heads, the rare rescale in one branch
-    float mt[HW];
-    float sv[HW][2][4];
-    bool grow_any = false;
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-    for (int i = 0; i < HW; ++i) {
-      float x = kNegInf;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          sv[i][kt][c] = logit(i, kt, c);
-          x = fmaxf(x, sv[i][kt][c]);
+        for (int i = 0; i < HW; ++i) {
+          // the accumulators start at bias / scale, so that they end at s / scale (the
+          // logit of key 4 lq + c of subtile kt for the lane's row, before the scale)
+          const int bp = bias_pos0 + i * SL - 16 * kt;
+          sacc[i][kt] = f32x4_t{bl[bp], bl[bp - 1], bl[bp - 2], bl[bp - 3]};
         }
-      mt[i] = wave_max_rows(x);
-      grow_any |= mt[i] > m_run[i] + kRescaleSlack2;
-    }
-    if (__ballot(grow_any) != 0) {
 #pragma unroll
-      for (int i = 0; i < HW; ++i) {
-        const bool grow = mt[i] > m_run[i] + kRescaleSlack2;
-        const float m_new = grow ? mt[i] : m_run[i];
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[i] - m_new) : 1.f;
-        l_run[i] *= alpha;
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t kop = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
-        m_run[i] = m_new;
-      }
-    }
-    // V^T fragments of the tile (each feeds all HW heads)
-    bf16x8_t vop[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int cc = 2 * dt + ((lr & 3) >> 1);
-      const int k0 = 4 * lq + (lr >> 2);
-      const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
-      const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
-      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off0));
-      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off1));
-      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0), w1 = __builtin_bit_cast(u32x2_t, v1);
-      vop[dt] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0.x, w0.y, w1.x, w1.y});
-    }
-    f32x4_t vs[2];
-    if constexpr (FP8) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        vs[kt] = *reinterpret_cast<const f32x4_t*>(&scale_lds[buf][32 + 16 * kt + 4 * lq]);
-    }
-    // per head: P = exp(s - m) from the logits again, packed as the B operand, then
-    // O^T += V^T P^T (the next head's exponentials overlap these MFMAs)
-#pragma unroll
-    for (int i = 0; i < HW; ++i) {
-      const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]);
-      float pv[2][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float p = __builtin_amdgcn_exp2f(sv[i][kt][c] + mb);
-          psum += p;
-          pv[kt][c] = FP8 ? (p > 0.f ? p * vs[kt][c] : 0.f) : p;
+          for (int i = 0; i < HW; ++i) {
+            sacc[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[i][s], sacc[i][kt], 0, 0, 0);
+          }
         }
-      l_run[i] += psum;
-      const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
-                          pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, pk);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, o[i][dt], 0, 0, 0);
-      if constexpr (FP8) {
-        // P times the V scales is not a bf16 value: its rounding remainder in a second
-        // PV product, so that one visible key gives its value to within the output's
-        // own rounding
-        const u32x4_t pr = {pack_bf16x2_rem(pv[0][0], pv[0][1], pk.x),
-                            pack_bf16x2_rem(pv[0][2], pv[0][3], pk.y),
-                            pack_bf16x2_rem(pv[1][0], pv[1][1], pk.z),
-                            pack_bf16x2_rem(pv[1][2], pv[1][3], pk.w)};
-        const bf16x8_t pop_lo = __builtin_bit_cast(bf16x8_t, pr);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          o[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop_lo, o[i][dt], 0, 0, 0);
       }
-      __builtin_amdgcn_s_setprio(0);
     }
   };
 
-  // ---- tile loop: the next tile's loads in flight while a tile is attended. Tiles
-  // that need no mask form one contiguous run; the masked tiles before and after it run
-  // in loops of their own, so that each loop body holds one instance of the attention.
-  const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-  Tile R;
-  for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
-    const int c1 = min(c0 + chunk_keys, j_end);
-    stage_pages(c0, c1);
-    const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
-    // fast tiles i: c0 + 32 i + 31 <= p0, and with a window p_last - (c0 + 32 i) <= W - 1
-    int i_lo = 0;
-    if (W > 0) {
-      const int first = p_last - W + 1 - c0;             // smallest fast j0 - c0
-      i_lo = first <= 0 ? 0 : min((first + kTileKeys - 1) / kTileKeys, nt);
+  // V(t): masks (FAST = false: the tiles that cross the diagonal or the window edge),
+  // the tile maximum, the rare rescale, P = exp(s - m); then the wave's share of the
+  // stores and the next loads
+  Shares X;
+  auto v_half = [&](int t, auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    if (live(t)) {
+      const int j0 = j_begin + t * kTileKeys;
+      (void)j0;
+      // sv = s / scale (masked keys: -inf) and each lane's maximum of each head in base 2
+      float sv[HW][2][4];
+      float lm[HW];
+      bool grow_any = false;
+#pragma unroll
+      for (int i = 0; i < HW; ++i) {
+        float x = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float sc = sacc[i][kt][c];
+            if (!FAST) {
+              const int dist = row_p - (j0 + 16 * kt + 4 * lq + c);
+              const bool vis = row_ok && dist >= 0 && (W == 0 || dist < W);
+              sc = vis ? sc : kNegInf;
+            }
+            sv[i][kt][c] = sc;
+            x = fmaxf(x, sc);
+          }
+        lm[i] = x * scale2;
+        // the reference point m of a row moves only when its tile maximum passes m by
+        // kRescaleSlack2: the test on each lane's own maximum is the same test
+        grow_any |= lm[i] > m_run[i] + kRescaleSlack2;
+      }
+      // one test for all heads, the rare rescale in one branch (the row maximum from
+      // the 4 lanes of each row)
+      if (__ballot(grow_any) != 0) {
+#pragma unroll
+        for (int i = 0; i < HW; ++i) {
+          const float mt = wave_max_rows(lm[i]);
+          const bool grow = mt > m_run[i] + kRescaleSlack2;
+          const float m_new = grow ? mt : m_run[i];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[i] - m_new) : 1.f;
+          l_run[i] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+          m_run[i] = m_new;
+        }
+      }
+      // P = exp2(sv scale log2 e - m), packed as the B operand of O^T += V^T P^T
+#pragma unroll
+      for (int i = 0; i < HW; ++i) {
+        const float mb = -(m_run[i] == kNegInf ? 0.f : m_run[i]);
+        float pv[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i][kt][c], scale2, mb));
+            psum += p;
+            pv[kt][c] = p;
+          }
+        l_run[i] += psum;
+        const u32x4_t pk = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                            pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+        pop[i] = __builtin_bit_cast(bf16x8_t, pk);
+      }
     }
-    const int last = p0 - (kTileKeys - 1) - c0;           // largest fast j0 - c0
-    const int i_hi = last < 0 ? i_lo : max(i_lo, min(last / kTileKeys + 1, nt));
-    load_tile(R, c0);
-    auto step = [&](int i, auto fast_tag) {
-      const int j0 = c0 + i * kTileKeys;
-      const int buf = i & 1;
-      store_tile(R, j0, buf);
-      if (i + 1 < nt) load_tile(R, j0 + kTileKeys);
-      __syncthreads();                       // tile i and its bias slices are in LDS
-      compute_tile(j0, buf, fast_tag);
-    };
-    int i = 0;
-    for (; i < i_lo; ++i) step(i, std::false_type{});
-    for (; i < i_hi; ++i) step(i, std::true_type{});
-    for (; i < nt; ++i) step(i, std::false_type{});
+    store_shares(X, t);
+    if ((t & (chunk_tiles - 1)) == 0 && t + chunk_tiles < nt)
+      stage_chunk((t >> (chunk_shift - 5)) + 1);             // chunk_tiles = 2^(chunk_shift - 5)
+    load_shares(X, t + 1);
+  };
+
+  // ---- prologue: chunk 0's page ids; group A stores what its V(-1) would, group B
+  // what its V(-2) would, then B's V(-1) shares A's M(0) half ----
+  stage_chunk(0);
+  __syncthreads();
+  load_shares(X, grp ? -2 : -1);
+  store_shares(X, grp ? -2 : -1);
+  load_shares(X, grp ? -1 : 0);
+  __syncthreads();
+  if (grp) {
+    store_shares(X, -1);
+    load_shares(X, 0);
+    __syncthreads();
   }
+
+  // ---- tile loop: fast tiles (every key visible to every row: no mask code) form one
+  // contiguous run; the masked tiles before it (window edge) and after it (diagonal)
+  // run in loops of their own, so that each loop body holds one instance of the
+  // softmax. Fast tiles: j0 + 31 <= p0, and with a window p_last - j0 <= W - 1. ----
+  int x_lo = 0;
+  if (W > 0) {
+    const int first = p_last - W + 1 - j_begin;          // smallest fast j0 - j_begin
+    x_lo = first <= 0 ? 0 : min((first + kTileKeys - 1) / kTileKeys, nt);
+  }
+  const int last = p0 - (kTileKeys - 1) - j_begin;        // largest fast j0 - j_begin
+  const int x_hi = last < 0 ? x_lo : max(x_lo, min(last / kTileKeys + 1, nt));
+  int t = 0;
+  for (; t < x_lo; ++t) {
+    m_half(t);
+    __syncthreads();
+    v_half(t, std::false_type{});
+    __syncthreads();
+  }
+  for (; t < x_hi; ++t) {
+    m_half(t);
+    __syncthreads();
+    v_half(t, std::true_type{});
+    __syncthreads();
+  }
+  for (; t < nt; ++t) {
+    m_half(t);
+    __syncthreads();
+    v_half(t, std::false_type{});
+    __syncthreads();
+  }
+  m_half(nt);                                 // P V of the last tile
+  if (!grp) __syncthreads();                  // pairs with group B's last barrier
 
   // ---- epilogue: every row's output and log-sum-exp, per head ----
 #pragma unroll
