@@ -106,12 +106,11 @@ rattn_status rattn_plan(const rattn_problem* prob, rattn_plan_t* plan_out) {
   if (p == nullptr) return RATTN_E_NOMEM;
   p->prob = *prob;
   const int G = prob->num_q_heads / prob->num_kv_heads;
-  const int rt = rattn::row_tiles_for(*prob);
+  const rattn::SplitShape sh = rattn::split_shape(*prob);
   int bpc = (int64_t)G * prob->n_query_rows > rattn::kMaxRows
                 ? 1
-                : rattn::split_kv_blocks_per_cu(
-                      rt > 1 ? 1 : rattn::waves_for(G, prob->n_query_rows),
-                      prob->kv_dtype == RATTN_KV_FP8_E4M3, rattn::uses_even_shares(*prob), rt);
+                : rattn::split_kv_blocks_per_cu(sh.waves, prob->kv_dtype == RATTN_KV_FP8_E4M3,
+                                                rattn::uses_even_shares(*prob), sh.rt);
   if (bpc < 1) bpc = rattn::kDefaultBlocksPerCU;
   p->plan = rattn::make_plan(*prob, cus, bpc);
   p->device = dev;
@@ -241,11 +240,14 @@ rattn_status device_shape(int dev, const rattn_problem& p, int32_t* cus, int32_t
   if (dev < 0 || dev >= 64) return RATTN_E_HIP;
   const int G = p.num_q_heads / p.num_kv_heads;
   const bool prefill = (int64_t)G * p.n_query_rows > rattn::kMaxRows;
-  const int rt = prefill ? 1 : rattn::row_tiles_for(p);
-  const int waves = prefill ? 0 : rt > 1 ? 1 : rattn::waves_for(G, p.n_query_rows);
+  const rattn::SplitShape sh = prefill ? rattn::SplitShape{0, 1} : rattn::split_shape(p);
+  const int waves = sh.waves, rt = sh.rt;
   const bool fp8 = p.kv_dtype == RATTN_KV_FP8_E4M3;
   const bool even = rattn::uses_even_shares(p);
-  const int shape = rt > 1 ? 2 + rt : (waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0);
+  // layouts: one row tile in 1, 2, 4 or 8 waves (0-3); one wave of 2 or 3 row tiles
+  // (4, 5); four waves of 2 (6)
+  const int shape = rt > 1 ? (waves == 1 ? 2 + rt : 6)
+                           : (waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0);
   const int key = shape * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);
   std::lock_guard<std::mutex> lock(g_shape_mutex);
   DeviceShape& ds = g_shapes[dev];

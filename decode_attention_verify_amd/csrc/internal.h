@@ -38,21 +38,35 @@ inline int waves_for(int G, int n) {
   return slice <= 64 * w * kBiasPerThread ? w : 0;
 }
 
-// Row tiles of a one-wave piece: 2 or 3 for 17 to 48 packed rows (the 3- to 8-row verify
-// of 6-head groups) over a bf16 cache when every row sees at least kRowTilesMinSpan
-// keys, else 1 (the multi-wave groups of waves_for). The wave reads each K and V
-// fragment once for its tiles, with no per-tile barrier, but keeps one tile in flight:
-// on MI355X the 8-row verify over 32K-256K keys ran 7 % faster, the same step over a
-// 1,024-key window 26 % slower. (4 and 5 tiles per wave spill registers.)
+// Row tiles per wave. Over a bf16 cache whose rows all see at least kRowTilesMinSpan
+// keys, a piece of 17 to 48 packed rows runs as one wave of 2 or 3 row tiles (16 rows
+// each, or fewer rows spread evenly over them), and a piece of 65 to 128 rows as four
+// waves of two row tiles (up to 32 rows per wave); other row counts and spans keep one
+// row tile per wave (waves_for). A wave reads each K and V fragment once for its tiles.
+// On MI355X the 8-row verify of 6-head groups over 32K-256K keys ran 7 % faster as one
+// wave of three tiles than as four waves of one, the same step over a 1,024-key window
+// 26 % slower. (4 and 5 tiles per wave spill registers.)
 constexpr int kRowTilesMinSpan = 8192;
-inline int row_tiles_for(const rattn_problem& p) {
+
+struct SplitShape {
+  int waves;   // waves per split work-group (0: none fits)
+  int rt;      // row tiles per wave
+};
+
+// The split kernel's layout for a problem of at most kMaxRows packed rows per unit.
+inline SplitShape split_shape(const rattn_problem& p) {
   const int G = p.num_q_heads / p.num_kv_heads;
-  const int64_t rows = (int64_t)G * p.n_query_rows;
-  if (p.kv_dtype != RATTN_KV_BF16 || rows <= 16 || rows > 16 * kMaxRowTiles) return 1;
+  const int n = p.n_query_rows;
+  const int64_t rows = (int64_t)G * n;
   const int64_t span = p.window > 0 ? (int64_t)p.window : (int64_t)p.max_seq_len;
-  if (span < kRowTilesMinSpan) return 1;
-  if ((int64_t)G * (kTileKeys + p.n_query_rows - 1) > 64 * kBiasPerThreadRows) return 1;
-  return (int)((rows + 15) / 16);
+  const int64_t slice = (int64_t)G * (kTileKeys + n - 1);
+  if (p.kv_dtype == RATTN_KV_BF16 && span >= kRowTilesMinSpan) {
+    if (rows > 16 && rows <= 16 * kMaxRowTiles && slice <= 64 * kBiasPerThreadRows)
+      return SplitShape{1, (int)((rows + 15) / 16)};
+    if (rows > 64 && rows <= kMaxRows && slice <= 64 * 4 * kBiasPerThread)
+      return SplitShape{4, 2};
+  }
+  return SplitShape{waves_for(G, n), 1};
 }
 
 // A unit of single-wave bf16 pieces split in 2 or kMergeWaves pieces runs as one

@@ -26,14 +26,16 @@ namespace rattn {
 // ---------------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------------
-// variant index: waves per piece (1, 2, 4, 8) or row tiles of a one-wave piece (2, 3),
-// KV format, partition; single-wave pieces also in merging groups of kMergeWaves
+// variant index: waves per piece (1, 2, 4, 8) of one row tile each, one wave of 2 or 3
+// row tiles, or 4 waves of 2; KV format, partition; single-wave pieces also in merging
+// groups of kMergeWaves
 #define RATTN_VARIANTS(X)                                                               \
   X(1, false, false, 1) X(1, true, false, 1) X(2, false, false, 1) X(2, true, false, 1)  \
   X(4, false, false, 1) X(4, true, false, 1) X(8, false, false, 1) X(8, true, false, 1)  \
   X(1, false, true, 1) X(1, true, true, 1) X(2, false, true, 1) X(2, true, true, 1)      \
   X(4, false, true, 1) X(4, true, true, 1) X(8, false, true, 1) X(8, true, true, 1)      \
-  X(1, false, false, 2) X(1, false, true, 2) X(1, false, false, 3) X(1, false, true, 3)
+  X(1, false, false, 2) X(1, false, true, 2) X(1, false, false, 3) X(1, false, true, 3)      \
+  X(4, false, false, 2) X(4, false, true, 2)
 
 static int variant_key(int waves, bool fp8, bool even, int rt) {
   return (rt * 16 + waves) * 4 + (fp8 ? 2 : 0) + (even ? 1 : 0);

@@ -57,7 +57,7 @@ rattn_status validate_problem(const rattn_problem* p) {
     if (((int64_t)p->batch * p->num_kv_heads * blocks + 7) * 64 * kPrefillWaves >=
         ((int64_t)1 << 31))
       return RATTN_E_UNSUPPORTED;
-  } else if (waves_for(G, p->n_query_rows) == 0) {
+  } else if (split_shape(*p).waves == 0) {
     // a tile's bias slice (G heads x (32 + n - 1) distances) must fit the work-group's
     // loads
     return RATTN_E_UNSUPPORTED;
@@ -112,8 +112,9 @@ Plan make_plan(const rattn_problem& p, int32_t num_cus, int32_t blocks_per_cu) {
   const int32_t rows = G * p.n_query_rows;
   if (rows > kMaxRows) return make_prefill_plan(p, num_cus, blocks_per_cu);
   Plan pl{};
-  pl.rt = row_tiles_for(p);
-  pl.waves = pl.rt > 1 ? 1 : waves_for(G, p.n_query_rows);
+  const SplitShape sh = split_shape(p);
+  pl.rt = sh.rt;
+  pl.waves = sh.waves;
   pl.num_cus = num_cus;
   pl.blocks_per_cu = blocks_per_cu;
   const int64_t units = (int64_t)p.batch * p.num_kv_heads;

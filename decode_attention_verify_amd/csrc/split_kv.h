@@ -10,10 +10,10 @@
 // Design on gfx950:
 //  * one work-group of 1, 2, 4 or 8 waves per piece of a (sequence, KV head) unit; the
 //    G*n packed query rows (G = Hq/Hkv) go to 16-row MFMA tiles, one per wave (6 rows pad
-//    to 16 here, not to 64 as in the pages' Blackwell tile; the 72 rows of a 9-token step
-//    on 8-head groups take 8 waves of 9 rows); or one wave holding RT 16-row tiles, which
-//    reads each K and V fragment from LDS once for all of them (the 48 rows of an 8-row
-//    verify: 3 tiles, no padding, no barrier);
+//    to 16 here, not to 64 as in the pages' Blackwell tile); or waves holding RT row
+//    tiles each, which read each K and V fragment from LDS once for all of them (the 48
+//    rows of an 8-row verify: one wave of 3 tiles, no padding, no barrier; the 72 rows of
+//    a 9-token step on 8-head groups: 4 waves of two 9-row tiles);
 //  * K and V tiles of 32 keys are read with non-temporal 16-byte loads in row order (a
 //    16-lane pass reads 256 contiguous bytes), two tiles in registers (four for 8-wave
 //    groups over a bf16 cache), and stored to LDS
@@ -58,17 +58,19 @@ namespace rattn {
 // would; the waves then merge their pieces through LDS into the unit's output, so that
 // no combine launch follows (see the epilogue).
 //
-// RT > 1 (one wave, WR = 1): the wave holds RT 16-row MFMA tiles of the unit's packed
-// rows. Each K fragment and V^T fragment it reads from LDS feeds RT matrix instructions;
-// the queries and the tile's sheared bias slice are staged in LDS. The O accumulators
-// (32 registers per row tile) leave the arithmetic registers to the tiles in flight, so
-// the wave runs alone on its SIMD with the full register file.
+// RT > 1: each wave holds RT MFMA tiles of its share of the unit's packed rows (rows
+// spread evenly over them). Each K fragment and V^T fragment it reads from LDS feeds RT
+// matrix instructions; the queries (each wave its own block) and the tile's sheared bias
+// slice are staged in LDS, and one tile is in flight. A one-wave piece runs alone on its
+// SIMD with the full register file (the O accumulators, 32 registers per row tile, leave
+// the arithmetic registers to the tile in flight); four waves of two tiles run two waves
+// per SIMD, two groups per CU.
 template <int WR, bool FP8, bool EVEN, int WS, int RT>
 __global__ __launch_bounds__(64 * WR * WS)
 __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void split_kv_kernel(
     KernelArgs a) {
   static_assert(WS == 1 || (WR == 1 && !FP8 && !EVEN), "merging work-groups: bf16 pieces");
-  static_assert(RT == 1 || (WR == 1 && WS == 1), "row tiles of one wave: a one-wave group");
+  static_assert(RT == 1 || WS == 1, "row tiles of a wave: not in a merging group");
   constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
   // Tiles in registers. Eight waves hold 2 of a tile's 16-byte loads each, so four tiles
   // cost them 32 registers: the 9-token step on 8-head groups over 32K-256K keys (72
@@ -87,11 +89,11 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
   // WR (two buffers exactly when several waves share one).
   constexpr bool STAGE_BIAS = WR > 1 || RT > 1;
   constexpr int BIAS_BUFS = WR > 1 ? 2 : 1;
-  constexpr int BPT = RT > 1 ? kBiasPerThreadRows : kBiasPerThread;   // slice loads per lane
+  constexpr int BPT = RT > 1 && WR == 1 ? kBiasPerThreadRows : kBiasPerThread;   // slice loads per lane
   __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? 64 * WR * BPT : 1];
   // RT > 1: the queries of the wave's RT * 16 rows, row i's 16-byte chunk c at
   // klds_off(i, c) (the B operand reads of one instruction hit distinct banks)
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[RT > 1 ? RT * 16 * 256 : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[RT > 1 ? WR : 1][RT > 1 ? RT * 16 * 256 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = WR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -105,7 +107,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
   const int S = a.page_size;
   const int W = a.window;
   const int64_t Hkv = a.num_kv_heads;
-  const int rpw = (R + WR - 1) / WR;
+  const int rpw = (R + WR - 1) / WR;          // rows per wave
+  const int rpt = RT == 1 ? rpw : (rpw + RT - 1) / RT;   // rows per row tile (<= 16)
 
   const int64_t wg = (int64_t)blockIdx.x * WS + wsi;   // the piece
   const int k_split = a.splits_per_unit;     // used when !EVEN
@@ -126,8 +129,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
   bool row_ok[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    rho[t] = RT == 1 ? wave * rpw + lr : 16 * t + lr;
-    row_ok[t] = (RT > 1 || lr < rpw) && rho[t] < R;
+    rho[t] = wave * rpw + t * rpt + lr;
+    row_ok[t] = lr < rpt && t * rpt + lr < rpw && rho[t] < R;
     r_of_row[t] = row_ok[t] ? rho[t] / G : 0;
     hl_of_row[t] = row_ok[t] ? rho[t] - r_of_row[t] * G : 0;
   }
@@ -294,16 +297,19 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         qreg[s] = __builtin_bit_cast(bf16x8_t, v);
       }
     } else {
-      // the unit's queries into LDS: 16 lanes read one 256-byte row, four rows per pass.
-      // Every load is issued before the first store (a row the sequence lacks reads its
-      // first row and stores zeros), so that they share one memory round trip.
+      // the wave's queries into its LDS block: 16 lanes read one 256-byte row, four rows
+      // per pass. Every load is issued before the first store (a tile row without a
+      // query row reads the unit's first row and stores zeros), so that they share one
+      // memory round trip. Each wave reads only its own block.
       u32x4_t qv[4 * RT];
       bool qlive[4 * RT];
 #pragma unroll
       for (int k = 0; k < 4 * RT; ++k) {
-        const int i = 4 * k + lq;                    // packed row
+        const int ti = 4 * k + lq;                   // tile row: tile ti / 16, row ti % 16
+        const int tt = ti >> 4, tl = ti & 15;
+        const int i = wave * rpw + tt * rpt + tl;    // packed row
         const int r = i / G;
-        qlive[k] = i < R && r < nb;
+        qlive[k] = tl < rpt && tt * rpt + tl < rpw && i < R && r < nb;
         const int rr = qlive[k] ? r : 0, hh = qlive[k] ? i - r * G : 0;
         qv[k] = ld16(a.q + ((int64_t)(row_base + rr) * a.num_q_heads + g * G + hh) * kHeadDim +
                      8 * lr);
@@ -311,7 +317,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
 #pragma unroll
       for (int k = 0; k < 4 * RT; ++k) {
         const unsigned keep = qlive[k] ? ~0u : 0u;
-        *reinterpret_cast<u32x4_t*>(q_lds + klds_off(4 * k + lq, lr)) =
+        *reinterpret_cast<u32x4_t*>(q_lds[RT > 1 ? wave : 0] + klds_off(4 * k + lq, lr)) =
             qv[k] & u32x4_t{keep, keep, keep, keep};
       }
     }
@@ -537,7 +543,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
           if constexpr (RT == 1) qop = qreg[s];
           else
             qop = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(q_lds + klds_off(16 * t + lr, 4 * s + lq)));
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(q_lds[RT > 1 ? wave : 0] +
+                                                            klds_off(16 * t + lr, 4 * s + lq)));
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
             sacc[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kt], qop, sacc[t][kt], 0, 0, 0);
@@ -680,9 +687,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         load_tile(A, c0);
         for (int i = 0; i < nt; ++i) {
           const int j0 = c0 + i * kTileKeys;
-          stage_tile(A, j0, 0);
+          stage_tile(A, j0, i & 1);          // several waves alternate two buffers
           if (i + 1 < nt) load_tile(A, j0 + kTileKeys);
-          attend_tile(A, j0, 0);
+          attend_tile(A, j0, i & 1);
         }
       }
     }

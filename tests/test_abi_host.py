@@ -243,21 +243,30 @@ def test_read_probe_rejects_bad_arguments():
 
 @pytest.mark.parametrize("hq,n", [(64, 9), (48, 11), (48, 21), (32, 32), (64, 16)])
 @pytest.mark.parametrize("kv", [binding.RATTN_KV_BF16, binding.RATTN_KV_FP8_E4M3])
-def test_planner_eight_wave_groups(hq, n, kv):
+def test_planner_65_to_128_rows(hq, n, kv):
     # 65 to 128 packed rows (the 9-token step on 8-head groups: 72 rows) stay on the
-    # split kernel, one 16-row tile per wave in 8-wave work-groups, for both cache
-    # formats; a full-context batch is shared evenly and merged by the combine
+    # split kernel: over a bf16 cache and long spans four waves of two row tiles each,
+    # else one 16-row tile per wave in 8-wave work-groups (an E4M3 cache, a short span);
+    # a full-context batch is shared evenly and merged by the combine
     G = hq // 8
     assert 64 < G * n <= 128
+    want = (4, 2) if kv == binding.RATTN_KV_BF16 else (8, 1)
     p = headline(batch=4, num_q_heads=hq, n_query_rows=n, max_seq_len=262144,
                  max_pages_per_seq=16384, num_pages=65536, dmax=262143, kv_dtype=kv)
     info = binding.rattn_plan_describe(p, 256)
-    assert info.kernel == binding.RATTN_KERNEL_SPLIT_KV and info.row_tiles == 8
+    assert info.kernel == binding.RATTN_KERNEL_SPLIT_KV
+    assert (info.row_tiles, info.tiles_per_wave) == want
     assert info.pieces_per_group == 1 and info.combine_blocks == -(-4 * n * hq // 4)
     assert info.workspace_bytes >= (info.grid_x + 32) * G * n * 129 * 4
     # batch 1: the unit's keys cut into pieces of equal length
     one = binding.rattn_plan_describe(headline(num_q_heads=hq, n_query_rows=n, kv_dtype=kv), 256)
-    assert one.row_tiles == 8 and one.num_splits > 1 and one.grid_x == 8 * one.num_splits
+    assert (one.row_tiles, one.tiles_per_wave) == want
+    assert one.num_splits > 1 and one.grid_x == 8 * one.num_splits
+    # a window of 1,024 keys: one row tile per wave
+    short = binding.rattn_plan_describe(
+        headline(num_q_heads=hq, n_query_rows=n, kv_dtype=kv, window=1024, max_seq_len=32768,
+                 max_pages_per_seq=2048), 256)
+    assert (short.row_tiles, short.tiles_per_wave) == (8, 1)
 
 
 def test_static_entry_checks_on_the_host():

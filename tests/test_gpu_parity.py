@@ -123,6 +123,26 @@ def test_row_tiles_per_wave(n, batch, splits, dmax, lens):
     assert info["row_tiles"] == 1 and info["tiles_per_wave"] == -(-6 * n // 16)
 
 
+# ----- 65 to 128 packed rows over long spans: four waves, each holding two row tiles
+
+@pytest.mark.parametrize("hq,n,batch,splits,dmax,lens", [
+    (64, 9, 6, 0, 3000, ("uniform", 9, 2000)),   # 72 rows (the 9-token step), even shares
+    (64, 9, 1, 5, 4000, 3000),                   # 5 pieces per unit
+    (64, 16, 2, 0, 45, ("uniform", 16, 1500)),   # 128 rows, the Dmax clamp
+    (48, 11, 2, 300, 3000, ("uniform", 11, 2500)),   # 66 rows, pieces without keys
+    (32, 20, 3, 0, 3000, ("uniform", 20, 2000)),     # 4-head groups, 80 rows
+])
+def test_four_waves_of_two_row_tiles(hq, n, batch, splits, dmax, lens):
+    # the planning bound (max_seq_len = 9,000) picks the four-wave layout; rows per wave
+    # spread evenly over the wave's two tiles; short sequences, so that the oracle checks
+    # every row
+    sp = small("full_100k", batch=batch, n_rows=n, num_q_heads=hq, num_kv_heads=8,
+               seq_len=lens, dmax=dmax, max_seq_len=9000, name="rows_4x2")
+    _, _, info = check_case(sp, seed=hq + n + batch + splits, num_splits=splits,
+                            poison=dmax > 45)
+    assert info["row_tiles"] == 4 and info["tiles_per_wave"] == 2
+
+
 # ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
 
 @pytest.mark.parametrize("name", ["tp4_100k", "tp8_100k"])
