@@ -92,6 +92,17 @@ WORKLOADS = {
     "prefill_8x2k_fp8": "chunked prefill: 8 sequences, a chunk of 2048 query tokens each at "
                         "100,000 keys (the chunk included), 48q/8kv, d=128, causal, E4M3 KV + "
                         "fp32 per-token-per-head scales, paged (page 64)",
+    "verify_b16_fp8": "speculative verify, 8 causal rows, 48q/8kv, d=128, batch 16, full layer, "
+                      "seq_lens log-uniform [32768,262144], E4M3 KV + fp32 per-token-per-head "
+                      "scales, paged (page 64)",
+    "decode_b16_fp8": "full-context layer decode, 48q/8kv, d=128, batch 16, 1 row, seq_lens "
+                      "log-uniform [32768,262144], E4M3 KV + fp32 per-token-per-head scales, "
+                      "paged (page 64)",
+    "verify3_b16_8k": "speculative verify, 3 causal rows (2 drafts), 48q/8kv, d=128, batch 16, "
+                      "full layer, seq_lens log-uniform [2048,8191], bf16 paged KV (page 16)",
+    "verify3_b16_fp8": "speculative verify, 3 causal rows (2 drafts), 48q/8kv, d=128, batch 16, "
+                       "full layer, seq_lens log-uniform [32768,262144], E4M3 KV + fp32 "
+                       "per-token-per-head scales, paged (page 64)",
     "verify_b16_varlen": "speculative verify with 1..8 rows per sequence (seeded), 48q/8kv, "
                          "d=128, batch 16, full layer, seq_lens log-uniform [32768,262144], "
                          "bf16 paged KV (page 16)",

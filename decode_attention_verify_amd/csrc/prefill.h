@@ -82,6 +82,7 @@ void prefill_kernel(KernelArgs a) {
   const int S = a.page_size;
   const int W = a.window;
   const float scale2 = a.softmax_scale * kLog2e;
+  const float inv_scale = 1.f / a.softmax_scale;
   constexpr float kRescaleSlack2 = 8.f;      // kRescaleSlack in base 2
   constexpr float kLn2 = 0.6931471805599453f;
 
@@ -227,11 +228,10 @@ void prefill_kernel(KernelArgs a) {
     if (xk >= 0 && xk < nt) {
       *reinterpret_cast<u32x4_t*>(klds[xk & 1] + klds_off(ld_key, ld_ch)) = X.k;
       // the bias divided by the softmax scale: the S accumulators' initial value
-      const float bmul = 1.f / a.softmax_scale;
 #pragma unroll
       for (int q = 0; q < BIAS_PER_THREAD; ++q) {
         const int e = tid + NT * q;
-        if (e < BIAS_ELEMS) bias_lds[xk & 1][e] = X.bs[q] * bmul;
+        if (e < BIAS_ELEMS) bias_lds[xk & 1][e] = X.bs[q] * inv_scale;
       }
     }
     if (xv >= 0 && xv < nt) {

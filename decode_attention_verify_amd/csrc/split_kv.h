@@ -15,8 +15,7 @@
 //    rows of an 8-row verify: one wave of 3 tiles, no padding, no barrier; the 72 rows of
 //    a 9-token step on 8-head groups: 4 waves of two 9-row tiles);
 //  * K and V tiles of 32 keys are read with non-temporal 16-byte loads in row order (a
-//    16-lane pass reads 256 contiguous bytes), two tiles in registers (four for 8-wave
-//    groups over a bf16 cache), and stored to LDS
+//    16-lane pass reads 256 contiguous bytes), two tiles in flight, and stored to LDS
 //    with XOR-swizzled 16-byte chunks; page ids are staged in LDS per chunk of pages;
 //  * S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 with K (read back from LDS) as the A
 //    operand; the S^T accumulator layout (lane = query row, 4 keys per lane) is exactly
@@ -65,17 +64,23 @@ namespace rattn {
 // SIMD with the full register file (the O accumulators, 32 registers per row tile, leave
 // the arithmetic registers to the tile in flight); four waves of two tiles run two waves
 // per SIMD, two groups per CU.
+// Waves per SIMD: one for a single bf16 wave (its two tiles in flight take 128 registers)
+// and for a wave of row tiles (the accumulators of 2 or 3 tiles), and for 2-wave groups of
+// even shares over a bf16 cache (at two per SIMD they spilled 104 bytes per lane; the
+// 3-row step over 2K-8K keys at batch 16 ran 87 us at two, 73 at one); else two.
+template <int WR, bool FP8, bool EVEN, int RT>
+constexpr int split_kv_occupancy() {
+  return (WR == 1 && (!FP8 || RT > 1)) || (WR == 2 && EVEN && !FP8 && RT == 1) ? 1 : 2;
+}
+#define OCCUPANCY (split_kv_occupancy<WR, FP8, EVEN, RT>())
+
 template <int WR, bool FP8, bool EVEN, int WS, int RT>
 __global__ __launch_bounds__(64 * WR * WS)
-__attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void split_kv_kernel(
+__attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     KernelArgs a) {
   static_assert(WS == 1 || (WR == 1 && !FP8 && !EVEN), "merging work-groups: bf16 pieces");
   static_assert(RT == 1 || WS == 1, "row tiles of a wave: not in a merging group");
   constexpr int TILE_BUFS = WR > 1 ? 2 : 1;   // LDS tile buffers (see process_tile)
-  // Tiles in registers. Eight waves hold 2 of a tile's 16-byte loads each, so four tiles
-  // cost them 32 registers: the 9-token step on 8-head groups over 32K-256K keys (72
-  // rows) ran 705 -> 678 us with four, 692 with three. An E4M3 cache gained nothing.
-  constexpr int TILE_DEPTH = WR == 8 && !FP8 ? 4 : 2;
   // per wave of a merging work-group (WS > 1): its own tile buffer and page ids
   __shared__ __attribute__((aligned(16))) unsigned char klds[WS * TILE_BUFS][kTileKeys * 256];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[WS * TILE_BUFS][kTileKeys * 256];
@@ -118,8 +123,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
     T = __builtin_amdgcn_readfirstlane(total_tiles(a, lane));   // the same in every lane
     P = min((int64_t)gridDim.x, (int64_t)T);
     if (wg >= P) return;                     // uniform over the work-group
-    t_begin = wg * T / P;
-    t_end = (wg + 1) * T / P;
+    t_begin = uniform(wg * T / P);
+    t_end = uniform((wg + 1) * T / P);
   }
 
   // ---- this lane's query row in each of the wave's row tiles (row rho[t] of the unit's
@@ -212,9 +217,9 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
       const int sidx = (int)(wg - u * k_split);
       b = (int)(u / Hkv);
       g = (int)(u - (int64_t)b * Hkv);
-      sg = seq_geom(a, b, true);
-      tile0 = (int)((int64_t)sidx * sg.tiles / k_split);
-      tile1 = (int)((int64_t)(sidx + 1) * sg.tiles / k_split);
+      sg = uniform(seq_geom(a, b, true));
+      tile0 = uniform((int)((int64_t)sidx * sg.tiles / k_split));
+      tile1 = uniform((int)((int64_t)(sidx + 1) * sg.tiles / k_split));
       whole = k_split == 1;
       prow0 = wg * R;
       more = false;
@@ -232,8 +237,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
       locate_tile(a, lane, (int)t_begin, b, before);
       b = __builtin_amdgcn_readfirstlane(b);           // the same in every lane
       before = __builtin_amdgcn_readfirstlane(before);
-      sg = seq_geom(a, b, false);
-      g = (t_begin - before) / sg.tiles;
+      sg = uniform(seq_geom(a, b, false));
+      g = uniform((int)((t_begin - before) / sg.tiles));
       const int64_t ustart = before + (int64_t)g * sg.tiles;
       const int64_t uend = ustart + sg.tiles;
       const int64_t piece_end = min(t_end, uend);
@@ -258,7 +263,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
     bool row_live[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) row_live[t] = row_ok[t] && r_of_row[t] < nb;
-    const int row_base = seq_rows(a, b, false).base;
+    const int row_base = uniform(seq_rows(a, b, false).base);
     const int j_begin = sg.base + tile0 * kTileKeys;
     const int j_end = min(sg.base + tile1 * kTileKeys, L);
 
@@ -672,8 +677,8 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
       attend_tile(X, j0, buf);
     };
 
-    // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave:
-    // TILE_DEPTH tiles in registers. Several row tiles (their accumulators take the
+    // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave: two
+    // tiles in flight in registers. Several row tiles (their accumulators take the
     // registers): one, whose loads are issued as soon as the tile before it is in LDS,
     // so that they are in flight while the wave attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
@@ -695,7 +700,7 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
     }
     // Two tiles in registers: the loads of tile i + 1 are issued before tile i is staged.
     Tile A, B;
-    for (int c0 = j_begin; !ONE_IN_FLIGHT && TILE_DEPTH == 2 && c0 < j_end; c0 += chunk_keys) {
+    for (int c0 = j_begin; !ONE_IN_FLIGHT && c0 < j_end; c0 += chunk_keys) {
       const int c1 = min(c0 + chunk_keys, j_end);
       stage_pages(c0, c1);
       const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
@@ -715,38 +720,6 @@ __attribute__((amdgpu_waves_per_eu(WR == 1 && (!FP8 || RT > 1) ? 1 : 2))) void s
         process_tile(B, j0 + kTileKeys, 1);
       } else {
         process_tile(A, c0 + i * kTileKeys, 0);
-      }
-    }
-    // D = TILE_DEPTH > 2 tiles in registers (D even): the loads of tile i + D - 1 are
-    // issued before tile i is staged, so that D - 1 tiles are in flight while one is
-    // attended. Tile i + d sits in X[d % D] and LDS buffer d & 1 (i is a multiple of D).
-    constexpr int D = TILE_DEPTH > 2 ? TILE_DEPTH : 2;
-    static_assert(D % 2 == 0, "the LDS buffer of a tile follows its slot");
-    Tile X[TILE_DEPTH > 2 ? D : 1];
-    for (int c0 = j_begin; !ONE_IN_FLIGHT && TILE_DEPTH > 2 && c0 < j_end; c0 += chunk_keys) {
-      const int c1 = min(c0 + chunk_keys, j_end);
-      stage_pages(c0, c1);
-      const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
-#pragma unroll
-      for (int d = 0; d + 1 < D; ++d)
-        if (d < nt) load_tile(X[d], c0 + d * kTileKeys);
-      int i = 0;
-      // every load of the loop body is issued unconditionally
-      for (; i + 2 * D - 1 <= nt; i += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-          const int j0 = c0 + (i + d) * kTileKeys;
-          load_tile(X[(d + D - 1) % D], j0 + (D - 1) * kTileKeys);
-          process_tile(X[d], j0, d & 1);
-        }
-      }
-      // the last D - 1 .. 2 D - 2 tiles of the chunk
-#pragma unroll
-      for (int d = 0; d < 2 * D - 2; ++d) {
-        if (i + d >= nt) break;              // uniform
-        const int j0 = c0 + (i + d) * kTileKeys;
-        if (i + d + D - 1 < nt) load_tile(X[(d + D - 1) % D], j0 + (D - 1) * kTileKeys);
-        process_tile(X[d % D], j0, d & 1);
       }
     }
 

@@ -97,6 +97,16 @@ def _named_specs():
                             ("loguniform", 32768, 262144), bias_decay=1e-5),
         # FP8 cache at 1M context, page 64
         "fp8_1m": Spec("fp8_1m", 1, 1, 48, 8, 128, 0, 1048575, 64, KV_FP8, 1048576),
+        # batched full-context layers over an FP8 cache (page 64): decode and verify
+        "decode_b16_fp8": Spec("decode_b16_fp8", 16, 1, 48, 8, 128, 0, 262143, 64, KV_FP8,
+                               ("loguniform", 32768, 262144), bias_decay=1e-5),
+        "verify_b16_fp8": Spec("verify_b16_fp8", 16, 8, 48, 8, 128, 0, 262143, 64, KV_FP8,
+                               ("loguniform", 32768, 262144), bias_decay=1e-5),
+        "verify3_b16_fp8": Spec("verify3_b16_fp8", 16, 3, 48, 8, 128, 0, 262143, 64, KV_FP8,
+                                ("loguniform", 32768, 262144), bias_decay=1e-5),
+        # the 3-row step over short contexts (the planning bound below 8,192 keys)
+        "verify3_b16_8k": Spec("verify3_b16_8k", 16, 3, 48, 8, 128, 0, 8191, 16, KV_BF16,
+                               ("loguniform", 2048, 8191), bias_decay=1e-5),
         # the previous model generation's layer shapes (page 1, model table, Inkling
         # column: full layers 64 query / 8 KV heads, sliding layers 64 / 16 with a window
         # of 512; page 2, model architecture: up to 9 tokens per step with MTP heads)

@@ -123,6 +123,22 @@ def test_row_tiles_per_wave(n, batch, splits, dmax, lens):
     assert info["row_tiles"] == 1 and info["tiles_per_wave"] == -(-6 * n // 16)
 
 
+# ---------------- batched full-context layers through the even-share variants, full size
+
+@pytest.mark.parametrize("name,kv_head", [
+    ("verify_b16_fp8", 3),     # E4M3, 48 rows: 4-wave groups
+    ("decode_b16_fp8", 6),     # E4M3, 6 rows: one wave
+    ("verify3_b16_fp8", 1),    # E4M3, 18 rows: 2-wave groups
+])
+def test_batched_full_layers_e4m3_sampled(name, kv_head):
+    check_case(synth.spec(name), seed=0, gen_device="cuda", kv_heads=[kv_head])
+
+
+def test_three_rows_short_contexts():
+    # 18 packed rows, planning bound 8,191 keys: 2-wave groups, even shares; every unit
+    check_case(synth.spec("verify3_b16_8k"), seed=0, gen_device="cuda")
+
+
 # ----- 65 to 128 packed rows over long spans: four waves, each holding two row tiles
 
 @pytest.mark.parametrize("hq,n,batch,splits,dmax,lens", [
