@@ -176,20 +176,6 @@ __device__ __forceinline__ SeqGeom seq_geom(const KernelArgs& a, int b, bool fla
   return seq_geom(a, b, seq_rows(a, b, flag_bad).n, flag_bad);
 }
 
-// A value the same in every lane, moved to scalar registers (a sequence's geometry is
-// read with vector loads; without this its arithmetic and the tile loop's indices stay
-// in vector registers).
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform(int64_t x) {
-  const unsigned long long u = (unsigned long long)x;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
-  return (int64_t)(((unsigned long long)hi << 32) | lo);
-}
-__device__ __forceinline__ SeqGeom uniform(SeqGeom g) {
-  return SeqGeom{uniform(g.nb), uniform(g.L), uniform(g.k_lo), uniform(g.base), uniform(g.tiles)};
-}
-
 // Tiles of all units (every lane returns the total; below 2^31 by validation).
 __device__ int total_tiles(const KernelArgs& a, int lane) {
   int sum = 0;

@@ -123,8 +123,8 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     T = __builtin_amdgcn_readfirstlane(total_tiles(a, lane));   // the same in every lane
     P = min((int64_t)gridDim.x, (int64_t)T);
     if (wg >= P) return;                     // uniform over the work-group
-    t_begin = uniform(wg * T / P);
-    t_end = uniform((wg + 1) * T / P);
+    t_begin = wg * T / P;
+    t_end = (wg + 1) * T / P;
   }
 
   // ---- this lane's query row in each of the wave's row tiles (row rho[t] of the unit's
@@ -217,9 +217,9 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
       const int sidx = (int)(wg - u * k_split);
       b = (int)(u / Hkv);
       g = (int)(u - (int64_t)b * Hkv);
-      sg = uniform(seq_geom(a, b, true));
-      tile0 = uniform((int)((int64_t)sidx * sg.tiles / k_split));
-      tile1 = uniform((int)((int64_t)(sidx + 1) * sg.tiles / k_split));
+      sg = seq_geom(a, b, true);
+      tile0 = (int)((int64_t)sidx * sg.tiles / k_split);
+      tile1 = (int)((int64_t)(sidx + 1) * sg.tiles / k_split);
       whole = k_split == 1;
       prow0 = wg * R;
       more = false;
@@ -237,8 +237,8 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
       locate_tile(a, lane, (int)t_begin, b, before);
       b = __builtin_amdgcn_readfirstlane(b);           // the same in every lane
       before = __builtin_amdgcn_readfirstlane(before);
-      sg = uniform(seq_geom(a, b, false));
-      g = uniform((int)((t_begin - before) / sg.tiles));
+      sg = seq_geom(a, b, false);
+      g = (t_begin - before) / sg.tiles;
       const int64_t ustart = before + (int64_t)g * sg.tiles;
       const int64_t uend = ustart + sg.tiles;
       const int64_t piece_end = min(t_end, uend);
@@ -263,7 +263,7 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     bool row_live[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) row_live[t] = row_ok[t] && r_of_row[t] < nb;
-    const int row_base = uniform(seq_rows(a, b, false).base);
+    const int row_base = seq_rows(a, b, false).base;
     const int j_begin = sg.base + tile0 * kTileKeys;
     const int j_end = min(sg.base + tile1 * kTileKeys, L);
 
