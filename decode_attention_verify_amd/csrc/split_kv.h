@@ -60,10 +60,10 @@ namespace rattn {
 // RT > 1: each wave holds RT MFMA tiles of its share of the unit's packed rows (rows
 // spread evenly over them). Each K fragment and V^T fragment it reads from LDS feeds RT
 // matrix instructions; the queries (each wave its own block) and the tile's sheared bias
-// slice are staged in LDS, and one tile is in flight. A one-wave piece runs alone on its
-// SIMD with the full register file (the O accumulators, 32 registers per row tile, leave
-// the arithmetic registers to the tile in flight); four waves of two tiles run two waves
-// per SIMD, two groups per CU.
+// slice are staged in LDS. A one-wave piece runs alone on its SIMD with the full register
+// file and one tile in flight (the O accumulators, 32 registers per row tile, leave the
+// arithmetic registers to that tile); four waves of two tiles run two waves per SIMD, two
+// groups per CU, with two tiles in flight (each wave holds a quarter of a tile's loads).
 // Waves per SIMD: one for a single bf16 wave (its two tiles in flight take 128 registers)
 // and for a wave of row tiles (the accumulators of 2 or 3 tiles), and for 2-wave groups of
 // even shares over a bf16 cache (at two per SIMD they spilled 104 bytes per lane; the
@@ -678,11 +678,47 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     };
 
     // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave: two
-    // tiles in flight in registers. Several row tiles (their accumulators take the
-    // registers): one, whose loads are issued as soon as the tile before it is in LDS,
-    // so that they are in flight while the wave attends that tile ----
+    // tiles in registers. Several row tiles in a lone wave (their accumulators take the
+    // registers): one tile in flight, whose loads are issued as soon as the tile before
+    // it is in LDS, so that they are in flight while the wave attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-    constexpr bool ONE_IN_FLIGHT = RT > 1;
+    constexpr bool TWO_AHEAD = RT > 1 && WR > 1;
+    constexpr bool ONE_IN_FLIGHT = RT > 1 && !TWO_AHEAD;
+    if constexpr (TWO_AHEAD) {
+      // Several waves of row tiles (a quarter of each tile's loads per wave): two tiles in
+      // flight while one is attended, in registers A and B by turns. Each tile's loads are
+      // issued right after the tile two places before it is in LDS. In the steady state
+      // every load is issued without a condition, so that the compiler waits for exactly
+      // one tile; a chunk of fewer than two tiles loads its one tile twice.
+      Tile A, B;
+      for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
+        const int c1 = min(c0 + chunk_keys, j_end);
+        stage_pages(c0, c1);
+        const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+        load_tile(A, c0);
+        load_tile(B, c0 + min(1, nt - 1) * kTileKeys);
+        int i = 0;
+        for (; i + 4 <= nt; i += 2) {
+          const int j0 = c0 + i * kTileKeys;
+          stage_tile(A, j0, 0);
+          load_tile(A, j0 + 2 * kTileKeys);
+          attend_tile(A, j0, 0);
+          stage_tile(B, j0 + kTileKeys, 1);
+          load_tile(B, j0 + 3 * kTileKeys);
+          attend_tile(B, j0 + kTileKeys, 1);
+        }
+        // the last 1, 2 or 3 tiles (uniform), tile i in A and tile i + 1 in B
+        const int j0 = c0 + i * kTileKeys;
+        const int rest = nt - i;
+        stage_tile(A, j0, 0);
+        if (rest == 3) load_tile(A, j0 + 2 * kTileKeys);
+        attend_tile(A, j0, 0);
+        if (rest >= 2) {
+          process_tile(B, j0 + kTileKeys, 1);
+          if (rest == 3) process_tile(A, j0 + 2 * kTileKeys, 0);
+        }
+      }
+    }
     if constexpr (ONE_IN_FLIGHT) {
       Tile A;
       for (int c0 = j_begin; c0 < j_end; c0 += chunk_keys) {
@@ -692,7 +728,7 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
         load_tile(A, c0);
         for (int i = 0; i < nt; ++i) {
           const int j0 = c0 + i * kTileKeys;
-          stage_tile(A, j0, i & 1);          // several waves alternate two buffers
+          stage_tile(A, j0, 0);              // a lone wave: one LDS tile buffer
           if (i + 1 < nt) load_tile(A, j0 + kTileKeys);
           attend_tile(A, j0, i & 1);
         }
@@ -700,7 +736,7 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     }
     // Two tiles in registers: the loads of tile i + 1 are issued before tile i is staged.
     Tile A, B;
-    for (int c0 = j_begin; !ONE_IN_FLIGHT && c0 < j_end; c0 += chunk_keys) {
+    for (int c0 = j_begin; RT == 1 && c0 < j_end; c0 += chunk_keys) {
       const int c1 = min(c0 + chunk_keys, j_end);
       stage_pages(c0, c1);
       const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;

@@ -159,6 +159,18 @@ def test_four_waves_of_two_row_tiles(hq, n, batch, splits, dmax, lens):
     assert info["row_tiles"] == 4 and info["tiles_per_wave"] == 2
 
 
+@pytest.mark.parametrize("splits,L", [(63, 2000), (32, 2000), (21, 2000), (13, 2000),
+                                      (9, 2000), (2, 20000)])
+def test_four_waves_two_tiles_in_flight(splits, L):
+    # the four-wave layout keeps two tiles in flight; 63 tiles in 63, 32, 21, 13 and 9
+    # pieces give pieces of 1 to 7 tiles (each way its tile loop can end), and 20,000 keys
+    # in two pieces give pieces that span two chunks of page ids
+    sp = small("full_100k", batch=1, n_rows=9, num_q_heads=64, num_kv_heads=8, seq_len=L,
+               dmax=max(L, 9000), max_seq_len=max(L, 9000), name="rows_4x2_tails")
+    _, _, info = check_case(sp, seed=splits, num_splits=splits)
+    assert info["row_tiles"] == 4 and info["tiles_per_wave"] == 2
+
+
 # ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
 
 @pytest.mark.parametrize("name", ["tp4_100k", "tp8_100k"])
