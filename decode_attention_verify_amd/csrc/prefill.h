@@ -65,7 +65,11 @@ void prefill_kernel(KernelArgs a) {
   constexpr int KPP = NT / 16;               // keys one load pass of the group covers
   constexpr int SPK = kTileKeys / KPP;       // passes per K (or V) tile
   static_assert(TB * HG == NW && TB >= 1 && SPK >= 1 && SPK * KPP == kTileKeys, "shape");
-  __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
+  // K rows padded to 272 bytes: the 16 rows one fragment read touches start 4 banks apart
+  // (no conflicts), and the four fragments of a row tile lie at fixed offsets from one
+  // lane address, so that each read's offset is an immediate
+  constexpr int KROW = 272;
+  __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * KROW];
   __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
   __shared__ float bias_lds[2][BIAS_ELEMS];
   __shared__ int pages_lds[2][kChunkPages + 1];   // two chunks of page ids
@@ -226,12 +230,14 @@ void prefill_kernel(KernelArgs a) {
   auto store_shares = [&](const Shares& X, int p) {
     const int xk = p + 1 + grp, xv = p + grp;
     if (xk >= 0 && xk < nt) {
-      *reinterpret_cast<u32x4_t*>(klds[xk & 1] + klds_off(ld_key, ld_ch)) = X.k;
-      // the bias divided by the softmax scale: the S accumulators' initial value
+      *reinterpret_cast<u32x4_t*>(klds[xk & 1] + ld_key * KROW + 16 * ld_ch) = X.k;
+      // the bias divided by the softmax scale: the S accumulators' initial value. Each
+      // head's slice is stored in reverse, position pos at SL - 1 - pos, so that the four
+      // entries a lane's accumulator takes are ascending in LDS
 #pragma unroll
       for (int q = 0; q < BIAS_PER_THREAD; ++q) {
         const int e = tid + NT * q;
-        if (e < BIAS_ELEMS) bias_lds[xk & 1][e] = X.bs[q] * inv_scale;
+        if (e < BIAS_ELEMS) bias_lds[xk & 1][e + SL - 1 - 2 * bs_pos[q]] = X.bs[q] * inv_scale;
       }
     }
     if (xv >= 0 && xv < nt) {
@@ -253,7 +259,8 @@ void prefill_kernel(KernelArgs a) {
     for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4_t{0, 0, 0, 0};
   }
   // this lane's bias slice position for key 4 lq of subtile 0, at head 0 of the wave
-  const int bias_pos0 = (hg * HW) * SL + 16 * tb + lr - 4 * lq + (kTileKeys - 1);
+  // (stored reversed: key 4 lq + c of subtile kt of head i at bias_rev0 + i SL + 16 kt + c)
+  const int bias_rev0 = (hg * HW) * SL + (SL - 1) - (16 * tb + lr - 4 * lq + (kTileKeys - 1));
   // tile x has a key that one of the wave's rows sees (tiles run in key order: after
   // the first tile past the wave's last row, none has)
   auto live = [&](int x) { return wave_live && j_begin + x * kTileKeys <= wave_last_p; };
@@ -294,13 +301,13 @@ void prefill_kernel(KernelArgs a) {
         for (int i = 0; i < HW; ++i) {
           // the accumulators start at bias / scale, so that they end at s / scale (the
           // logit of key 4 lq + c of subtile kt for the lane's row, before the scale)
-          const int bp = bias_pos0 + i * SL - 16 * kt;
-          sacc[i][kt] = f32x4_t{bl[bp], bl[bp - 1], bl[bp - 2], bl[bp - 3]};
+          const int bp = bias_rev0 + i * SL + 16 * kt;
+          sacc[i][kt] = f32x4_t{bl[bp], bl[bp + 1], bl[bp + 2], bl[bp + 3]};
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8_t kop = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + (16 * kt + lr) * KROW + 16 * (4 * s + lq)));
 #pragma unroll
           for (int i = 0; i < HW; ++i) {
             sacc[i][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qreg[i][s], sacc[i][kt], 0, 0, 0);
