@@ -165,9 +165,11 @@ void prefill_kernel(KernelArgs a) {
   const int chunk_tiles = chunk_keys / kTileKeys;                // >= 16, a power of 2
 
   // ---- page ids, staged in LDS per chunk of keys, two chunk buffers. The ids of chunk
-  // c + 1 are staged in the V half of the chunk's first tile: the first load of chunk
-  // c + 1 comes at least 2 chunk_tiles - 3 halves later, and the last load of chunk c - 1
-  // (the buffer's previous chunk) came before. ----
+  // c + 1 are staged in the V half of the chunk's first tile (group A's half 2 c T + 2,
+  // B's 2 c T + 3, T tiles per chunk). The ids are read in the M half before a tile's
+  // loads (tile_base): the first read of chunk c + 1 comes at least 2 T - 5 halves after
+  // its staging began, and the last read of chunk c - 1 (the buffer's previous chunk) at
+  // least 5 halves before it. ----
   const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
   auto stage_chunk = [&](int c) {
     const int c0 = j_begin + c * chunk_keys;
@@ -184,12 +186,21 @@ void prefill_kernel(KernelArgs a) {
     }
   };
   // first token (in the cache) of the 16-key subtile kt of tile x (uniform arguments)
-  auto tile_tok = [&](int x, int kt) -> int64_t {
-    const int js = min(max(j_begin + x * kTileKeys + 16 * kt, sub_lo), sub_hi);
+  // in two steps: the page id read from LDS (tile_page), then the token (tile_tok), so
+  // that the read can be issued well before its value is used
+  auto tile_js = [&](int x, int kt) {
+    return min(max(j_begin + x * kTileKeys + 16 * kt, sub_lo), sub_hi);
+  };
+  auto tile_page = [&](int x, int kt) -> int {
+    const int js = tile_js(x, kt);
     const int c = (js - j_begin) >> chunk_shift;
     const int idx = min(max((js >> a.page_shift) - ((j_begin + (c << chunk_shift)) >> a.page_shift), 0),
                         kChunkPages);
-    const int ph = __builtin_amdgcn_readfirstlane(pages_lds[c & 1][idx]);
+    return pages_lds[c & 1][idx];
+  };
+  auto tile_tok = [&](int x, int kt, int page) -> int64_t {
+    const int ph = __builtin_amdgcn_readfirstlane(page);
+    const int js = tile_js(x, kt);
     return ((int64_t)ph * Hkv + g) * S + (js & (S - 1));
   };
 
@@ -216,11 +227,29 @@ void prefill_kernel(KernelArgs a) {
     bs_pos[q] = e - hi * SL;
     bs_row[q] = e < BIAS_ELEMS ? (g * G + hi) * (a.dmax + 1) : -1;
   }
-  auto load_shares = [&](Shares& X, int p) {
-    const int xk = clamp_tile(p + 1 + grp), xv = clamp_tile(p + grp), xb = xk;
-    // wave w reads keys 4 w .. 4 w + 3: subtile grp
-    X.k = ld16(kc + tile_tok(xk, grp) * 256 + ld_off);
-    X.v = ld16(vc + tile_tok(xv, grp) * 256 + ld_off);
+  // the byte offsets, in the caches, of the 16-key subtiles that load_shares(X, p) reads
+  // (uniform), worked out a half ahead of the loads: the M half issues the two page-id
+  // reads before its fragment reads and finishes the offsets after its last matrix
+  // instruction, so that neither the reads' latency nor the scalar products delay the
+  // V half's loads
+  struct TilePages {
+    int k, v;
+  };
+  struct TileBase {
+    int64_t k, v;
+  };
+  // wave w reads keys 4 w .. 4 w + 3: subtile grp
+  auto tile_pages = [&](int p) -> TilePages {
+    return TilePages{tile_page(clamp_tile(p + 1 + grp), grp), tile_page(clamp_tile(p + grp), grp)};
+  };
+  auto tile_base = [&](int p, const TilePages& pg) -> TileBase {
+    return TileBase{tile_tok(clamp_tile(p + 1 + grp), grp, pg.k) * 256,
+                    tile_tok(clamp_tile(p + grp), grp, pg.v) * 256};
+  };
+  auto load_shares = [&](Shares& X, int p, const TileBase& tb) {
+    const int xb = clamp_tile(p + 1 + grp);
+    X.k = ld16(kc + tb.k + ld_off);
+    X.v = ld16(vc + tb.v + ld_off);
     // slice element e: head e / SL of the group, distance p0 - j0 - 31 + e % SL, clamped
     // to [0, Dmax] (a masked key reads an in-range entry)
     const int d0 = p0 - (j_begin + xb * kTileKeys) - (kTileKeys - 1);
@@ -275,7 +304,9 @@ void prefill_kernel(KernelArgs a) {
 
   // M(t): P V of tile t - 1, then S^T = K Q^T of tile t; each K or V^T fragment read
   // from LDS feeds the MFMAs of all HW heads
+  TileBase next_base;                        // load_shares(X, t + 1) of V(t), from M(t)
   auto m_half = [&](int t) {
+    const TilePages next_pages = tile_pages(t + 1);
     if (t >= 1 && live(t - 1)) {
       const unsigned char* vl = vlds[(t - 1) & 1];
 #pragma unroll
@@ -320,6 +351,8 @@ void prefill_kernel(KernelArgs a) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    next_base = tile_base(t + 1, next_pages);
   };
 
   // V(t): masks (FAST = false: the tiles that cross the diagonal or the window edge),
@@ -394,20 +427,20 @@ void prefill_kernel(KernelArgs a) {
     store_shares(X, t);
     if ((t & (chunk_tiles - 1)) == 0 && t + chunk_tiles < nt)
       stage_chunk((t >> (chunk_shift - 5)) + 1);             // chunk_tiles = 2^(chunk_shift - 5)
-    load_shares(X, t + 1);
+    load_shares(X, t + 1, next_base);
   };
 
   // ---- prologue: chunk 0's page ids; group A stores what its V(-1) would, group B
   // what its V(-2) would, then B's V(-1) shares A's M(0) half ----
   stage_chunk(0);
   __syncthreads();
-  load_shares(X, grp ? -2 : -1);
+  load_shares(X, grp ? -2 : -1, tile_base(grp ? -2 : -1, tile_pages(grp ? -2 : -1)));
   store_shares(X, grp ? -2 : -1);
-  load_shares(X, grp ? -1 : 0);
+  load_shares(X, grp ? -1 : 0, tile_base(grp ? -1 : 0, tile_pages(grp ? -1 : 0)));
   __syncthreads();
   if (grp) {
     store_shares(X, -1);
-    load_shares(X, 0);
+    load_shares(X, 0, tile_base(0, tile_pages(0)));
     __syncthreads();
   }
 
