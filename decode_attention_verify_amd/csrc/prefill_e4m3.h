@@ -59,8 +59,11 @@ void prefill_e4m3_kernel(KernelArgs a) {
   static_assert(TB * HG == NW && TB >= 1, "shape");
   // 32 keys x 128 bytes of K, then of V, one 16-byte load per thread
   static_assert(NT == 2 * kTileKeys * 8, "one E4M3 load per thread per tile");
-  __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * 256];
+  // decoded tiles with padded rows (K 272 bytes, V 288), as in the bf16 prefill kernel:
+  // every fragment read's offset from one lane address is an immediate
+  constexpr int KROW = 272, VROW = 288;
+  __shared__ __attribute__((aligned(16))) unsigned char klds[2][kTileKeys * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char vlds[2][kTileKeys * VROW];
   __shared__ float bias_lds[2][BIAS_ELEMS];
   __shared__ int pages_lds[kChunkPages + 1];
   // a tile's 32 K scales, then its 32 V scales
@@ -215,11 +218,11 @@ void prefill_e4m3_kernel(KernelArgs a) {
     const u32x2_t c2 = e4m3x4_to_bf16x4(raw.z), c3 = e4m3x4_to_bf16x4(raw.w);
     const u32x4_t lo = {c0.x, c0.y, c1.x, c1.y}, hi = {c2.x, c2.y, c3.x, c3.y};
     if (f_kv) {
-      *reinterpret_cast<u32x4_t*>(vl + vlds_off(f_key, 2 * f_ch)) = lo;
-      *reinterpret_cast<u32x4_t*>(vl + vlds_off(f_key, 2 * f_ch + 1)) = hi;
+      *reinterpret_cast<u32x4_t*>(vl + f_key * VROW + 32 * f_ch) = lo;
+      *reinterpret_cast<u32x4_t*>(vl + f_key * VROW + 32 * f_ch + 16) = hi;
     } else {
-      *reinterpret_cast<u32x4_t*>(kl + klds_off(f_key, 2 * f_ch)) = lo;
-      *reinterpret_cast<u32x4_t*>(kl + klds_off(f_key, 2 * f_ch + 1)) = hi;
+      *reinterpret_cast<u32x4_t*>(kl + f_key * KROW + 32 * f_ch) = lo;
+      *reinterpret_cast<u32x4_t*>(kl + f_key * KROW + 32 * f_ch + 16) = hi;
     }
     if (tid < 64) scale_lds[buf][tid] = X.sc;
 #pragma unroll
@@ -249,7 +252,7 @@ void prefill_e4m3_kernel(KernelArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const bf16x8_t kop = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + klds_off(16 * kt + lr, 4 * s + lq)));
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(kl + (16 * kt + lr) * KROW + 16 * (4 * s + lq)));
 #pragma unroll
         for (int i = 0; i < HW; ++i) {
           const bf16x8_t qop = __builtin_bit_cast(
@@ -313,8 +316,8 @@ void prefill_e4m3_kernel(KernelArgs a) {
     for (int dt = 0; dt < 8; ++dt) {
       const int cc = 2 * dt + ((lr & 3) >> 1);
       const int k0 = 4 * lq + (lr >> 2);
-      const int off0 = vlds_off(k0, cc) + 8 * (lr & 1);
-      const int off1 = vlds_off(16 + k0, cc) + 8 * (lr & 1);
+      const int off0 = k0 * VROW + 16 * cc + 8 * (lr & 1);
+      const int off1 = (16 + k0) * VROW + 16 * cc + 8 * (lr & 1);
       const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (i16x4_t __attribute__((address_space(3)))*)(const_cast<unsigned char*>(vl) + off0));
       const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
