@@ -23,15 +23,17 @@
 //    run nearly as fast as each alone, while one wave mixing both gets no overlap; two
 //    waves of one SIMD in the same phase (one barrier per tile) left the matrix units
 //    idle while both ran their softmax;
-//  * 32-key K/V tiles double-buffered in LDS, each thread loading 16 bytes of a K row
-//    and 16 of a V row (16 lanes read a 256-byte row, through the caches, which the
-//    unit's other blocks hit); every K or V^T fragment read from LDS feeds the MFMAs of
-//    all HW heads;
+//  * 32-key K/V tiles double-buffered in LDS in padded rows (so that every fragment
+//    read's offset is an immediate), each thread loading 16 bytes of a K row and 16 of a
+//    V row (16 lanes read a 256-byte row, through the caches, which the unit's other
+//    blocks hit); every K or V^T fragment read from LDS feeds the MFMAs of all HW heads;
+//    the page ids of a tile's loads are read from LDS a half ahead of the loads;
 //  * the bias is sheared: for a tile at key j0, head h needs distances p0 - j0 - 31 ..
 //    p0 + M - 1 - j0 (p0 the position of the block's first token), one contiguous slice
 //    of M + 31 entries which the work-group stages in LDS (divided by the softmax
-//    scale) next to the tile; row t reads key j at slice position (t - t0) - (j - j0) +
-//    31, as the initial value of its S^T accumulator, so that the MFMAs leave s / scale;
+//    scale, in reverse order) next to the tile; row t reads key j at slice position
+//    (t - t0) - (j - j0) + 31, as the initial value of its S^T accumulator, so that the
+//    MFMAs leave s / scale;
 //  * logits in base 2 (s / scale times scale log2 e, one FMA that also subtracts the
 //    row's reference point before the exponential), masks (causal and window, compiled
 //    only into the instance for tiles that cross the diagonal or the window edge), lazy
