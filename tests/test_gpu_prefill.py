@@ -57,6 +57,16 @@ def test_prefill_fp8_cache(hq, hkv, n, W, page_size):
     assert info["kernel"] == binding.RATTN_KERNEL_PREFILL
 
 
+@pytest.mark.parametrize("W", [0, 64])
+def test_prefill_dmax_clamp(W):
+    # most distances past Dmax = 45: every clamped entry of a bias slice (stored in
+    # reverse in LDS) is the table's last column
+    sp = small("full_100k", batch=2, n_rows=100, seq_len=("uniform", 100, 1500), window=W,
+               dmax=45, name="prefill_dmax")
+    _, _, info = check_case(sp, seed=45 + W)
+    assert info["kernel"] == binding.RATTN_KERNEL_PREFILL
+
+
 def test_prefill_whole_sequence_is_the_chunk():
     # the first chunk of a prompt: L = n, every row causal over the chunk alone
     sp = small("full_100k", batch=3, n_rows=200, seq_len=200, dmax=250, bias_decay=0.0,
