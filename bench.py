@@ -92,6 +92,12 @@ WORKLOADS = {
     "prefill_8x2k_fp8": "chunked prefill: 8 sequences, a chunk of 2048 query tokens each at "
                         "100,000 keys (the chunk included), 48q/8kv, d=128, causal, E4M3 KV + "
                         "fp32 per-token-per-head scales, paged (page 64)",
+    "prefill_4x2k_g8": "chunked prefill: 4 sequences, a chunk of 2048 query tokens each at "
+                       "32,768 keys (the chunk included), 64q/8kv, d=128, causal, bf16 paged "
+                       "KV (page 16)",
+    "prefill_4x2k_g4": "chunked prefill: 4 sequences, a chunk of 2048 query tokens each at "
+                       "32,768 keys (the chunk included), 64q/16kv, d=128, causal, bf16 paged "
+                       "KV (page 16)",
     "verify_b16_fp8": "speculative verify, 8 causal rows, 48q/8kv, d=128, batch 16, full layer, "
                       "seq_lens log-uniform [32768,262144], E4M3 KV + fp32 per-token-per-head "
                       "scales, paged (page 64)",

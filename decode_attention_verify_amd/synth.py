@@ -139,6 +139,12 @@ def _named_specs():
         # the same chunks over an E4M3 cache (page 2's roadmap: FP8 global attention)
         "prefill_8x2k_fp8": Spec("prefill_8x2k_fp8", 8, 2048, 48, 8, 128, 0, 131071, 64,
                                  KV_FP8, 100000, bias_decay=1e-5),
+        # chunks on the previous generation's layer shapes (64q heads): 8-head groups (64/8)
+        # and 4-head groups (64/16), 4 chunks of 2048 tokens at 32K
+        "prefill_4x2k_g8": Spec("prefill_4x2k_g8", 4, 2048, 64, 8, 128, 0, 131071, 16,
+                                KV_BF16, 32768, bias_decay=1e-5),
+        "prefill_4x2k_g4": Spec("prefill_4x2k_g4", 4, 2048, 64, 16, 128, 0, 131071, 16,
+                                KV_BF16, 32768, bias_decay=1e-5),
         # verify where each sequence checks its own number of drafts, 1..8 (page 3,
         # adaptive verification)
         "verify_b16_varlen": Spec("verify_b16_varlen", 16, 8, 48, 8, 128, 0, 262143, 16,

@@ -74,7 +74,8 @@ def test_prefill_whole_sequence_is_the_chunk():
     check_case(sp, seed=4)
 
 
-@pytest.mark.parametrize("name", ["prefill_8x2k", "prefill_8x2k_fp8"])
+@pytest.mark.parametrize("name", ["prefill_8x2k", "prefill_8x2k_fp8", "prefill_4x2k_g8",
+                                  "prefill_4x2k_g4"])
 def test_prefill_full_size_sampled(name):
     sp = synth.spec(name)
     say("prefill full size: %s B=%d n=%d L=%s kv=%s" % (sp.name, sp.batch, sp.n_rows,
@@ -93,7 +94,8 @@ def test_prefill_full_size_sampled(name):
     picks = [(b, r, g) for b, r, g in zip(rng.integers(0, sp.batch, 12),
                                           rng.integers(0, sp.n_rows, 12),
                                           rng.integers(0, sp.num_kv_heads, 12))]
-    picks += [(0, 0, 0), (7, sp.n_rows - 1, 7), (3, 1023, 2)]
+    B, H = sp.batch, sp.num_kv_heads
+    picks += [(0, 0, 0), (B - 1, sp.n_rows - 1, H - 1), (min(3, B - 1), 1023, min(2, H - 1))]
     for b, r, g in picks:
         L = int(cpu.seq_lens[b])
         q1 = cpu.q[b:b + 1, r:r + 1].contiguous().view(torch.uint16).numpy()
