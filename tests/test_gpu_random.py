@@ -2,7 +2,9 @@
 sequence (including chunks that take the prefill kernel), windows, Dmax below the
 reachable distances, page sizes, both cache formats and forced split counts, drawn
 together so that their combinations, not only each feature alone, meet the oracle.
-Unused cache slots, pages and bias columns hold NaN (``poison``)."""
+Unused cache slots, pages and bias columns hold NaN (``poison``). The split-kernel
+problems run again with a seeded number of rows per sequence (0 allowed) through
+rattn_decode_varlen."""
 
 import dataclasses
 import math
@@ -13,6 +15,7 @@ import pytest
 from decode_attention_verify_amd import binding, synth
 
 from tests.parity import check_case
+from tests.test_gpu_varlen import check_varlen
 
 kMaxRows = 128          # packed rows above which a call takes the prefill kernel
 
@@ -86,3 +89,16 @@ def test_random_cases_plan():
 def test_random_shapes(i):
     sp, splits, seed = spec_of(i)
     check_case(sp, seed=seed, num_splits=splits)
+
+
+def _split_kernel(i):
+    fields = CASES[i][0]
+    return fields["n_rows"] * fields["num_q_heads"] // fields["num_kv_heads"] <= kMaxRows
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", [i for i in range(len(CASES)) if _split_kernel(i)])
+def test_random_shapes_varlen(i):
+    sp, splits, seed = spec_of(i)
+    rows = synth.draw_rows_per_seq(sp.batch, sp.n_rows, seed=seed, allow_zero=True)
+    check_varlen(sp, rows, seed, num_splits=splits)
