@@ -4,7 +4,8 @@ reachable distances, page sizes, both cache formats and forced split counts, dra
 together so that their combinations, not only each feature alone, meet the oracle.
 Unused cache slots, pages and bias columns hold NaN (``poison``). The split-kernel
 problems run again with a seeded number of rows per sequence (0 allowed) through
-rattn_decode_varlen."""
+rattn_decode_varlen, and every other problem's shapes append n new tokens per sequence
+(rattn_append_kv), compared bit for bit."""
 
 import dataclasses
 import math
@@ -15,6 +16,7 @@ import pytest
 from decode_attention_verify_amd import binding, synth
 
 from tests.parity import check_case
+from tests.test_gpu_append import _append_both, _as_codes, _new_rows, _oracle_append, _same_bits
 from tests.test_gpu_varlen import check_varlen
 
 kMaxRows = 128          # packed rows above which a call takes the prefill kernel
@@ -102,3 +104,19 @@ def test_random_shapes_varlen(i):
     sp, splits, seed = spec_of(i)
     rows = synth.draw_rows_per_seq(sp.batch, sp.n_rows, seed=seed, allow_zero=True)
     check_varlen(sp, rows, seed, num_splits=splits)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(0, len(CASES), 2))
+def test_random_shapes_append(i):
+    sp, _, seed = spec_of(i)
+    case = synth.make_case(sp, seed=seed)
+    k_new, v_new = _new_rows(sp.batch, sp.n_rows, sp.num_kv_heads, sp.head_dim, seed=seed)
+    kc, vc, ks, vs, flags, _ = _append_both(case, k_new, v_new)
+    assert flags == 0
+    ok, ov, oks, ovs = _oracle_append(case, k_new, v_new)
+    _same_bits(_as_codes(kc), ok, "K cache")
+    _same_bits(_as_codes(vc), ov, "V cache")
+    if sp.kv_format == synth.KV_FP8:
+        _same_bits(ks, oks, "K scales")
+        _same_bits(vs, ovs, "V scales")
