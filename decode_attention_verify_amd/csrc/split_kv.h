@@ -586,30 +586,42 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
             if constexpr (STAGE_BIAS) bv[kt][i] = bl[bias_pos[t] + 16 * kt + i];
             else bv[kt][i] = X.bs[4 * kt + i];
           }
+        // the logits and this lane's maximum; the masks only on tiles at the edges of
+        // the visible range (one uniform branch around each form of the loop)
         float sv[2][4];
         float mt = kNegInf;
+        if (fast) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float scl = FP8 ? a.softmax_scale * ks[kt][i] : a.softmax_scale;
-            float sc = __builtin_fmaf(sacc[t][kt][i], scl, bv[kt][i]);
-            if (!fast) {
+            for (int i = 0; i < 4; ++i) {
+              const float scl = FP8 ? a.softmax_scale * ks[kt][i] : a.softmax_scale;
+              sv[kt][i] = __builtin_fmaf(sacc[t][kt][i], scl, bv[kt][i]);
+              mt = fmaxf(mt, sv[kt][i]);
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float scl = FP8 ? a.softmax_scale * ks[kt][i] : a.softmax_scale;
+              const float sc = __builtin_fmaf(sacc[t][kt][i], scl, bv[kt][i]);
               const int dist = row_p[t] - (j0 + 16 * kt + 4 * lq + i);
               const bool vis = row_live[t] && dist >= 0 && (W == 0 || dist < W);
-              sc = vis ? sc : kNegInf;
+              sv[kt][i] = vis ? sc : kNegInf;
+              mt = fmaxf(mt, sv[kt][i]);
             }
-            sv[kt][i] = sc;
-            mt = fmaxf(mt, sc);
-          }
         }
-        mt = wave_max_rows(mt);
         // The reference point m of a row moves only when the tile's maximum exceeds it
         // by more than kRescaleSlack, so that the accumulators are rescaled on few
         // tiles; p = exp(s - m) then stays below exp(kRescaleSlack). O and l share m, so
-        // the quotient O / l and lse = m + ln l are unchanged by the choice of m.
-        const bool grow = mt > m_run[t] + kRescaleSlack;   // false while mt = -inf
-        if (__ballot(grow) != 0) {                         // wave-uniform
+        // the quotient O / l and lse = m + ln l are unchanged by the choice of m. The
+        // test runs on each lane's own maximum: a row's maximum passes m + kRescaleSlack
+        // exactly when the maximum of one of its 4 lanes does, so the row maximum is
+        // taken (across the lanes) only in the rare branch.
+        if (__ballot(mt > m_run[t] + kRescaleSlack) != 0) {   // wave-uniform; false at -inf
+          mt = wave_max_rows(mt);
+          const bool grow = mt > m_run[t] + kRescaleSlack;
           const float m_new = grow ? mt : m_run[t];
           const float alpha = grow ? __builtin_amdgcn_exp2f((m_run[t] - m_new) * kLog2e) : 1.f;
           l_run[t] *= alpha;
