@@ -39,7 +39,8 @@ rattn_status validate_problem(const rattn_problem* p) {
   if ((int64_t)p->max_seq_len > (int64_t)p->max_pages_per_seq * p->page_size)
     return RATTN_E_INVALID;
   if (p->window < 0 || p->dmax < 0) return RATTN_E_INVALID;
-  if (!std::isfinite(p->softmax_scale)) return RATTN_E_INVALID;
+  // a positive normal float: the kernels divide the bias by it and take maxima of s / scale
+  if (!std::isnormal(p->softmax_scale) || !(p->softmax_scale > 0.f)) return RATTN_E_INVALID;
   if (p->kv_dtype != RATTN_KV_BF16 && p->kv_dtype != RATTN_KV_FP8_E4M3) return RATTN_E_INVALID;
   if (p->num_splits < 0) return RATTN_E_INVALID;
   // valid, but outside what the kernels implement

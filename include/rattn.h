@@ -105,7 +105,9 @@ typedef struct {
   int32_t max_seq_len;       /* upper bound on seq_lens[]; <= max_pages_per_seq*page_size */
   int32_t window;            /* 0 = full context; W > 0 = W keys including the token      */
   int32_t dmax;              /* largest distance with its own bias column (>= 0)          */
-  float softmax_scale;       /* multiplies q . k (1/sqrt(head_dim) for the pages' models) */
+  float softmax_scale;       /* multiplies q . k (1/sqrt(head_dim) for the pages' models);*/
+                             /* a positive normal float, else RATTN_E_INVALID; the bias  */
+                             /* divided by it must stay finite in fp32                   */
   int32_t kv_dtype;          /* rattn_kv_dtype                                            */
   int32_t num_splits;        /* 0 = planner; > 0 forces num_splits pieces (key ranges)    */
                              /* per (sequence, KV head) unit (at most 4096; at most      */

@@ -41,6 +41,8 @@ INVALID = [
     dict(n_query_rows=0), dict(page_size=0), dict(num_pages=0), dict(max_pages_per_seq=0),
     dict(max_seq_len=0), dict(max_seq_len=100001), dict(window=-1), dict(dmax=-1),
     dict(softmax_scale=float("inf")), dict(softmax_scale=float("nan")), dict(kv_dtype=2),
+    # the scale must be a positive normal float (the kernels divide the bias by it)
+    dict(softmax_scale=0.0), dict(softmax_scale=-0.08), dict(softmax_scale=1e-40),
     dict(num_splits=-1),
 ]
 UNSUPPORTED = [
