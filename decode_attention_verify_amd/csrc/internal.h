@@ -21,6 +21,9 @@ constexpr int kBiasPerThread = 4;
 constexpr int kMaxWaves = 8;      // waves of a split work-group (one 16-row tile each)
 // A one-wave piece of several row tiles loads the slice alone: 8 loads per lane
 constexpr int kBiasPerThreadRows = 8;
+// Four waves of two row tiles: 2 loads per lane (slices of up to 512 entries: the 9-row
+// step of an 8-head group needs 320), which keeps the two tiles in flight in registers
+constexpr int kBiasPerThreadPair = 2;
 constexpr int kMaxRowTiles = 3;   // row tiles of a one-wave piece (48 rows)
 
 // Waves per split work-group for G query heads per KV head and n rows: each wave owns
@@ -63,7 +66,7 @@ inline SplitShape split_shape(const rattn_problem& p) {
   if (p.kv_dtype == RATTN_KV_BF16 && span >= kRowTilesMinSpan) {
     if (rows > 16 && rows <= 16 * kMaxRowTiles && slice <= 64 * kBiasPerThreadRows)
       return SplitShape{1, (int)((rows + 15) / 16)};
-    if (rows > 64 && rows <= kMaxRows && slice <= 64 * 4 * kBiasPerThread)
+    if (rows > 64 && rows <= kMaxRows && slice <= 64 * 4 * kBiasPerThreadPair)
       return SplitShape{4, 2};
   }
   return SplitShape{waves_for(G, n), 1};

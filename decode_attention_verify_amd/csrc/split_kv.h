@@ -94,7 +94,8 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
   // WR (two buffers exactly when several waves share one).
   constexpr bool STAGE_BIAS = WR > 1 || RT > 1;
   constexpr int BIAS_BUFS = WR > 1 ? 2 : 1;
-  constexpr int BPT = RT > 1 && WR == 1 ? kBiasPerThreadRows : kBiasPerThread;   // slice loads per lane
+  constexpr int BPT = RT == 1 ? kBiasPerThread
+                      : (WR == 1 ? kBiasPerThreadRows : kBiasPerThreadPair);   // slice loads per lane
   __shared__ float bias_lds[BIAS_BUFS][STAGE_BIAS ? 64 * WR * BPT : 1];
   // RT > 1: the queries of the wave's RT * 16 rows, row i's 16-byte chunk c at
   // klds_off(i, c) (the B operand reads of one instruction hit distinct banks)

@@ -271,6 +271,20 @@ def test_planner_65_to_128_rows(hq, n, kv):
     assert (short.row_tiles, short.tiles_per_wave) == (8, 1)
 
 
+def test_planner_two_row_tiles_bias_share():
+    # four waves of two row tiles load a tile's bias slice with 2 loads per lane: a
+    # 16-head group's slice (16 x 36 entries at n = 5) goes to 8-wave groups instead
+    for hq, n, want in ((128, 5, (8, 1)), (128, 8, (8, 1)), (96, 6, (4, 2)), (64, 16, (4, 2))):
+        G = hq // 8
+        assert 64 < G * n <= 128
+        assert (G * (32 + n - 1) <= 512) == (want == (4, 2))
+        p = headline(batch=4, num_q_heads=hq, n_query_rows=n, max_seq_len=262144,
+                     max_pages_per_seq=16384, num_pages=65536, dmax=262143)
+        info = binding.rattn_plan_describe(p, 256)
+        assert info.kernel == binding.RATTN_KERNEL_SPLIT_KV
+        assert (info.row_tiles, info.tiles_per_wave) == want, (hq, n)
+
+
 def test_static_entry_checks_on_the_host():
     # rattn_decode_static validates the problem and its pointers before any HIP call
     lib = binding.load()

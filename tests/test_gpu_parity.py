@@ -171,6 +171,16 @@ def test_four_waves_two_tiles_in_flight(splits, L):
     assert info["row_tiles"] == 4 and info["tiles_per_wave"] == 2
 
 
+@pytest.mark.parametrize("n,batch", [(5, 2), (8, 1)])
+def test_sixteen_head_groups_long_span(n, batch):
+    # 80 and 128 packed rows of 16-head groups over more than 8,192 keys: their bias slice
+    # (16 x (31 + n) entries) exceeds the two-row-tile layout's share, so 8-wave groups run
+    sp = small("full_100k", batch=batch, n_rows=n, num_q_heads=16, num_kv_heads=1,
+               seq_len=("uniform", 8500, 9500), dmax=9000, max_seq_len=9500, name="g16_long")
+    _, _, info = check_case(sp, seed=n)
+    assert info["row_tiles"] == 8 and info["tiles_per_wave"] == 1
+
+
 # ------------------------- one GPU's share of the headline layer under TP4 / TP8 (KV heads)
 
 @pytest.mark.parametrize("name", ["tp4_100k", "tp8_100k"])
