@@ -27,7 +27,9 @@
 //    read's offset is an immediate), each thread loading 16 bytes of a K row and 16 of a
 //    V row (16 lanes read a 256-byte row, through the caches, which the unit's other
 //    blocks hit); every K or V^T fragment read from LDS feeds the MFMAs of all HW heads;
-//    the page ids of a tile's loads are read from LDS a half ahead of the loads;
+//    the page ids of a tile's loads are read from LDS a half ahead of the loads; with
+//    two heads per wave a thread holds two sets of these shares, loaded two tiles
+//    before they are stored (one tile with three heads, whose registers are full);
 //  * the bias is sheared: for a tile at key j0, head h needs distances p0 - j0 - 31 ..
 //    p0 + M - 1 - j0 (p0 the position of the block's first token), one contiguous slice
 //    of M + 31 entries which the work-group stages in LDS (divided by the softmax
@@ -159,6 +161,11 @@ void prefill_kernel(KernelArgs a) {
   //    slice of tile t + 1 + g and of V_{t+g}: each buffer is written after its
   //    previous tile's last read and before its tile's first read.
   static_assert(NW == 8, "two groups of one wave per SIMD");
+  // Tiles between a share's loads and its stores. With two heads per wave the registers
+  // hold two sets of shares, so a V half loads the shares it stores two tiles later
+  // (about three halves of latency cover instead of one and a half); three heads per
+  // wave keep one set.
+  constexpr int LEAD = HW <= 2 ? 2 : 1;
   static_assert(SPK == 1, "one K and one V load per thread and tile");
   const int grp = wave >> 2;
   const int nt = (j_end - j_begin + kTileKeys - 1) / kTileKeys;   // tiles, >= 1
@@ -168,10 +175,10 @@ void prefill_kernel(KernelArgs a) {
 
   // ---- page ids, staged in LDS per chunk of keys, two chunk buffers. The ids of chunk
   // c + 1 are staged in the V half of the chunk's first tile (group A's half 2 c T + 2,
-  // B's 2 c T + 3, T tiles per chunk). The ids are read in the M half before a tile's
-  // loads (tile_base): the first read of chunk c + 1 comes at least 2 T - 5 halves after
-  // its staging began, and the last read of chunk c - 1 (the buffer's previous chunk) at
-  // least 5 halves before it. ----
+  // B's 2 c T + 3, T tiles per chunk). The ids are read in the M half that precedes a
+  // tile's loads (tile_base), LEAD tiles before its stores: the first read of chunk c + 1
+  // comes at least 2 T - 5 - 2 LEAD halves after its staging began, and the last read
+  // of chunk c - 1 (the buffer's previous chunk) at least 4 halves before it. ----
   const int32_t* pt_row = a.page_table + (int64_t)b * a.max_pages;
   auto stage_chunk = [&](int c) {
     const int c0 = j_begin + c * chunk_keys;
@@ -308,7 +315,7 @@ void prefill_kernel(KernelArgs a) {
   // from LDS feeds the MFMAs of all HW heads
   TileBase next_base;                        // load_shares(X, t + 1) of V(t), from M(t)
   auto m_half = [&](int t) {
-    const TilePages next_pages = tile_pages(t + 1);
+    const TilePages next_pages = tile_pages(t + LEAD);
     if (t >= 1 && live(t - 1)) {
       const unsigned char* vl = vlds[(t - 1) & 1];
 #pragma unroll
@@ -354,14 +361,15 @@ void prefill_kernel(KernelArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    next_base = tile_base(t + 1, next_pages);
+    next_base = tile_base(t + LEAD, next_pages);
   };
 
   // V(t): masks (FAST = false: the tiles that cross the diagonal or the window edge),
   // the tile maximum, the rare rescale, P = exp(s - m); then the wave's share of the
   // stores and the next loads
-  Shares X;
-  auto v_half = [&](int t, auto fast_tag) {
+  // X0: the shares this V half stores; X1 (LEAD = 2): the next V half's
+  Shares X0, X1;
+  auto v_half = [&](int t, auto fast_tag, Shares& X) {
     constexpr bool FAST = decltype(fast_tag)::value;
     if (live(t)) {
       const int j0 = j_begin + t * kTileKeys;
@@ -429,21 +437,34 @@ void prefill_kernel(KernelArgs a) {
     store_shares(X, t);
     if ((t & (chunk_tiles - 1)) == 0 && t + chunk_tiles < nt)
       stage_chunk((t >> (chunk_shift - 5)) + 1);             // chunk_tiles = 2^(chunk_shift - 5)
-    load_shares(X, t + 1, next_base);
+    load_shares(X, t + LEAD, next_base);
   };
 
   // ---- prologue: chunk 0's page ids; group A stores what its V(-1) would, group B
-  // what its V(-2) would, then B's V(-1) shares A's M(0) half ----
+  // what its V(-2) would, then B's V(-1) shares A's M(0) half. Each group ends holding
+  // the shares of V(0) (and of V(1) with two sets). ----
+  auto load_at = [&](Shares& X, int p) { load_shares(X, p, tile_base(p, tile_pages(p))); };
   stage_chunk(0);
   __syncthreads();
-  load_shares(X, grp ? -2 : -1, tile_base(grp ? -2 : -1, tile_pages(grp ? -2 : -1)));
-  store_shares(X, grp ? -2 : -1);
-  load_shares(X, grp ? -1 : 0, tile_base(grp ? -1 : 0, tile_pages(grp ? -1 : 0)));
-  __syncthreads();
-  if (grp) {
-    store_shares(X, -1);
-    load_shares(X, 0, tile_base(0, tile_pages(0)));
+  load_at(X0, grp ? -2 : -1);
+  store_shares(X0, grp ? -2 : -1);
+  if constexpr (LEAD == 2) {
+    if (grp) {
+      load_at(X0, -1);
+      __syncthreads();
+      store_shares(X0, -1);
+    }
+    load_at(X0, 0);
+    load_at(X1, 1);
     __syncthreads();
+  } else {
+    load_at(X0, grp ? -1 : 0);
+    __syncthreads();
+    if (grp) {
+      store_shares(X0, -1);
+      load_at(X0, 0);
+      __syncthreads();
+    }
   }
 
   // ---- tile loop: fast tiles (every key visible to every row: no mask code) form one
@@ -458,23 +479,55 @@ void prefill_kernel(KernelArgs a) {
   const int last = p0 - (kTileKeys - 1) - j_begin;        // largest fast j0 - j_begin
   const int x_hi = last < 0 ? x_lo : max(x_lo, min(last / kTileKeys + 1, nt));
   int t = 0;
-  for (; t < x_lo; ++t) {
-    m_half(t);
-    __syncthreads();
-    v_half(t, std::false_type{});
-    __syncthreads();
-  }
-  for (; t < x_hi; ++t) {
-    m_half(t);
-    __syncthreads();
-    v_half(t, std::true_type{});
-    __syncthreads();
-  }
-  for (; t < nt; ++t) {
-    m_half(t);
-    __syncthreads();
-    v_half(t, std::false_type{});
-    __syncthreads();
+  // tiles t .. t_end - 1; with two sets, V(t) stores X0 and V(t + 1) X1, and a run of
+  // odd length leaves the sets exchanged for the next run
+  auto run = [&](int t_end, auto fast_tag) {
+    {
+      for (; t + 1 < t_end; t += 2) {
+        m_half(t);
+        __syncthreads();
+        v_half(t, fast_tag, X0);
+        __syncthreads();
+        m_half(t + 1);
+        __syncthreads();
+        v_half(t + 1, fast_tag, X1);
+        __syncthreads();
+      }
+      if (t < t_end) {
+        m_half(t);
+        __syncthreads();
+        v_half(t, fast_tag, X0);
+        __syncthreads();
+        ++t;
+        const Shares x = X0;
+        X0 = X1;
+        X1 = x;
+      }
+    }
+  };
+  if constexpr (LEAD == 2) {
+    run(x_lo, std::false_type{});
+    run(x_hi, std::true_type{});
+    run(nt, std::false_type{});
+  } else {
+    for (; t < x_lo; ++t) {
+      m_half(t);
+      __syncthreads();
+      v_half(t, std::false_type{}, X0);
+      __syncthreads();
+    }
+    for (; t < x_hi; ++t) {
+      m_half(t);
+      __syncthreads();
+      v_half(t, std::true_type{}, X0);
+      __syncthreads();
+    }
+    for (; t < nt; ++t) {
+      m_half(t);
+      __syncthreads();
+      v_half(t, std::false_type{}, X0);
+      __syncthreads();
+    }
   }
   m_half(nt);                                 // P V of the last tile
   if (!grp) __syncthreads();                  // pairs with group B's last barrier
