@@ -43,9 +43,9 @@ inline int waves_for(int G, int n) {
 
 // Row tiles per wave. Over a bf16 cache whose rows all see at least kRowTilesMinSpan
 // keys, a piece of 17 to 48 packed rows runs as one wave of 2 or 3 row tiles (16 rows
-// each, or fewer rows spread evenly over them), and a piece of 65 to 128 rows as four
-// waves of two row tiles (up to 32 rows per wave); other row counts and spans keep one
-// row tile per wave (waves_for). A wave reads each K and V fragment once for its tiles.
+// each, or fewer rows spread evenly over them), and a piece of 65 to 128 rows whose bias
+// slice has at most 512 entries as four waves of two row tiles (up to 32 rows per wave);
+// other row counts, slices and spans keep one row tile per wave (waves_for). A wave reads each K and V fragment once for its tiles.
 // On MI355X the 8-row verify of 6-head groups over 32K-256K keys ran 7 % faster as one
 // wave of three tiles than as four waves of one, the same step over a 1,024-key window
 // 26 % slower. (4 and 5 tiles per wave spill registers.)
