@@ -63,7 +63,8 @@ namespace rattn {
 // slice are staged in LDS. A one-wave piece runs alone on its SIMD with the full register
 // file and one tile in flight (the O accumulators, 32 registers per row tile, leave the
 // arithmetic registers to that tile); four waves of two tiles run two waves per SIMD, two
-// groups per CU, with two tiles in flight (each wave holds a quarter of a tile's loads).
+// groups per CU, with two tiles in flight (each wave holds a quarter of a tile's loads),
+// as do groups of four or eight waves of one row tile.
 // Waves per SIMD: one for a single bf16 wave (its two tiles in flight take 128 registers)
 // and for a wave of row tiles (the accumulators of 2 or 3 tiles), and for 2-wave groups of
 // even shares over a bf16 cache (at two per SIMD they spilled 104 bytes per lane; the
@@ -690,16 +691,21 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
       attend_tile(X, j0, buf);
     };
 
-    // ---- tile loop, chunks of at most kChunkPages pages. One row tile per wave: two
-    // tiles in registers. Several row tiles in a lone wave (their accumulators take the
-    // registers): one tile in flight, whose loads are issued as soon as the tile before
-    // it is in LDS, so that they are in flight while the wave attends that tile ----
+    // ---- tile loop, chunks of at most kChunkPages pages. Groups of four or eight waves
+    // (each wave a quarter or an eighth of a tile's loads): two tiles in flight while one
+    // is attended. One or two waves of one row tile: two tiles in registers, the next
+    // tile's loads in flight while one is attended. Several row tiles in a lone wave
+    // (their accumulators take the registers): one tile in flight, whose loads are issued
+    // as soon as the tile before it is in LDS, so that they are in flight while the wave
+    // attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-    constexpr bool TWO_AHEAD = RT > 1 && WR > 1;
+    constexpr bool TWO_AHEAD = (RT > 1 && WR > 1) || WR >= 4;
     constexpr bool ONE_IN_FLIGHT = RT > 1 && !TWO_AHEAD;
     if constexpr (TWO_AHEAD) {
-      // Several waves of row tiles (a quarter of each tile's loads per wave): two tiles in
-      // flight while one is attended, in registers A and B by turns. Each tile's loads are
+      // Groups of four or eight waves: two tiles in flight while one is attended, in
+      // registers A and B by turns. (Over short pieces, as in a window layer's verify, a
+      // tile's loads then wait less; one or two waves, whose share of a tile is larger,
+      // keep the other loop.) Each tile's loads are
       // issued right after the tile two places before it is in LDS. In the steady state
       // every load is issued without a condition, so that the compiler waits for exactly
       // one tile; a chunk of fewer than two tiles loads its one tile twice.
@@ -749,7 +755,7 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     }
     // Two tiles in registers: the loads of tile i + 1 are issued before tile i is staged.
     Tile A, B;
-    for (int c0 = j_begin; RT == 1 && c0 < j_end; c0 += chunk_keys) {
+    for (int c0 = j_begin; RT == 1 && !TWO_AHEAD && c0 < j_end; c0 += chunk_keys) {
       const int c1 = min(c0 + chunk_keys, j_end);
       stage_pages(c0, c1);
       const int nt = (c1 - c0 + kTileKeys - 1) / kTileKeys;
