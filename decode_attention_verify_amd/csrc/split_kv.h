@@ -64,7 +64,8 @@ namespace rattn {
 // file and one tile in flight (the O accumulators, 32 registers per row tile, leave the
 // arithmetic registers to that tile); four waves of two tiles run two waves per SIMD, two
 // groups per CU, with two tiles in flight (each wave holds a quarter of a tile's loads),
-// as do groups of four or eight waves of one row tile.
+// as do groups of four or eight waves of one row tile and two-wave groups of even shares
+// over a bf16 cache.
 // Waves per SIMD: one for a single bf16 wave (its two tiles in flight take 128 registers)
 // and for a wave of row tiles (the accumulators of 2 or 3 tiles), and for 2-wave groups of
 // even shares over a bf16 cache (at two per SIMD they spilled 104 bytes per lane; the
@@ -692,20 +693,20 @@ __attribute__((amdgpu_waves_per_eu(OCCUPANCY))) void split_kv_kernel(
     };
 
     // ---- tile loop, chunks of at most kChunkPages pages. Groups of four or eight waves
-    // (each wave a quarter or an eighth of a tile's loads): two tiles in flight while one
-    // is attended. One or two waves of one row tile: two tiles in registers, the next
-    // tile's loads in flight while one is attended. Several row tiles in a lone wave
+    // (each wave a quarter or an eighth of a tile's loads), and two waves of even shares
+    // over a bf16 cache (one per SIMD): two tiles in flight while one is attended. One
+    // wave, or two waves at two per SIMD, of one row tile: two tiles in registers, the
+    // next tile's loads in flight while one is attended. Several row tiles in a lone wave
     // (their accumulators take the registers): one tile in flight, whose loads are issued
     // as soon as the tile before it is in LDS, so that they are in flight while the wave
     // attends that tile ----
     const int chunk_keys = (int)min((int64_t)kChunkPages * S, (int64_t)1 << 30);
-    constexpr bool TWO_AHEAD = (RT > 1 && WR > 1) || WR >= 4;
+    constexpr bool TWO_AHEAD = (RT > 1 && WR > 1) || WR >= 4 || (WR == 2 && EVEN && !FP8);
     constexpr bool ONE_IN_FLIGHT = RT > 1 && !TWO_AHEAD;
     if constexpr (TWO_AHEAD) {
-      // Groups of four or eight waves: two tiles in flight while one is attended, in
-      // registers A and B by turns. (Over short pieces, as in a window layer's verify, a
-      // tile's loads then wait less; one or two waves, whose share of a tile is larger,
-      // keep the other loop.) Each tile's loads are
+      // Two tiles in flight while one is attended, in registers A and B by turns. (Over
+      // short pieces, as in a window layer's verify, a tile's loads then wait less; a lone
+      // wave, whose share of a tile is the whole tile, keeps the other loop.) Each tile's loads are
       // issued right after the tile two places before it is in LDS. In the steady state
       // every load is issued without a condition, so that the compiler waits for exactly
       // one tile; a chunk of fewer than two tiles loads its one tile twice.
