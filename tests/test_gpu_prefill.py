@@ -57,13 +57,14 @@ def test_prefill_fp8_cache(hq, hkv, n, W, page_size):
     assert info["kernel"] == binding.RATTN_KERNEL_PREFILL
 
 
-@pytest.mark.parametrize("W", [0, 64])
-def test_prefill_dmax_clamp(W):
-    # most distances past Dmax = 45: every clamped entry of a bias slice (stored in
-    # reverse in LDS) is the table's last column
+@pytest.mark.parametrize("W,dmax", [(0, 45), (64, 45), (0, 0), (1, 0), (1, 7), (2, 1)])
+def test_prefill_dmax_clamp(W, dmax):
+    # most distances past Dmax: every clamped entry of a bias slice (stored in reverse in
+    # LDS) is the table's last column; Dmax = 0 gives every key one bias, and a window of
+    # one key leaves each row its own key alone
     sp = small("full_100k", batch=2, n_rows=100, seq_len=("uniform", 100, 1500), window=W,
-               dmax=45, name="prefill_dmax")
-    _, _, info = check_case(sp, seed=45 + W)
+               dmax=dmax, name="prefill_dmax")
+    _, _, info = check_case(sp, seed=45 + W + dmax)
     assert info["kernel"] == binding.RATTN_KERNEL_PREFILL
 
 
