@@ -482,29 +482,29 @@ void prefill_kernel(KernelArgs a) {
   // tiles t .. t_end - 1; with two sets, V(t) stores X0 and V(t + 1) X1, and a run of
   // odd length leaves the sets exchanged for the next run
   auto run = [&](int t_end, auto fast_tag) {
-    {
-      for (; t + 1 < t_end; t += 2) {
-        m_half(t);
-        __syncthreads();
-        v_half(t, fast_tag, X0);
-        __syncthreads();
-        m_half(t + 1);
-        __syncthreads();
-        v_half(t + 1, fast_tag, X1);
-        __syncthreads();
-      }
-      if (t < t_end) {
-        m_half(t);
-        __syncthreads();
-        v_half(t, fast_tag, X0);
-        __syncthreads();
-        ++t;
-        const Shares x = X0;
-        X0 = X1;
-        X1 = x;
-      }
+    for (; t + 1 < t_end; t += 2) {
+      m_half(t);
+      __syncthreads();
+      v_half(t, fast_tag, X0);
+      __syncthreads();
+      m_half(t + 1);
+      __syncthreads();
+      v_half(t + 1, fast_tag, X1);
+      __syncthreads();
+    }
+    if (t < t_end) {
+      m_half(t);
+      __syncthreads();
+      v_half(t, fast_tag, X0);
+      __syncthreads();
+      ++t;
+      const Shares x = X0;
+      X0 = X1;
+      X1 = x;
     }
   };
+  // (one set keeps loops of its own: written as runs of two steps, the same schedule
+  // compiled to a three-head kernel with more registers and a slower loop)
   if constexpr (LEAD == 2) {
     run(x_lo, std::false_type{});
     run(x_hi, std::true_type{});
